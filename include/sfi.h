@@ -1,0 +1,246 @@
+/*
+ * sfi.h - C ABI of libsfi, the Slow-Fast Inference (SFI) decode-attention
+ * hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the SFI page ("Slow-Fast Inference: Training-Free Inference
+ * Acceleration via Within-Sentence Support Stability",
+ * thelatestinai.com/papers/2603.12038), the SparseSpec-L abstract ("A Sparse
+ * Glimpse of the Whole: Train-Free Self-Speculative Decoding") and the
+ * ASPIRE abstract.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is DEVICE memory owned by the caller; the
+ *    descriptors (sfi_shape, sfi_paged_kv) and any array documented as "host"
+ *    are host memory read during the call only.  The library allocates
+ *    nothing, owns no stream and keeps no state beyond a thread-local error
+ *    string.
+ *  - Layouts are dense row-major with the shapes given.  B = batch,
+ *    Hq / Hkv = query / KV heads, G = Hq / Hkv, d = head_dim, P = page_size.
+ *    Query head h reads KV head h / G.
+ *  - A paged pool k or v has shape [num_pages, Hkv, P, d]; token j of request
+ *    b, KV head g, is row [block_table[b * max_pages + j / P], g, j % P].
+ *  - seq_lens[b] (device int32) counts every token of request b including its
+ *    t_q query tokens, whose K/V must already be in the pool; query token t
+ *    sits at position seq_lens[b] - t_q + t and sees keys [0, that position].
+ *  - Candidate set of a slow step / verification: positions
+ *    [n_sink, max(n_sink, seq_lens[b] - t_q + 1 - n_recent)).  Recent window
+ *    of a fast step: [max(n_sink, seq_lens[b] - n_recent), seq_lens[b]).
+ *  - Outputs out / lse are float32; lse is the natural-log sum of exp(logit)
+ *    over the keys seen, logit = scale * q . k.  A row that sees no key gets
+ *    out = 0 and lse = -inf.
+ *  - Calls only enqueue work on `stream` (a hipStream_t, NULL = default
+ *    stream) and return without synchronising.  Ordering across streams is
+ *    the caller's job (events).
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued; on failure nothing is launched, no output is touched, and
+ *    sfi_last_error() describes the problem.  A failed launch returns
+ *    SFI_ERR_HIP.  No C++ exception crosses this boundary.
+ *  - Device-side safety: block-table entries outside [0, num_pages), and
+ *    positions outside [0, seq_lens[b]), are never dereferenced; keys behind
+ *    such entries are skipped (attention) or written as zero rows (pack).
+ *    seq_lens[b] is clamped to [0, min(max_seq_len, max_pages * P)].
+ *  - Supported: d in {64, 128}; G in {1, 2, 4, 8}; P = 16; dtype F32 or BF16
+ *    for t_q = 1; BF16 with t_q * G <= 64 for t_q in [2, 16].  Pointers to
+ *    q, k, v, compact buffers, out and workspace must be 16-byte aligned.
+ */
+#ifndef SFI_H_
+#define SFI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SFI_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SFI_API __attribute__((visibility("default")))
+#else
+#define SFI_API
+#endif
+
+typedef enum sfi_status {
+  SFI_OK = 0,
+  SFI_ERR_INVALID_ARG = 1, /* null / misaligned pointer, out-of-range size */
+  SFI_ERR_UNSUPPORTED = 2, /* valid request outside the supported shapes   */
+  SFI_ERR_WORKSPACE = 3,   /* workspace smaller than the size query says   */
+  SFI_ERR_HIP = 4          /* the HIP runtime reported an error            */
+} sfi_status;
+
+typedef enum sfi_dtype { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
+
+/* Problem shape shared by the attention and pack calls (host memory). */
+typedef struct sfi_shape {
+  int32_t batch;        /* B >= 1                                           */
+  int32_t num_q_heads;  /* Hq                                               */
+  int32_t num_kv_heads; /* Hkv, Hq % Hkv == 0                               */
+  int32_t head_dim;     /* d                                                */
+  int32_t dtype;        /* sfi_dtype of q, the pools and the compact buffers */
+  float scale;          /* logit scale, normally 1 / sqrt(d)                */
+} sfi_shape;
+
+/* Paged KV cache (host descriptor of device memory).  The whole cache stays
+ * resident: tokens left out of the sparse state remain recallable
+ * (SparseSpec-L abstract: the dense KV cache is never discarded). */
+typedef struct sfi_paged_kv {
+  const void* k;              /* [num_pages, Hkv, P, d]                      */
+  const void* v;              /* [num_pages, Hkv, P, d]                      */
+  const int32_t* block_table; /* [B, max_pages] physical page ids            */
+  int32_t max_pages;          /* row length of block_table                   */
+  int32_t page_size;          /* P, must be 16                               */
+  int32_t num_pages;          /* pool size in pages                          */
+  int32_t max_seq_len;        /* host upper bound on every seq_lens[b]; sizes
+                                 the launch (and the workspace)             */
+} sfi_paged_kv;
+
+/*
+ * Slow step: dense attention that also emits the masked logits.
+ * SFI page, Fig. 2 caption: a slow step performs dense attention and collects
+ * masked attention logits over the allowed candidate set for the Selector;
+ * Table 1 uses dense-attention latency as its baseline.  With t_q > 1 it is
+ * full-context causal verification of t_q draft tokens that also yields the
+ * per-head statistics reused as the importance signal (SparseSpec-L
+ * abstract).
+ *
+ *  q       [B, t_q, Hq, d]  dtype            t_q in [1, 16]
+ *  out     [B, t_q, Hq, d]  float32
+ *  lse     [B, t_q, Hq]     float32 or NULL
+ *  scores  [B, Hkv, score_stride] float32 or NULL (NULL = plain dense
+ *          attention).  scores[b, g, j] = sum over query tokens t and query
+ *          heads h of group g of scale * q[b,t,h] . k_j for j in the candidate
+ *          set, -inf for every other j < score_stride.  Requires
+ *          score_stride >= max_seq_len.
+ *  workspace: device scratch of at least sfi_dense_attn_workspace_size()
+ *          bytes (may be NULL when that size is 0).
+ */
+SFI_API sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                     const void* q, int32_t t_q, const int32_t* seq_lens,
+                                     int32_t n_sink, int32_t n_recent, float* out, float* lse,
+                                     float* scores, int64_t score_stride, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+SFI_API sfi_status sfi_dense_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                         int32_t t_q, size_t* bytes);
+
+/*
+ * Selector: top-k over each KV head's masked logits.
+ * SFI page, Abstract and Fig. 2 caption (the Selector refreshes the selected
+ * memory from the slow step's logits); Fig. 3A (it runs on the auxiliary
+ * stream).  Per (b, g), among candidate positions the k_eff = min(k, number
+ * of candidates) with the largest score are chosen, equal scores going to
+ * the lower position (-0.0 == +0.0, -inf is the lowest score; NaN scores are
+ * not supported).  Output is exact and deterministic.
+ *
+ *  scores   [B, Hkv, score_stride] float32 (only candidate positions are read)
+ *  sel_idx  [B, Hkv, k] int32: the chosen positions ascending, then -1.
+ *  t_q, n_sink, n_recent define the candidate set as above.
+ *  workspace: at least sfi_select_topk_workspace_size() bytes.
+ */
+SFI_API sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_heads,
+                           int64_t score_stride, const int32_t* seq_lens, int32_t t_q,
+                           int32_t n_sink, int32_t n_recent, int32_t k, int32_t* sel_idx,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+SFI_API sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads,
+                                          int64_t score_stride, int32_t k, size_t* bytes);
+
+/*
+ * Cache reorganisation: gather-pack sink and selected tokens into the compact
+ * buffer (SFI page, Fig. 3B: sink and selected tokens packed into a
+ * contiguous compact buffer; Fig. 3A: reorganisation on the auxiliary
+ * stream).  For request b with ns = min(n_sink, seq_lens[b]) and k_eff = the
+ * number of entries of sel_idx[b, 0, :] before its first negative entry:
+ * row i < ns of KV head g is the token at position i; row ns + i is the
+ * token at position sel_idx[b, g, i].  Copies are bitwise.  n_compact[b] =
+ * ns + k_eff.  Rows from n_compact[b] to cap are not written.
+ *
+ *  sel_idx   [B, Hkv, k] int32 (as produced by sfi_select_topk)
+ *  compact_k [B, Hkv, cap, d] dtype, compact_v likewise; cap >= n_sink + k
+ *  n_compact [B] int32
+ */
+SFI_API sfi_status sfi_pack_compact(const sfi_shape* shape, const sfi_paged_kv* kv,
+                            const int32_t* seq_lens, int32_t n_sink, const int32_t* sel_idx,
+                            int32_t k, void* compact_k, void* compact_v, int32_t cap,
+                            int32_t* n_compact, void* stream);
+
+/*
+ * Fast step: sparse decode attention over the two-segment state.
+ * SFI page, Fig. 2 caption (fast steps attend to sink + selected + recent)
+ * and Fig. 3B (sink and selected stream from the contiguous compact buffer;
+ * recent tokens are read in place from paged KV).  One query token per
+ * request: out[b, h] = softmax attention of q[b, h] over compact rows
+ * [0, n_compact[b]) of KV head g(h) followed by the recent window.
+ *
+ *  q          [B, Hq, d] dtype
+ *  compact_k  [B, Hkv, cap, d] dtype, compact_v likewise
+ *  n_compact  [B] int32 (clamped to [0, cap])
+ *  out        [B, Hq, d] float32;  lse [B, Hq] float32 or NULL
+ *  workspace: at least sfi_sparse_decode_workspace_size() bytes.
+ */
+SFI_API sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                  const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                  const void* compact_k, const void* compact_v, int32_t cap,
+                                  const int32_t* n_compact, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+SFI_API sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                            int32_t cap, int32_t n_recent, size_t* bytes);
+
+/*
+ * Drafting and verifying requests in one launch (ASPIRE abstract: a unified
+ * mixed forward lets drafting and verifying requests share one batched
+ * pass; SparseSpec-L abstract: drafts attend over a sparse, recallable KV
+ * cache, verification is full-context attention that yields per-head
+ * statistics).  modes[b] = 0: request b drafts one token with the fast step
+ * (t_q[b] must be 1).  modes[b] = 1: request b verifies t_q[b] draft tokens
+ * with dense causal attention and writes its scores row.  BF16 only; B <= 64.
+ *
+ *  modes, t_q  host int32 [B]
+ *  q           [R, Hq, d] dtype, R = sum of t_q; request b's rows start at
+ *              the sum of t_q over requests before b
+ *  out         [R, Hq, d] float32;  lse [R, Hq] float32 or NULL
+ *  scores      [B, Hkv, score_stride] float32 or NULL; rows of drafting
+ *              requests are not written
+ *  compact_k/v, cap, n_compact as for sfi_sparse_decode_attn (used by
+ *              drafting requests only)
+ *  workspace: at least sfi_mixed_attn_workspace_size() bytes.
+ */
+SFI_API sfi_status sfi_mixed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                          const int32_t* modes, const int32_t* t_q, const int32_t* seq_lens,
+                          int32_t n_sink, int32_t n_recent, const void* compact_k,
+                          const void* compact_v, int32_t cap, const int32_t* n_compact,
+                          float* out, float* lse, float* scores, int64_t score_stride,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+SFI_API sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                         const int32_t* modes, const int32_t* t_q, int32_t cap,
+                                         int32_t n_recent, size_t* bytes);
+
+/*
+ * Launch plan of the split-K attention calls, for inspection and tests
+ * (host only, no GPU needed).  op: 0 = dense / verify (t_q as given),
+ * 1 = sparse decode.  Returns the tokens per split and splits per (b, g).
+ */
+SFI_API sfi_status sfi_plan_splits(int32_t op, const sfi_shape* shape, const sfi_paged_kv* kv,
+                           int32_t t_q, int32_t cap, int32_t n_recent,
+                           int32_t* split_tokens, int32_t* n_split);
+
+/*
+ * Measurement helper, not part of the decode path: a plain streaming copy
+ * of `bytes` bytes (a multiple of 16) from src to dst, used to calibrate
+ * hardware byte counters against a kernel of known traffic.
+ */
+SFI_API sfi_status sfi_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+SFI_API const char* sfi_status_string(sfi_status status);
+SFI_API const char* sfi_last_error(void);
+SFI_API int32_t sfi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFI_H_ */

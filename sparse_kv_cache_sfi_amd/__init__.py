@@ -1,0 +1,344 @@
+"""Python binding of libsfi, the SFI decode-attention path for MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libsfi.so`` behind the C ABI declared in ``include/sfi.h``.  PyTorch supplies
+device memory and streams.  There is no fallback: if the library is missing or
+a call fails, an exception is raised.
+
+Names follow that header:
+    dense_attn_with_stats  slow step (t_q = 1) / causal verification (t_q > 1)
+    select_topk            the Selector
+    pack_compact           gather-pack of sink + selected rows
+    sparse_decode_attn     fast step over compact + recent
+    mixed_attn             drafting and verifying requests in one launch
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "SfiError", "load", "dense_attn_with_stats", "select_topk", "pack_compact",
+    "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
+    "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfi.so")
+
+SFI_OK, SFI_ERR_INVALID_ARG, SFI_ERR_UNSUPPORTED, SFI_ERR_WORKSPACE, SFI_ERR_HIP = 0, 1, 2, 3, 4
+SFI_F32, SFI_BF16 = 0, 1
+PAGE_SIZE = 16
+
+
+class SfiShape(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("num_q_heads", c_int32), ("num_kv_heads", c_int32),
+                ("head_dim", c_int32), ("dtype", c_int32), ("scale", c_float)]
+
+
+class SfiPagedKV(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("block_table", c_void_p), ("max_pages", c_int32),
+                ("page_size", c_int32), ("num_pages", c_int32), ("max_seq_len", c_int32)]
+
+
+class SfiError(RuntimeError):
+    def __init__(self, status: int, call: str, message: str):
+        super().__init__(f"{call} failed with status {status}: {message}")
+        self.status = status
+
+
+_SHAPE_P, _KV_P = POINTER(SfiShape), POINTER(SfiPagedKV)
+_SIGS = {
+    "sfi_dense_attn_with_stats": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                  c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
+    "sfi_dense_attn_workspace_size": [_SHAPE_P, _KV_P, c_int32, POINTER(c_size_t)],
+    "sfi_select_topk": [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                        c_void_p, c_void_p, c_size_t, c_void_p],
+    "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, POINTER(c_size_t)],
+    "sfi_pack_compact": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                         c_void_p, c_void_p],
+    "sfi_sparse_decode_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                               c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "sfi_sparse_decode_workspace_size": [_SHAPE_P, _KV_P, c_int32, c_int32, POINTER(c_size_t)],
+    "sfi_mixed_attn": [_SHAPE_P, _KV_P, c_void_p, POINTER(c_int32), POINTER(c_int32), c_void_p, c_int32,
+                       c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                       c_void_p, c_size_t, c_void_p],
+    "sfi_mixed_attn_workspace_size": [_SHAPE_P, _KV_P, POINTER(c_int32), POINTER(c_int32), c_int32, c_int32,
+                                      POINTER(c_size_t)],
+    "sfi_plan_splits": [c_int32, _SHAPE_P, _KV_P, c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)],
+    "sfi_stream_copy": [c_void_p, c_void_p, c_size_t, c_void_p],
+    "sfi_status_string": [c_int32],
+    "sfi_last_error": [],
+    "sfi_version": [],
+}
+_RES = {"sfi_status_string": c_char_p, "sfi_last_error": c_char_p}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsfi.so from this package directory (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_kv_cache_sfi_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = _RES.get(name, c_int32)
+        _lib = lib
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != SFI_OK:
+        raise SfiError(st, name, lib.sfi_last_error().decode())
+
+
+# --------------------------------------------------------------------------- marshalling helpers
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SFI_BF16
+    if t.dtype == torch.float32:
+        return SFI_F32
+    raise TypeError(f"inputs must be bfloat16 or float32 (got {t.dtype})")
+
+
+def _stream(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _shape(B: int, Hq: int, Hkv: int, d: int, dtype: int, scale: Optional[float]) -> SfiShape:
+    return SfiShape(B, Hq, Hkv, d, dtype, float(scale if scale is not None else 1.0 / math.sqrt(d)))
+
+
+def _kv(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor, max_seq_len: int) -> SfiPagedKV:
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (block_table, "block_table")):
+        _dev(t, n)
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    if k_pool.shape != v_pool.shape or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool must have the same shape and dtype")
+    return SfiPagedKV(k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+                      k_pool.shape[2], k_pool.shape[0], int(max_seq_len))
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    _dev(t, name)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        return workspace
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# --------------------------------------------------------------------------- entry points
+
+def workspace_size(op: str, *, k_pool, block_table, Hq: int, dtype: torch.dtype, max_seq_len: int,
+                   t_q: int = 1, cap: int = 0, n_recent: int = 0, modes=None, t_q_per_req=None) -> int:
+    """Bytes of workspace the named call needs ('dense', 'sparse', 'select' or 'mixed')."""
+    B = block_table.shape[0]
+    num_pages, Hkv, P, d = k_pool.shape
+    shape = _shape(B, Hq, Hkv, d, SFI_BF16 if dtype == torch.bfloat16 else SFI_F32, None)
+    kv = SfiPagedKV(k_pool.data_ptr(), k_pool.data_ptr(), block_table.data_ptr(), block_table.shape[1], P,
+                    num_pages, int(max_seq_len))
+    out = c_size_t(0)
+    if op == "dense":
+        _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), t_q, ctypes.byref(out))
+    elif op == "sparse":
+        _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), cap, n_recent,
+              ctypes.byref(out))
+    elif op == "mixed":
+        m = (c_int32 * B)(*[int(x) for x in modes])
+        t = (c_int32 * B)(*[int(x) for x in t_q_per_req])
+        _call("sfi_mixed_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), m, t, cap, n_recent,
+              ctypes.byref(out))
+    else:
+        raise ValueError(op)
+    return int(out.value)
+
+
+def dense_attn_with_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, *, max_seq_len: int, n_sink: int = 0, n_recent: int = 0,
+                          scale: Optional[float] = None, with_scores: bool = True, score_stride: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None):
+    """Slow step / verification: q [B, t_q, Hq, d] -> (out [B, t_q, Hq, d] fp32, lse [B, t_q, Hq], scores
+    [B, Hkv, score_stride] or None)."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    B, t_q, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, t_q, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, t_q, Hq), dtype=torch.float32, device=dev)
+    if with_scores and scores is None:
+        stride = int(score_stride if score_stride is not None else max_seq_len)
+        scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
+    stride = scores.shape[-1] if scores is not None else 0
+    need = c_size_t(0)
+    _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), t_q, ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_dense_attn_with_stats", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), t_q,
+          seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), _ptr(scores), stride, _ptr(ws),
+          _nbytes(ws), _stream(stream, dev))
+    return out, lse, scores
+
+
+def select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, *, k: int, n_sink: int, n_recent: int,
+                t_q: int = 1, sel_idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Selector: scores [B, Hkv, stride] fp32 -> sel_idx [B, Hkv, k] int32 (ascending, -1 padded)."""
+    _dev(scores, "scores")
+    _i32(seq_lens, "seq_lens")
+    B, Hkv, stride = scores.shape
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=scores.device)
+    _call("sfi_select_topk", scores.data_ptr(), B, Hkv, stride, seq_lens.data_ptr(), t_q, n_sink, n_recent, k,
+          sel_idx.data_ptr(), None, 0, _stream(stream, scores.device))
+    return sel_idx
+
+
+def pack_compact(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                 sel_idx: torch.Tensor, *, n_sink: int, cap: int, max_seq_len: int,
+                 compact_k: Optional[torch.Tensor] = None, compact_v: Optional[torch.Tensor] = None,
+                 n_compact: Optional[torch.Tensor] = None, stream=None):
+    """Gather-pack: -> (compact_k, compact_v [B, Hkv, cap, d], n_compact [B] int32)."""
+    _i32(sel_idx, "sel_idx")
+    _i32(seq_lens, "seq_lens")
+    B, Hkv, k = sel_idx.shape
+    d = k_pool.shape[3]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hkv, Hkv, d, _dtype_code(k_pool), None)
+    dev = k_pool.device
+    if compact_k is None:
+        compact_k = torch.empty((B, Hkv, cap, d), dtype=k_pool.dtype, device=dev)
+    if compact_v is None:
+        compact_v = torch.empty((B, Hkv, cap, d), dtype=k_pool.dtype, device=dev)
+    if n_compact is None:
+        n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
+    _call("sfi_pack_compact", ctypes.byref(shape), ctypes.byref(kv), seq_lens.data_ptr(), n_sink,
+          sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
+          _stream(stream, dev))
+    return compact_k, compact_v, n_compact
+
+
+def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                       seq_lens: torch.Tensor, compact_k: torch.Tensor, compact_v: torch.Tensor,
+                       n_compact: torch.Tensor, *, n_sink: int, n_recent: int, max_seq_len: int,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Fast step: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq])."""
+    _dev(q, "q")
+    _dev(compact_k, "compact_k")
+    _dev(compact_v, "compact_v")
+    _i32(seq_lens, "seq_lens")
+    _i32(n_compact, "n_compact")
+    B, Hq, d = q.shape
+    Hkv, cap = compact_k.shape[1], compact_k.shape[2]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = c_size_t(0)
+    _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), cap, n_recent,
+          ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_sparse_decode_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
+          n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(),
+          _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
+    return out, lse
+
+
+def mixed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, modes: Sequence[int], t_q: Sequence[int], compact_k: torch.Tensor,
+               compact_v: torch.Tensor, n_compact: torch.Tensor, *, n_sink: int, n_recent: int, max_seq_len: int,
+               scale: Optional[float] = None, with_scores: bool = True, score_stride: Optional[int] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Drafting (mode 0) and verifying (mode 1) requests in one launch.  q [R, Hq, d] with R = sum(t_q)
+    -> (out [R, Hq, d], lse [R, Hq], scores [B, Hkv, stride] or None)."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    R, Hq, d = q.shape
+    B = len(modes)
+    Hkv, cap = compact_k.shape[1], compact_k.shape[2]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    m = (c_int32 * B)(*[int(x) for x in modes])
+    t = (c_int32 * B)(*[int(x) for x in t_q])
+    if out is None:
+        out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, Hq), dtype=torch.float32, device=dev)
+    if with_scores and scores is None:
+        stride = int(score_stride if score_stride is not None else max_seq_len)
+        scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
+    stride = scores.shape[-1] if scores is not None else 0
+    need = c_size_t(0)
+    _call("sfi_mixed_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), m, t, cap, n_recent,
+          ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_mixed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), m, t, seq_lens.data_ptr(),
+          n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(),
+          _ptr(lse), _ptr(scores), stride, _ptr(ws), _nbytes(ws), _stream(stream, dev))
+    return out, lse, scores
+
+
+def plan_splits(op: int, *, B: int, Hq: int, Hkv: int, d: int, bf16: bool, max_pages: int, num_pages: int,
+                max_seq_len: int, t_q: int = 1, cap: int = 0, n_recent: int = 0):
+    """(tokens per split, splits per (request, KV head)) chosen by the library; host only."""
+    shape = _shape(B, Hq, Hkv, d, SFI_BF16 if bf16 else SFI_F32, None)
+    kv = SfiPagedKV(16, 16, 16, max_pages, PAGE_SIZE, num_pages, max_seq_len)  # addresses unused by planning
+    st, ns = c_int32(0), c_int32(0)
+    _call("sfi_plan_splits", op, ctypes.byref(shape), ctypes.byref(kv), t_q, cap, n_recent, ctypes.byref(st),
+          ctypes.byref(ns))
+    return st.value, ns.value
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Calibration copy (not part of the decode path)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    n = min(_nbytes(src), _nbytes(dst))
+    _call("sfi_stream_copy", src.data_ptr(), dst.data_ptr(), n, _stream(stream, src.device))

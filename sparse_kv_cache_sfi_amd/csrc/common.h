@@ -1,0 +1,67 @@
+// Device helpers shared by the SFI kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfi {
+
+constexpr int kPage = 16;     // tokens per KV page
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;   // one 16-byte load
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// bfloat16 is the upper half of a float32: widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// v_dot2_f32_bf16: a.x*b.x + a.y*b.y + c with bf16 pairs (products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+// v_exp_f32 computes 2^x; exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of N consecutive lanes (N in {1,2,4,8,16}); every
+// lane of the group receives the group sum.  DPP quad_perm xor-1 / xor-2, then
+// row_half_mirror (pairs the two quads of 8 lanes), then row_mirror (pairs the
+// two halves of a 16-lane row).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Request length as the kernels use it: never beyond what the block table or the
+// launch plan can address.
+__device__ __forceinline__ int clamp_len(int L, int max_seq_len, int max_pages) {
+  return clampi(L, 0, min(max_seq_len, max_pages * kPage));
+}
+
+// Candidate range [lo, hi) of a slow step / verification with t_q query tokens.
+__device__ __forceinline__ void candidate_bounds(int L, int t_q, int n_sink, int n_recent, int* lo, int* hi) {
+  const int l = n_sink;
+  const int h = L - t_q + 1 - n_recent;
+  *lo = l;
+  *hi = h > l ? h : l;
+}
+
+}  // namespace sfi

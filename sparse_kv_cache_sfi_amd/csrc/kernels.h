@@ -1,0 +1,83 @@
+// Internal interface between the C-ABI layer (sfi_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfi {
+
+// Tokens processed by one work-group iteration of the split-K decode kernel is a
+// multiple of this; split sizes are rounded to it.
+constexpr int kDecodeTile = 64;
+// Largest split (tokens) a work-group handles; bounds the block-table slice it
+// stages in LDS.
+constexpr int kMaxSplitTokens = 4096;
+constexpr int kBtSlots = kMaxSplitTokens / 16 + 2;
+// Token tile of the MFMA verification kernel.
+constexpr int kVerifyTile = 32;
+// Largest batch of the mixed launch (its per-request plan travels in kernel arguments).
+constexpr int kMaxMixedBatch = 64;
+
+// Arguments of the split-K attention kernels (by value).
+struct AttnArgs {
+  int32_t Hq, Hkv;
+  int32_t max_pages, num_pages, max_seq_len;
+  const void* q;          // request b's rows start at q + b * q_stride_b elements
+  int64_t q_stride_b;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* ck;         // compact buffers [B, Hkv, cap, d] (sparse only)
+  const void* cv;
+  int32_t cap;
+  const int32_t* n_compact;
+  int32_t n_sink, n_recent;
+  float scale;            // logit scale
+  float scale_log2;       // scale * log2(e)
+  int32_t split_tokens, n_split;
+  int32_t t_q;            // query tokens of the request (dense / verify)
+  float* out;             // request b's rows start at out + b * out_stride_b
+  int64_t out_stride_b;
+  float* lse;             // request b's rows start at lse + b * lse_stride_b (nullable)
+  int64_t lse_stride_b;
+  float* part_o;          // split partials [rows, n_split, d]; row = b * rows_b + r
+  float* part_ml;         // [rows, n_split, 2] = (max in log2 units, sum)
+  int32_t rows_b;         // partial rows per request (t_q * Hq)
+  float* scores;          // [B, Hkv, score_stride] (nullable)
+  int64_t score_stride;
+};
+
+// Per-request plan of the mixed launch.
+struct MixedPlan {
+  int32_t n_req;
+  int32_t n_wg;                         // total work-groups
+  int32_t wg_begin[kMaxMixedBatch + 1]; // first work-group of each request (ordered list)
+  int32_t req[kMaxMixedBatch];          // request served by each list entry
+  int32_t mode[kMaxMixedBatch];         // 0 draft, 1 verify
+  int32_t t_q[kMaxMixedBatch];
+  int32_t q_row0[kMaxMixedBatch];       // first query row of the request
+  int32_t n_split[kMaxMixedBatch];
+  int32_t split_tokens[kMaxMixedBatch];
+};
+
+// Launchers.  Each returns hipGetLastError() after enqueueing.
+hipError_t launch_decode(const AttnArgs& a, int dtype, int d, int G, bool sparse, int B,
+                         hipStream_t stream);
+hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream);
+hipError_t launch_mixed(const AttnArgs& draft, const AttnArgs& verify, const MixedPlan& plan,
+                        int d, int G, hipStream_t stream);
+hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int n_split, int d,
+                          float* out, float* lse, hipStream_t stream);
+hipError_t launch_combine_mixed(const AttnArgs& draft, const AttnArgs& verify,
+                                const MixedPlan& plan, int d, hipStream_t stream);
+hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, const int32_t* seq_lens,
+                         int t_q, int n_sink, int n_recent, int k, int32_t* sel,
+                         hipStream_t stream);
+hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, int max_pages, int num_pages, int max_seq_len,
+                       const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck,
+                       void* cv, int cap, int32_t* n_compact, hipStream_t stream);
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace sfi

@@ -1,0 +1,119 @@
+// Cache reorganisation: gather-pack sink + selected tokens into the compact buffer.
+//
+// SFI page, Fig. 3B: sink and selected tokens are packed into a contiguous
+// compact buffer so that the fast step streams them sequentially; Fig. 3A runs
+// this reorganisation on the auxiliary stream.  Row i of (request b, KV head g)
+// is the token at position i for i < ns = min(n_sink, L_b), and the token at
+// sel_idx[b, g, i - ns] after that.  Each thread moves one 16-byte chunk of a
+// K row and of the matching V row (bitwise copy).  Positions outside [0, L_b),
+// or behind an invalid block-table entry, produce zero rows; negative entries
+// of sel_idx (padding) produce no row.
+#include "common.h"
+#include "kernels.h"
+
+namespace sfi {
+
+constexpr int kPackRowsPerBlock = 64;
+
+struct PackArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  int32_t max_pages, num_pages, max_seq_len, Hkv;
+  const int32_t* seq_lens;
+  int32_t n_sink;
+  const int32_t* sel;
+  int32_t k;
+  void* ck;
+  void* cv;
+  int32_t cap;
+  int32_t* n_compact;
+};
+
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
+  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;       // rows per pass of the work-group
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int L = clamp_len(p.seq_lens[b], p.max_seq_len, p.max_pages);
+  const int ns = min(p.n_sink, L);
+  const int32_t* srow = p.sel + ((int64_t)b * p.Hkv + g) * p.k;
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  const int chunk = threadIdx.x % CPR;
+  const int64_t dst_head = ((int64_t)b * p.Hkv + g) * p.cap;
+  const int64_t page_bytes = (int64_t)p.Hkv * kPage * ROW_BYTES;
+  const char* kp = reinterpret_cast<const char*>(p.k_pool);
+  const char* vp = reinterpret_cast<const char*>(p.v_pool);
+  char* ckp = reinterpret_cast<char*>(p.ck);
+  char* cvp = reinterpret_cast<char*>(p.cv);
+
+  for (int rr = threadIdx.x / CPR; rr < kPackRowsPerBlock; rr += RPP) {
+    const int i = blockIdx.x * kPackRowsPerBlock + rr;
+    if (i >= ns + p.k || i >= p.cap) continue;
+    const int pos = i < ns ? i : srow[i - ns];
+    if (pos < 0) continue;
+    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (pos < L) {
+      const int pg = bt[pos >> 4];
+      if (pg >= 0 && pg < p.num_pages) {
+        const int64_t off = (int64_t)pg * page_bytes + ((int64_t)g * kPage + (pos & 15)) * ROW_BYTES + chunk * 16;
+        kx = *reinterpret_cast<const u32x4*>(kp + off);
+        vx = *reinterpret_cast<const u32x4*>(vp + off);
+      }
+    }
+    const int64_t dst = (dst_head + i) * ROW_BYTES + chunk * 16;
+    *reinterpret_cast<u32x4*>(ckp + dst) = kx;
+    *reinterpret_cast<u32x4*>(cvp + dst) = vx;
+  }
+
+  if (blockIdx.x == 0 && g == 0) {
+    // n_compact[b] = ns + (entries of head 0's selection before its first negative one).
+    __shared__ int first_neg;
+    if (threadIdx.x == 0) first_neg = p.k;
+    __syncthreads();
+    const int32_t* s0 = p.sel + (int64_t)b * p.Hkv * p.k;
+    for (int i = threadIdx.x; i < p.k; i += 256)
+      if (s0[i] < 0) atomicMin(&first_neg, i);
+    __syncthreads();
+    if (threadIdx.x == 0) p.n_compact[b] = ns + first_neg;
+  }
+}
+
+hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, int max_pages, int num_pages, int max_seq_len,
+                       const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck, void* cv,
+                       int cap, int32_t* n_compact, hipStream_t stream) {
+  PackArgs p{k_pool, v_pool, block_table, max_pages, num_pages, max_seq_len, Hkv, seq_lens,
+             n_sink, sel, k, ck, cv, cap, n_compact};
+  const int rows = n_sink + k;
+  const dim3 grid((rows + kPackRowsPerBlock - 1) / kPackRowsPerBlock, Hkv, B), block(256);
+  const int row_bytes = d * (dtype == 1 ? 2 : 4);
+  switch (row_bytes) {
+    case 128: hipLaunchKernelGGL((pack_kernel<128>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((pack_kernel<256>), grid, block, 0, stream, p); break;
+    case 512: hipLaunchKernelGGL((pack_kernel<512>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- calibration copy
+// Plain streaming copy of n16 16-byte words; its hardware byte counters calibrate
+// the counters read on the attention kernels.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace sfi

@@ -1,0 +1,391 @@
+// C-ABI entry points of libsfi: host validation, split planning, workspace
+// sizing and kernel launches.  Every check runs before anything is enqueued, so
+// a rejected call launches nothing and touches no output.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/sfi.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sfi_status fail(sfi_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sfi_status ok() {
+  g_last_error.clear();
+  return SFI_OK;
+}
+
+sfi_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SFI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define SFI_TRY(expr)                 \
+  do {                                \
+    const sfi_status _s = (expr);     \
+    if (_s != SFI_OK) return _s;      \
+  } while (0)
+
+sfi_status check_shape(const sfi_shape* s) {
+  if (!s) return fail(SFI_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1) return fail(SFI_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(SFI_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads)
+    return fail(SFI_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", s->num_q_heads,
+                s->num_kv_heads);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SFI_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SFI_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->dtype != SFI_F32 && s->dtype != SFI_BF16)
+    return fail(SFI_ERR_INVALID_ARG, "dtype must be SFI_F32 or SFI_BF16 (got %d)", s->dtype);
+  if (!(s->scale > 0.f) || !std::isfinite(s->scale))
+    return fail(SFI_ERR_INVALID_ARG, "scale must be a positive finite number");
+  return SFI_OK;
+}
+
+sfi_status check_kv(const sfi_paged_kv* kv) {
+  if (!kv) return fail(SFI_ERR_INVALID_ARG, "kv descriptor is NULL");
+  if (!kv->k || !kv->v || !kv->block_table) return fail(SFI_ERR_INVALID_ARG, "kv.k, kv.v and kv.block_table must be non-NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(SFI_ERR_INVALID_ARG, "kv.k and kv.v must be 16-byte aligned");
+  if (kv->page_size != 16) return fail(SFI_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", kv->page_size);
+  if (kv->max_pages < 1 || kv->num_pages < 1)
+    return fail(SFI_ERR_INVALID_ARG, "max_pages and num_pages must be >= 1");
+  if (kv->max_seq_len < 1) return fail(SFI_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages * 16)
+    return fail(SFI_ERR_INVALID_ARG, "max_seq_len (%d) exceeds max_pages * page_size (%lld)", kv->max_seq_len,
+                (long long)kv->max_pages * 16);
+  return SFI_OK;
+}
+
+sfi_status check_ptr16(const void* p, const char* name, bool nullable = false) {
+  if (!p) return nullable ? SFI_OK : fail(SFI_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SFI_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return SFI_OK;
+}
+
+sfi_status check_budgets(int32_t n_sink, int32_t n_recent) {
+  if (n_sink < 0 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
+  return SFI_OK;
+}
+
+// Split-K plan: enough work-groups to fill the chip, but at least kMinSplit tokens
+// per split, at most kMaxSplitTokens, rounded to the decode tile.
+struct Split {
+  int tokens;
+  int n;
+};
+
+Split plan_split(int64_t units, int64_t n_tok, int tile) {
+  constexpr int64_t kMinSplit = 256;
+  constexpr int64_t kTargetWGs = 2048;
+  if (n_tok <= 0) return {tile, 1};
+  const int64_t by_min = (n_tok + kMinSplit - 1) / kMinSplit;
+  const int64_t want = (kTargetWGs + units - 1) / units;
+  int64_t ns = by_min < want ? by_min : want;
+  if (ns < 1) ns = 1;
+  int64_t st = (n_tok + ns - 1) / ns;
+  st = (st + tile - 1) / tile * tile;
+  if (st > sfi::kMaxSplitTokens) st = sfi::kMaxSplitTokens;
+  ns = (n_tok + st - 1) / st;
+  return {(int)st, (int)ns};
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of split partials: [rows, n_split, d] floats then [rows, n_split, 2].
+size_t partial_bytes(int64_t rows, int n_split, int d) {
+  if (n_split <= 1) return 0;
+  return align_up((size_t)rows * n_split * d * 4, 256) + align_up((size_t)rows * n_split * 2 * 4, 256);
+}
+
+Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
+  const int tile = t_q > 1 ? sfi::kVerifyTile : sfi::kDecodeTile;
+  return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, tile);
+}
+
+Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
+  const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
+  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile);
+}
+
+sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_t* seq_lens) {
+  sfi::AttnArgs a{};
+  a.Hq = s->num_q_heads;
+  a.Hkv = s->num_kv_heads;
+  a.max_pages = kv->max_pages;
+  a.num_pages = kv->num_pages;
+  a.max_seq_len = kv->max_seq_len;
+  a.k_pool = kv->k;
+  a.v_pool = kv->v;
+  a.block_table = kv->block_table;
+  a.seq_lens = seq_lens;
+  a.scale = s->scale;
+  a.scale_log2 = s->scale * sfi::kLog2e;
+  return a;
+}
+
+void set_partials(sfi::AttnArgs& a, void* ws, int64_t rows, int d) {
+  if (a.n_split <= 1) return;
+  char* p = static_cast<char*>(ws);
+  a.part_o = reinterpret_cast<float*>(p);
+  a.part_ml = reinterpret_cast<float*>(p + align_up((size_t)rows * a.n_split * d * 4, 256));
+}
+
+sfi_status check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return SFI_OK;
+  if (have < need) return fail(SFI_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", have, need);
+  if (!ws) return fail(SFI_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned16(ws)) return fail(SFI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return SFI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sfi_status sfi_dense_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, int32_t t_q, size_t* bytes) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
+  if (t_q < 1 || t_q > 16) return fail(SFI_ERR_INVALID_ARG, "t_q must be in [1, 16] (got %d)", t_q);
+  const Split sp = plan_dense(shape, kv, t_q);
+  *bytes = partial_bytes((int64_t)shape->batch * t_q * shape->num_q_heads, sp.n, shape->head_dim);
+  return ok();
+}
+
+sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, int32_t t_q,
+                                     const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
+                                     float* lse, float* scores, int64_t score_stride, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  SFI_TRY(check_ptr16(q, "q"));
+  SFI_TRY(check_ptr16(out, "out"));
+  if (!seq_lens) return fail(SFI_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (t_q < 1 || t_q > 16) return fail(SFI_ERR_INVALID_ARG, "t_q must be in [1, 16] (got %d)", t_q);
+  SFI_TRY(check_budgets(n_sink, n_recent));
+  if (scores && score_stride < kv->max_seq_len)
+    return fail(SFI_ERR_INVALID_ARG, "score_stride (%lld) must be >= max_seq_len (%d)", (long long)score_stride,
+                kv->max_seq_len);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (t_q > 1) {
+    if (shape->dtype != SFI_BF16) return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 needs bf16 inputs");
+    if (t_q * G > 64) return fail(SFI_ERR_UNSUPPORTED, "t_q * G must be <= 64 (got %d)", t_q * G);
+    return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 is not available in this build");
+  }
+  const Split sp = plan_dense(shape, kv, t_q);
+  const int64_t rows = (int64_t)shape->batch * t_q * shape->num_q_heads;
+  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
+
+  sfi::AttnArgs a = base_args(shape, kv, seq_lens);
+  a.q = q;
+  a.q_stride_b = (int64_t)t_q * shape->num_q_heads * shape->head_dim;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.split_tokens = sp.tokens;
+  a.n_split = sp.n;
+  a.t_q = t_q;
+  a.out = out;
+  a.out_stride_b = (int64_t)t_q * shape->num_q_heads * shape->head_dim;
+  a.lse = lse;
+  a.lse_stride_b = (int64_t)t_q * shape->num_q_heads;
+  a.rows_b = t_q * shape->num_q_heads;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  set_partials(a, workspace, rows, shape->head_dim);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (t_q == 1)
+    e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, false, shape->batch, st);
+  else
+    e = sfi::launch_verify(a, shape->head_dim, G, shape->batch, st);
+  if (e != hipSuccess) return hip_status(e, "attention launch");
+  if (sp.n > 1) {
+    e = sfi::launch_combine(a.part_o, a.part_ml, (int)rows, sp.n, shape->head_dim, out, lse, st);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return ok();
+}
+
+sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t k,
+                                          size_t* bytes) {
+  if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || num_kv_heads < 1 || score_stride < 1 || k < 1)
+    return fail(SFI_ERR_INVALID_ARG, "batch, num_kv_heads, score_stride and k must be >= 1");
+  *bytes = 0;
+  return ok();
+}
+
+sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_heads, int64_t score_stride,
+                           const int32_t* seq_lens, int32_t t_q, int32_t n_sink, int32_t n_recent, int32_t k,
+                           int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!scores || !seq_lens || !sel_idx) return fail(SFI_ERR_INVALID_ARG, "scores, seq_lens and sel_idx must be non-NULL");
+  if (batch < 1 || num_kv_heads < 1) return fail(SFI_ERR_INVALID_ARG, "batch and num_kv_heads must be >= 1");
+  if (score_stride < 1 || score_stride > INT32_MAX)
+    return fail(SFI_ERR_INVALID_ARG, "score_stride must be in [1, 2^31)");
+  if (k < 1) return fail(SFI_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (t_q < 1 || t_q > 16) return fail(SFI_ERR_INVALID_ARG, "t_q must be in [1, 16] (got %d)", t_q);
+  SFI_TRY(check_budgets(n_sink, n_recent));
+  const hipError_t e = sfi::launch_select(scores, batch, num_kv_heads, score_stride, seq_lens, t_q, n_sink, n_recent,
+                                          k, sel_idx, static_cast<hipStream_t>(stream));
+  return hip_status(e, "select launch");
+}
+
+sfi_status sfi_pack_compact(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens, int32_t n_sink,
+                            const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v, int32_t cap,
+                            int32_t* n_compact, void* stream) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!seq_lens || !sel_idx || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens, sel_idx and n_compact must be non-NULL");
+  SFI_TRY(check_ptr16(compact_k, "compact_k"));
+  SFI_TRY(check_ptr16(compact_v, "compact_v"));
+  if (k < 1) return fail(SFI_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (n_sink < 0) return fail(SFI_ERR_INVALID_ARG, "n_sink must be >= 0");
+  if ((int64_t)cap < (int64_t)n_sink + k)
+    return fail(SFI_ERR_INVALID_ARG, "cap (%d) must be >= n_sink + k (%lld)", cap, (long long)n_sink + k);
+  const hipError_t e = sfi::launch_pack(shape->dtype, shape->head_dim, shape->batch, shape->num_kv_heads, kv->k, kv->v,
+                                        kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len, seq_lens,
+                                        n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact,
+                                        static_cast<hipStream_t>(stream));
+  return hip_status(e, "pack launch");
+}
+
+sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, int32_t cap,
+                                            int32_t n_recent, size_t* bytes) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
+  if (cap < 0 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "cap and n_recent must be >= 0");
+  const Split sp = plan_sparse(shape, cap, n_recent, kv);
+  *bytes = partial_bytes((int64_t)shape->batch * shape->num_q_heads, sp.n, shape->head_dim);
+  return ok();
+}
+
+sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                  const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, const void* compact_k,
+                                  const void* compact_v, int32_t cap, const int32_t* n_compact, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  SFI_TRY(check_ptr16(q, "q"));
+  SFI_TRY(check_ptr16(out, "out"));
+  SFI_TRY(check_ptr16(compact_k, "compact_k"));
+  SFI_TRY(check_ptr16(compact_v, "compact_v"));
+  if (!seq_lens || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens and n_compact must be non-NULL");
+  SFI_TRY(check_budgets(n_sink, n_recent));
+  if (cap < 1) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1");
+  const Split sp = plan_sparse(shape, cap, n_recent, kv);
+  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
+  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
+
+  sfi::AttnArgs a = base_args(shape, kv, seq_lens);
+  a.q = q;
+  a.q_stride_b = (int64_t)shape->num_q_heads * shape->head_dim;
+  a.ck = compact_k;
+  a.cv = compact_v;
+  a.cap = cap;
+  a.n_compact = n_compact;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.split_tokens = sp.tokens;
+  a.n_split = sp.n;
+  a.t_q = 1;
+  a.out = out;
+  a.out_stride_b = (int64_t)shape->num_q_heads * shape->head_dim;
+  a.lse = lse;
+  a.lse_stride_b = shape->num_q_heads;
+  a.rows_b = shape->num_q_heads;
+  set_partials(a, workspace, rows, shape->head_dim);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipError_t e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, true, shape->batch, st);
+  if (e != hipSuccess) return hip_status(e, "sparse decode launch");
+  if (sp.n > 1) {
+    e = sfi::launch_combine(a.part_o, a.part_ml, (int)rows, sp.n, shape->head_dim, out, lse, st);
+    if (e != hipSuccess) return hip_status(e, "combine launch");
+  }
+  return ok();
+}
+
+sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,
+                                         const int32_t* t_q, int32_t cap, int32_t n_recent, size_t* bytes) {
+  (void)shape; (void)kv; (void)modes; (void)t_q; (void)cap; (void)n_recent; (void)bytes;
+  return fail(SFI_ERR_UNSUPPORTED, "mixed launch not available in this build");
+}
+
+sfi_status sfi_mixed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, const int32_t* modes,
+                          const int32_t* t_q, const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                          const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
+                          float* out, float* lse, float* scores, int64_t score_stride, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  (void)shape; (void)kv; (void)q; (void)modes; (void)t_q; (void)seq_lens; (void)n_sink; (void)n_recent;
+  (void)compact_k; (void)compact_v; (void)cap; (void)n_compact; (void)out; (void)lse; (void)scores;
+  (void)score_stride; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(SFI_ERR_UNSUPPORTED, "mixed launch not available in this build");
+}
+
+sfi_status sfi_plan_splits(int32_t op, const sfi_shape* shape, const sfi_paged_kv* kv, int32_t t_q, int32_t cap,
+                           int32_t n_recent, int32_t* split_tokens, int32_t* n_split) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!split_tokens || !n_split) return fail(SFI_ERR_INVALID_ARG, "output pointers are NULL");
+  Split sp;
+  if (op == 0) {
+    if (t_q < 1 || t_q > 16) return fail(SFI_ERR_INVALID_ARG, "t_q must be in [1, 16] (got %d)", t_q);
+    sp = plan_dense(shape, kv, t_q);
+  } else if (op == 1) {
+    if (cap < 0 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "cap and n_recent must be >= 0");
+    sp = plan_sparse(shape, cap, n_recent, kv);
+  } else {
+    return fail(SFI_ERR_INVALID_ARG, "op must be 0 (dense) or 1 (sparse)");
+  }
+  *split_tokens = sp.tokens;
+  *n_split = sp.n;
+  return ok();
+}
+
+sfi_status sfi_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  SFI_TRY(check_ptr16(src, "src"));
+  SFI_TRY(check_ptr16(dst, "dst"));
+  if (bytes % 16) return fail(SFI_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  return hip_status(sfi::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy launch");
+}
+
+const char* sfi_status_string(sfi_status status) {
+  switch (status) {
+    case SFI_OK: return "SFI_OK";
+    case SFI_ERR_INVALID_ARG: return "SFI_ERR_INVALID_ARG";
+    case SFI_ERR_UNSUPPORTED: return "SFI_ERR_UNSUPPORTED";
+    case SFI_ERR_WORKSPACE: return "SFI_ERR_WORKSPACE";
+    case SFI_ERR_HIP: return "SFI_ERR_HIP";
+  }
+  return "SFI_ERR_UNKNOWN";
+}
+
+const char* sfi_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sfi_version(void) { return SFI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/sfi.h declares,
+rejects bad arguments with the documented status before launching anything, and
+plans splits / workspaces consistently.  No compute call is made here (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_kv_cache_sfi_amd as sfi
+from sparse_kv_cache_sfi_amd import SfiPagedKV, SfiShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfi.h")
+
+FAKE = 0x10000            # a 16-byte aligned address; never dereferenced by a rejected call
+MISALIGNED = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sfi.load()
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^SFI_API\s+[\w\s\*]+?\b(sfi_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
+              "sfi_mixed_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_symbols():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sfi_version() == 10000
+    assert lib.sfi_status_string(0) == b"SFI_OK"
+    assert lib.sfi_status_string(3) == b"SFI_ERR_WORKSPACE"
+    assert lib.sfi_status_string(99) == b"SFI_ERR_UNKNOWN"
+
+
+def _shape(B=1, Hq=16, Hkv=8, d=128, dtype=1, scale=0.088):
+    return SfiShape(B, Hq, Hkv, d, dtype, scale)
+
+
+def _kv(k=FAKE, v=FAKE, bt=FAKE, max_pages=1024, page=16, num_pages=1024, max_len=16384):
+    return SfiPagedKV(k, v, bt, max_pages, page, num_pages, max_len)
+
+
+def _dense(lib, shape, kv, q=FAKE, t_q=1, lens=FAKE, n_sink=4, n_recent=64, out=FAKE, lse=FAKE, scores=FAKE,
+           stride=16384, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sfi_dense_attn_with_stats(ctypes.byref(shape) if shape is not None else None,
+                                         ctypes.byref(kv) if kv is not None else None, q, t_q, lens, n_sink,
+                                         n_recent, out, lse, scores, stride, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda a: a.update(shape=None), 1, "shape is NULL"),
+    (lambda a: a.update(kv=None), 1, "kv descriptor"),
+    (lambda a: a.update(shape=_shape(Hq=24)), 2, "1, 2, 4 or 8"),
+    (lambda a: a.update(shape=_shape(Hq=15)), 1, "multiple"),
+    (lambda a: a.update(shape=_shape(d=96)), 2, "head_dim"),
+    (lambda a: a.update(shape=_shape(dtype=7)), 1, "dtype"),
+    (lambda a: a.update(shape=_shape(scale=-1.0)), 1, "scale"),
+    (lambda a: a.update(shape=_shape(B=0)), 1, "batch"),
+    (lambda a: a.update(kv=_kv(page=32)), 2, "page_size"),
+    (lambda a: a.update(kv=_kv(max_len=20000)), 1, "max_seq_len"),
+    (lambda a: a.update(kv=_kv(k=MISALIGNED)), 1, "aligned"),
+    (lambda a: a.update(kv=_kv(bt=0)), 1, "non-NULL"),
+    (lambda a: a.update(q=0), 1, "q is NULL"),
+    (lambda a: a.update(q=MISALIGNED), 1, "q must be 16-byte aligned"),
+    (lambda a: a.update(out=0), 1, "out is NULL"),
+    (lambda a: a.update(lens=0), 1, "seq_lens"),
+    (lambda a: a.update(t_q=0), 1, "t_q"),
+    (lambda a: a.update(t_q=17), 1, "t_q"),
+    (lambda a: a.update(n_sink=-1), 1, "n_sink"),
+    (lambda a: a.update(stride=100), 1, "score_stride"),
+    (lambda a: a.update(ws_bytes=10), 3, "workspace"),
+    (lambda a: a.update(ws=0), 1, "workspace is NULL"),
+    (lambda a: a.update(shape=_shape(dtype=0), t_q=4), 2, "bf16"),
+    (lambda a: a.update(shape=_shape(Hq=64, Hkv=8), t_q=16), 2, "<= 64"),
+])
+def test_dense_rejects_bad_arguments(lib, mutate, status, msg):
+    args = dict(shape=_shape(), kv=_kv())
+    mutate(args)
+    st = _dense(lib, **args)
+    assert st == status, (st, lib.sfi_last_error())
+    assert msg in lib.sfi_last_error().decode()
+
+
+def test_select_rejects_bad_arguments(lib):
+    ok = dict(scores=FAKE, B=1, H=8, stride=16384, lens=FAKE, t_q=1, ns=4, nr=64, k=100, sel=FAKE)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.sfi_select_topk(a["scores"], a["B"], a["H"], a["stride"], a["lens"], a["t_q"], a["ns"], a["nr"],
+                                   a["k"], a["sel"], None, 0, None)
+    assert call(scores=0) == 1
+    assert call(sel=0) == 1
+    assert call(k=0) == 1 and "k must be" in lib.sfi_last_error().decode()
+    assert call(B=0) == 1
+    assert call(stride=0) == 1
+    assert call(t_q=0) == 1
+    assert call(nr=-3) == 1
+
+
+def test_pack_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def call(ck=FAKE, cv=FAKE, cap=200, k=100, n_sink=4, nc=FAKE, sel=FAKE):
+        return lib.sfi_pack_compact(ctypes.byref(shape), ctypes.byref(kv), FAKE, n_sink, sel, k, ck, cv, cap, nc,
+                                    None)
+    assert call(cap=103) == 1 and "cap" in lib.sfi_last_error().decode()
+    assert call(ck=MISALIGNED) == 1
+    assert call(nc=0) == 1
+    assert call(sel=0) == 1
+    assert call(k=0) == 1
+    assert call(n_sink=-1) == 1
+
+
+def test_sparse_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def call(q=FAKE, ck=FAKE, cap=2048, nc=FAKE, ws=FAKE, ws_bytes=1 << 40, n_recent=64, out=FAKE):
+        return lib.sfi_sparse_decode_attn(ctypes.byref(shape), ctypes.byref(kv), q, FAKE, 4, n_recent, ck, FAKE, cap,
+                                          nc, out, FAKE, ws, ws_bytes, None)
+    assert call(q=MISALIGNED) == 1
+    assert call(ck=0) == 1
+    assert call(nc=0) == 1
+    assert call(cap=0) == 1
+    assert call(n_recent=-1) == 1
+    assert call(out=0) == 1
+    assert call(ws_bytes=1) == 3
+
+
+def test_workspace_queries_match_the_plan(lib):
+    shape, kv = _shape(), _kv()
+    st, ns = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.sfi_plan_splits(0, ctypes.byref(shape), ctypes.byref(kv), 1, 0, 0, ctypes.byref(st),
+                               ctypes.byref(ns)) == 0
+    size = ctypes.c_size_t()
+    assert lib.sfi_dense_attn_workspace_size(ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(size)) == 0
+    if ns.value > 1:
+        assert size.value >= 16 * ns.value * (128 + 2) * 4
+    else:
+        assert size.value == 0
+
+
+@pytest.mark.parametrize("B,Hkv,n_tok", [(1, 8, 16384), (1, 8, 256), (16, 8, 32768), (4, 8, 65536),
+                                         (8, 8, 131072), (1, 1, 1), (3, 2, 3000), (64, 8, 100)])
+def test_split_plan_covers_every_token(B, Hkv, n_tok):
+    st, ns = sfi.plan_splits(0, B=B, Hq=4 * Hkv, Hkv=Hkv, d=128, bf16=True, max_pages=(n_tok + 15) // 16,
+                             num_pages=1, max_seq_len=n_tok)
+    assert st % 64 == 0 and 64 <= st <= 4096
+    assert ns * st >= n_tok and (ns - 1) * st < n_tok
+    assert ns == 1 or st >= 256 or B * Hkv * ns >= 2048
+
+
+def test_split_plan_of_the_16k_decode_layer():
+    # 1 request x 8 KV heads x 16384 tokens: 64 splits of 256 tokens -> 512 work-groups.
+    assert sfi.plan_splits(0, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384) == (256, 64)
+    # fast step, 1.6 % retention: 192 compact slots + 64 recent -> a single split
+    assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=192, n_recent=64) == (256, 1)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        sfi.select_topk(torch.zeros((1, 1, 8)), torch.zeros(1, dtype=torch.int32), k=2, n_sink=0, n_recent=0)
