@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the SFI decode-attention path on one MI355X.
+
+Workload (the layer the headline metric is quoted on): a Qwen3-0.6B-shaped
+decode layer in bf16 - batch 1, 16 query heads on 8 KV heads, head_dim 128,
+KV length 16384, page size 16, sink 4, recent 64.  One step is one pass of the
+whole t_q = 1 path on one batch:
+
+    slow step   dense attention + masked group logits        (main stream)
+    Selector    top-k per KV head, k = 1980 (12.5 % retention) (aux stream)
+    pack        gather-pack sink + selected into the compact buffer (aux stream)
+    fast step   sparse attention over compact + recent       (main stream, after pack)
+
+`value` = algorithmic KV bytes of the step (dense K/V read, pack read + write,
+fast-step K/V read) / step time.  Inputs are resident in HBM before timing;
+every step uses another of R replicas so the working set (>= 512 MiB) exceeds
+the 256 MB Infinity Cache.
+
+Also reported (same process, outside the timed steps): the retention sweep of
+the fast step against dense attention at 16K (batch 1 and batch 16), the dense
+kernel's HBM roofline fraction, and the fp64 oracle's throughput on host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode-attn effective KV GB/s (% HBM peak) + speedup vs dense at 16K"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def upload(a, dev):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def make_layers(n, L, B, frac, dev, seed0):
+    from sfi_synth import qwen06b_decode_case
+    out = []
+    for r in range(n):
+        c = qwen06b_decode_case(seed0 + r, L=L, B=B, frac=frac)
+        out.append(dict(case=c, k=upload(c.kv.k, dev), v=upload(c.kv.v, dev), bt=upload(c.kv.block_table, dev),
+                        lens=upload(c.seq_lens.astype("int32"), dev), q=upload(c.q, dev),
+                        q1=upload(c.q[:, 0], dev)))
+    return out
+
+
+def kv_bytes_dense(B, Hkv, L, d, esize=2):
+    return B * Hkv * L * 2 * d * esize
+
+
+def time_loop(fn, n, stream):
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for i in range(n):
+        fn(i)
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / n * 1e-3   # seconds per call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_kv_cache_sfi_amd as sfi
+
+    sfi.load()
+    dev = torch.device("cuda:0")
+    L, B, Hq, Hkv, d = 16384, 1, 16, 8, 128
+    n_sink, n_recent = 4, 64
+    frac = (1, 8)
+    R = args.replicas
+    log(f"generating {R} replicas of the 16K layer")
+    layers = make_layers(R, L, B, frac, dev, 1000)
+    c0 = layers[0]["case"]
+    k_sel = c0.k_sel
+    cap = n_sink + k_sel
+    max_len = L
+    main_s = torch.cuda.current_stream(dev)
+    aux_s = torch.cuda.Stream(device=dev)
+
+    # per-replica outputs and buffers, all allocated before timing
+    for ly in layers:
+        ly["out"] = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
+        ly["lse"] = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+        ly["scores"] = torch.empty((B, Hkv, max_len), dtype=torch.float32, device=dev)
+        ly["sel"] = torch.empty((B, Hkv, k_sel), dtype=torch.int32, device=dev)
+        ly["ck"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+        ly["cv"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+        ly["nc"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        ly["fout"] = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        ly["flse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ex = layers[0]
+    ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
+                                              dtype=torch.bfloat16, max_seq_len=max_len) + 16,
+                           dtype=torch.uint8, device=dev)
+    ws_sparse = torch.zeros(sfi.workspace_size("sparse", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
+                                               dtype=torch.bfloat16, max_seq_len=max_len, cap=cap,
+                                               n_recent=n_recent) + 16, dtype=torch.uint8, device=dev)
+    dense_ev = []
+
+    def step(i, record=False):
+        ly = layers[i % R]
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main_s)
+        sfi.dense_attn_with_stats(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
+                                  n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
+                                  scores=ly["scores"], workspace=ws_dense, stream=main_s)
+        if record:
+            e1.record(main_s)
+            dense_ev.append((e0, e1))
+        ready = torch.cuda.Event()
+        ready.record(main_s)
+        aux_s.wait_event(ready)
+        sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"],
+                        stream=aux_s)
+        sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
+                         max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
+                         stream=aux_s)
+        packed = torch.cuda.Event()
+        packed.record(aux_s)
+        main_s.wait_event(packed)
+        sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"], ly["cv"], ly["nc"],
+                               n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=ly["fout"],
+                               lse=ly["flse"], workspace=ws_sparse, stream=main_s)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0e.record(main_s)
+    for i in range(args.steps):
+        step(i, record=True)
+    t1e.record(main_s)
+    torch.cuda.synchronize()
+    step_s = t0e.elapsed_time(t1e) * 1e-3 / args.steps
+    dense_s = float(np.mean([a.elapsed_time(b) for a, b in dense_ev])) * 1e-3
+
+    esize = 2
+    n_c = cap
+    dense_kv = kv_bytes_dense(B, Hkv, L, d, esize)
+    pack_bytes = 2 * B * Hkv * n_c * 2 * d * esize
+    fast_kv = B * Hkv * (n_c + n_recent) * 2 * d * esize
+    step_bytes = dense_kv + pack_bytes + fast_kv
+    value = step_bytes / step_s / 1e9
+    dense_alg = dense_kv + B * Hkv * L * 4            # K/V read + scores written
+    roof = {"kernel": "decode_kernel<bf16,d128,G2,dense+scores> (slow step)", "bound": "hbm",
+            "achieved": dense_alg / dense_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+            "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6}
+    log(f"step {step_s * 1e6:.1f} us, {value:.0f} GB/s; dense kernel {dense_s * 1e6:.1f} us "
+        f"= {roof['achieved']:.0f} GB/s ({100 * roof['frac']:.1f}% of peak)")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: B=1, Hq=16, Hkv=8, d=128, page 16, "
+                               "sink 4, recent 64, selected 1980 (12.5% retention); step = slow step "
+                               "(dense + logits) + Selector + pack (aux stream) + fast step",
+                   "global_batch": B, "seq_len": L, "replicas": R, "step_kv_bytes": step_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": roof,
+    }
+
+    if not args.no_sweep:
+        result["sweep"] = sweep(sfi, layers, dev, main_s, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense, ws_sparse)
+        log("batch-16 sweep")
+        big = make_layers(1, L, 16, frac, dev, 5000)
+        result["sweep_b16"] = sweep(sfi, big, dev, main_s, 16, Hq, Hkv, d, L, n_sink, n_recent, None, None)
+        del big
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, L, B, frac, n_sink, n_recent, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense, ws_sparse):
+    """Fast step at each Table 1 retention vs plain dense attention at the same shape."""
+    import torch
+    from sfi_synth import RETENTIONS, retention_budget
+    R = len(layers)
+    max_len = L
+    ex = layers[0]
+    if ws_dense is None:
+        ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
+                                                  dtype=torch.bfloat16, max_seq_len=max_len) + 16,
+                               dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev) for _ in range(R)]
+    lses = [torch.empty((B, 1, Hq), dtype=torch.float32, device=dev) for _ in range(R)]
+    n_rep = max(20, 400 // R * R)
+
+    def dense(i):
+        ly = layers[i % R]
+        sfi.dense_attn_with_stats(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
+                                  with_scores=False, out=outs[i % R], lse=lses[i % R], workspace=ws_dense,
+                                  stream=stream)
+    for i in range(R):
+        dense(i)
+    t_dense = time_loop(dense, n_rep, stream)
+    dense_kv = kv_bytes_dense(B, Hkv, L, d)
+    rows = []
+    rng = __import__("numpy").random.default_rng(9)
+    for frac in RETENTIONS:
+        k = retention_budget(L, frac, n_sink, n_recent)
+        cap = n_sink + max(k, 1)
+        # selection: k random candidates per (b, g) (the fast step's cost does not depend on which)
+        import numpy as np
+        lo, hi = n_sink, L - n_recent
+        comp = []
+        for ly in layers:
+            sel = np.full((B, Hkv, max(k, 1)), -1, np.int32)
+            for b in range(B):
+                for g in range(Hkv):
+                    if k:
+                        sel[b, g, :k] = np.sort(rng.choice(np.arange(lo, hi), k, replace=False))
+            sel_d = torch.from_numpy(sel).to(dev)
+            ck, cv, nc = sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], sel_d, n_sink=n_sink, cap=cap,
+                                          max_seq_len=max_len, stream=stream)
+            comp.append((ck, cv, nc, torch.empty((B, Hq, d), dtype=torch.float32, device=dev),
+                         torch.empty((B, Hq), dtype=torch.float32, device=dev)))
+        ws = torch.zeros(sfi.workspace_size("sparse", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
+                                            dtype=torch.bfloat16, max_seq_len=max_len, cap=cap, n_recent=n_recent)
+                         + 16, dtype=torch.uint8, device=dev)
+
+        def fast(i):
+            ly = layers[i % R]
+            ck, cv, nc, o, l = comp[i % R]
+            sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ck, cv, nc, n_sink=n_sink,
+                                   n_recent=n_recent, max_seq_len=max_len, out=o, lse=l, workspace=ws,
+                                   stream=stream)
+        for i in range(R):
+            fast(i)
+        t = time_loop(fast, n_rep, stream)
+        kv = B * Hkv * (n_sink + k + n_recent) * 2 * d * 2
+        r = (n_sink + k + n_recent) / L
+        rows.append({"retention_pct": round(100 * r, 2), "selected": k, "fast_us": round(t * 1e6, 2),
+                     "fast_GBps": round(kv / t / 1e9, 1), "fast_pct_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 1),
+                     "dense_us": round(t_dense * 1e6, 2), "dense_GBps": round(dense_kv / t_dense / 1e9, 1),
+                     "speedup": round(t_dense / t, 3), "speedup_x_r": round(t_dense / t * r, 3)})
+        del comp
+    log("sweep " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows))
+    return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows}
+
+
+def cpu_baseline(budget_s, L, B, frac, n_sink, n_recent, step_bytes):
+    """The fp64 oracle timed on host cores on the same workload (one request, all 8 KV heads), one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    from sfi_synth import qwen06b_decode_case
+    c = qwen06b_decode_case(1000, L=L, B=B, frac=frac)
+    t_start = time.perf_counter()
+    n = 0
+    with threadpool_limits(limits=1):
+        while True:
+            b = 0
+            Qv = c.q_values()[b]
+            O.dense_attention(Qv, c.kv.k, c.kv.v, c.kv.block_table[b], L, c.scale, c.Hkv, kv_dtype="bf16")
+            S = O.group_scores(Qv, c.kv.k, c.kv.block_table[b], L, c.scale, c.Hkv, n_sink, n_recent, L,
+                               kv_dtype="bf16")
+            lo, hi = O.candidate_range(L, 1, n_sink, n_recent)
+            sel = np.stack([O.select_topk(S[g].astype(np.float32), lo, hi, c.k_sel) for g in range(c.Hkv)])
+            ck, cv, nc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, sel, n_sink + c.k_sel)
+            O.sparse_decode(Qv[0], ck, cv, nc, c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, n_recent, c.scale,
+                            kv_dtype="bf16")
+            n += 1
+            if time.perf_counter() - t_start >= budget_s:
+                break
+    dt = (time.perf_counter() - t_start) / n
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full steps of the same 16K layer (slow step + Selector + pack + fast step, "
+                      f"1 request x 8 KV heads), fp64 NumPy, one thread; {dt:.2f} s per step",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,10 @@
  *  - Outputs out / lse are float32; lse is the natural-log sum of exp(logit)
  *    over the keys seen, logit = scale * q . k.  A row that sees no key gets
  *    out = 0 and lse = -inf.
+ *  - Workspaces: a workspace must be zero-filled before its first use (it
+ *    starts with split-K arrival counters); every call leaves those counters
+ *    at zero again, so one workspace may serve calls of any shape.  Calls
+ *    that share a workspace must be ordered on one stream (or by events).
  *  - Calls only enqueue work on `stream` (a hipStream_t, NULL = default
  *    stream) and return without synchronising.  Ordering across streams is
  *    the caller's job (events).

@@ -157,7 +157,8 @@ def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Option
         return workspace
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    # Zero-filled: the split-K arrival counters at its start must read zero on first use.
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def _nbytes(t: Optional[torch.Tensor]) -> int:

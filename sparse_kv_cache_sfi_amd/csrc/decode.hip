@@ -48,7 +48,8 @@ struct DecodeShape {
   static constexpr int U = (LPR == 16 && C == 1) ? 4 : 2;      // slots per iteration
   static constexpr int WAVES = 4;
   static constexpr int TILE = WAVES * U * ROWS;                // tokens per work-group iteration
-  static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4;
+  static constexpr int TAIL = 2 * kMaxSplits * G * 4 + 2 * G * 4;   // split tail: (w, l) per split, M and L per head
+  static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4 + 16 + TAIL;
   static_assert(C >= 1, "row too short for the lane mapping");
 };
 
@@ -71,6 +72,84 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
   acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
   acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
   return acc;
+}
+
+// Split partials cross XCDs, whose L2 caches are not coherent with each other.
+// They are written and read with agent-scope atomic accesses (coherent at the
+// device level, no cache-wide write-back or invalidate), and the writer drains
+// its stores before it takes a ticket.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K tail: the last work-group of (b, g) to finish merges all splits of the
+// group's G query heads in fixed split order (M = max m_s; out = sum 2^(m_s - M) o_s
+// / sum 2^(m_s - M) l_s; lse = (M + log2 of that sum) * ln 2; an empty split adds 0)
+// and returns the arrival counter to zero.  All (m, l) pairs are fetched at once
+// into LDS; each output element then streams its ns partials in batches of 8.
+template <int D, int G>
+__device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const int g, int* flag, float* tail) {
+  constexpr int NT = 256;
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const int ticket = __hip_atomic_fetch_add(&a.counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
+    *flag = (ticket == a.n_split - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+  const int ns = a.n_split;
+  float* w_s = tail;                   // [G][ns]: m, then the weight 2^(m - M)
+  float* l_s = tail + G * kMaxSplits;  // [G][ns]
+  float* M_h = tail + 2 * G * kMaxSplits;
+  float* L_h = M_h + G;
+  const int64_t row0 = (int64_t)b * a.rows_b + g * G;
+  for (int i = tid; i < G * ns; i += NT) {
+    const int h = i / ns, s = i % ns;
+    const float* ml = a.part_ml + ((row0 + h) * ns + s) * 2;
+    w_s[h * kMaxSplits + s] = load_coherent(ml);
+    l_s[h * kMaxSplits + s] = load_coherent(ml + 1);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = neg_inf();
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, w_s[tid * kMaxSplits + s]);
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float m = w_s[tid * kMaxSplits + s];
+      const float wt = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
+      w_s[tid * kMaxSplits + s] = wt;
+      L = fmaf(wt, l_s[tid * kMaxSplits + s], L);
+    }
+    M_h[tid] = M;
+    L_h[tid] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int h = idx / D, e = idx % D;
+    const float* po = a.part_o + (row0 + h) * ns * D + e;
+    const float* wh = w_s + h * kMaxSplits;
+    float os = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (s0 + j < ns) ? load_coherent(po + (int64_t)(s0 + j) * D) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ns) os = fmaf(wh[s0 + j], v[j], os);
+    }
+    const float ls = L_h[h];
+    const int hq = g * G + h;
+    a.out[(int64_t)b * a.out_stride_b + (int64_t)hq * D + e] = ls > 0.f ? os / ls : 0.f;
+    if (e == 0 && a.lse)
+      a.lse[(int64_t)b * a.lse_stride_b + hq] = ls > 0.f ? (M_h[h] + log2f(ls)) * kLn2 : neg_inf();
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 template <typename T, int D, int G, bool SPARSE, bool SCORES>
@@ -151,36 +230,39 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   struct Buf {
     u32x4 k[U][C];
     u32x4 v[U][C];
-    int pos[U];
-    bool in[U];  // inside this split's token range
-    bool ok[U];  // and backed by a valid page
   };
 
+  // Where slot u of iteration `it` comes from: its position p, whether it lies in
+  // this split (in) and whether it is backed by a compact row or a valid page (ok).
+  auto locate = [&](int it, int u, int& vi, int& p, bool& in, bool& compact, int& pg, bool& ok) {
+    vi = t0 + it * TILE + (w * U + u) * ROWS + r;
+    in = vi < t1;
+    compact = SPARSE && vi < n_c;
+    p = compact ? vi : rs + vi - n_c;
+    const int slot = in && !compact ? (p >> 4) - pg_lo : 0;
+    pg = bt_s[slot];
+    ok = in && (compact || pg >= 0);
+  };
+
+  // Issue the loads of one iteration.  Every lane always loads (rows outside the
+  // split or behind an invalid page read row 0 of the pool and are masked), so the
+  // loop carries no conditionally-loaded registers.
   auto issue = [&](int it, Buf& B) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int vi = t0 + it * TILE + (w * U + u) * ROWS + r;
-      const bool in = vi < t1;
-      bool ok = in;
-      const T* kr = kpool;
-      const T* vr = vpool;
-      int p = vi;
-      if (SPARSE && vi < n_c) {
-        kr = ckb + (int64_t)vi * D;
-        vr = cvb + (int64_t)vi * D;
-      } else {
-        p = rs + vi - n_c;
-        const int pg = in ? bt_s[(p >> 4) - pg_lo] : -1;
-        ok = in && pg >= 0;
-        if (ok) {
-          const int64_t off = (int64_t)pg * page_elems + head_off + (int64_t)(p & 15) * D;
-          kr = kpool + off;
-          vr = vpool + off;
+      int vi, p, pg;
+      bool in, compact, ok;
+      locate(it, u, vi, p, in, compact, pg, ok);
+      int64_t off = (int64_t)(pg < 0 ? 0 : pg) * page_elems + head_off + (int64_t)(p & 15) * D;
+      off = ok ? off : 0;
+      const T* kr = kpool + off;
+      const T* vr = vpool + off;
+      if constexpr (SPARSE) {
+        if (compact) {
+          kr = ckb + (int64_t)vi * D;
+          vr = cvb + (int64_t)vi * D;
         }
       }
-      B.pos[u] = p;
-      B.in[u] = in;
-      B.ok[u] = ok;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         B.k[u][c] = *reinterpret_cast<const u32x4*>(kr + (c * LPR + sub) * EPC);
@@ -189,7 +271,15 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   };
 
-  auto compute = [&](const Buf& B) {
+  auto compute = [&](int it, const Buf& B) {
+    bool in_[U], ok_[U];
+    int pos_[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int vi, pg;
+      bool compact;
+      locate(it, u, vi, pos_[u], in_[u], compact, pg, ok_[u]);
+    }
     float s[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -203,12 +293,12 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     if constexpr (SCORES) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (sub == 0 && B.in[u]) {
+        if (sub == 0 && in_[u]) {
           float sc = 0.f;
 #pragma unroll
           for (int h = 0; h < G; ++h) sc += s[u][h];
-          const int j = B.pos[u];
-          srow[j] = (B.ok[u] && j >= clo && j < chi) ? sc * a.scale : neg_inf();
+          const int j = pos_[u];
+          srow[j] = (ok_[u] && j >= clo && j < chi) ? sc * a.scale : neg_inf();
         }
       }
     }
@@ -217,7 +307,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) s[u][h] = B.ok[u] ? s[u][h] * a.scale_log2 : neg_inf();
+      for (int u = 0; u < U; ++u) s[u][h] = ok_[u] ? s[u][h] * a.scale_log2 : neg_inf();
       mx[h] = s[0][h];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx[h] = fmaxf(mx[h], s[u][h]);
@@ -268,14 +358,25 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   };
 
+  // Two-deep software pipeline; the prefetches are unconditional (see issue()).
   const int n_it = (t1 > t0) ? (t1 - t0 + TILE - 1) / TILE : 0;
   Buf A, Bb;
-  if (n_it > 0) issue(0, A);
-  for (int it = 0; it < n_it; it += 2) {
-    if (it + 1 < n_it) issue(it + 1, Bb);
-    compute(A);
-    if (it + 2 < n_it) issue(it + 2, A);
-    if (it + 1 < n_it) compute(Bb);
+  if (n_it > 0) {
+    // Scheduling barriers keep each refill below the last use of its buffer (so
+    // the buffers keep their registers across the back edge; a hoisted refill
+    // forces copies that wait on the loads) and all of a refill's loads ahead of
+    // the computation they overlap.
+    issue(0, A);
+    for (int it = 0; it < n_it; it += 2) {
+      issue(it + 1, Bb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, A);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(it + 2, A);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it + 1, Bb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if constexpr (SCORES) {
@@ -341,13 +442,15 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       if (e == 0 && a.lse) a.lse[(int64_t)b * a.lse_stride_b + hq] = ls > 0.f ? (M + log2f(ls)) * kLn2 : neg_inf();
     } else {
       const int64_t prow = ((int64_t)b * a.rows_b + hq) * a.n_split + split;
-      a.part_o[prow * D + e] = os;
+      store_coherent(a.part_o + prow * D + e, os);
       if (e == 0) {
-        a.part_ml[prow * 2] = M;
-        a.part_ml[prow * 2 + 1] = ls;
+        store_coherent(a.part_ml + prow * 2, M);
+        store_coherent(a.part_ml + prow * 2 + 1, ls);
       }
     }
   }
+  if (a.n_split > 1)
+    split_tail<D, G>(a, b, g, reinterpret_cast<int*>(wml + WAVES * G * 2), wml + WAVES * G * 2 + 4);
 }
 
 template <typename T, int D, int G, bool SPARSE, bool SCORES>

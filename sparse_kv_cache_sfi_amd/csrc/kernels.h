@@ -13,6 +13,14 @@ constexpr int kDecodeTile = 64;
 // stages in LDS.
 constexpr int kMaxSplitTokens = 4096;
 constexpr int kBtSlots = kMaxSplitTokens / 16 + 2;
+// Most splits per (request, KV head); the split tail keeps one weight per split
+// and head in LDS.
+constexpr int kMaxSplits = 256;
+// Split-K arrival counters live at the start of every workspace that holds
+// partials: one int per (request, KV head), at most kMaxCounters of them.  They
+// must be zero before the first call; every call returns them to zero.
+constexpr int kMaxCounters = 65536;
+constexpr size_t kCounterBytes = (size_t)kMaxCounters * 4;
 // Token tile of the MFMA verification kernel.
 constexpr int kVerifyTile = 32;
 // Largest batch of the mixed launch (its per-request plan travels in kernel arguments).
@@ -43,6 +51,7 @@ struct AttnArgs {
   int64_t lse_stride_b;
   float* part_o;          // split partials [rows, n_split, d]; row = b * rows_b + r
   float* part_ml;         // [rows, n_split, 2] = (max in log2 units, sum)
+  int32_t* counters;      // [B * Hkv] split arrival counters (zero between calls)
   int32_t rows_b;         // partial rows per request (t_q * Hq)
   float* scores;          // [B, Hkv, score_stride] (nullable)
   int64_t score_stride;

@@ -7,7 +7,7 @@
 #include <cmath>
 #include <string>
 
-#include "../../include/sfi.h"
+#include "sfi.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +34,9 @@ sfi_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(SFI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// Longest sequence (or compact + recent span) one split-K launch can cover.
+constexpr int64_t kMaxTokens = (int64_t)sfi::kMaxSplits * sfi::kMaxSplitTokens;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -71,6 +74,8 @@ sfi_status check_kv(const sfi_paged_kv* kv) {
   if (kv->max_pages < 1 || kv->num_pages < 1)
     return fail(SFI_ERR_INVALID_ARG, "max_pages and num_pages must be >= 1");
   if (kv->max_seq_len < 1) return fail(SFI_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (kv->max_seq_len > kMaxTokens)
+    return fail(SFI_ERR_UNSUPPORTED, "max_seq_len (%d) exceeds %lld tokens", kv->max_seq_len, (long long)kMaxTokens);
   if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages * 16)
     return fail(SFI_ERR_INVALID_ARG, "max_seq_len (%d) exceeds max_pages * page_size (%lld)", kv->max_seq_len,
                 (long long)kv->max_pages * 16);
@@ -89,7 +94,8 @@ sfi_status check_budgets(int32_t n_sink, int32_t n_recent) {
 }
 
 // Split-K plan: enough work-groups to fill the chip, but at least kMinSplit tokens
-// per split, at most kMaxSplitTokens, rounded to the decode tile.
+// per split, at most kMaxSplitTokens, at most kMaxSplits splits, rounded to the
+// decode tile.
 struct Split {
   int tokens;
   int n;
@@ -102,6 +108,7 @@ Split plan_split(int64_t units, int64_t n_tok, int tile) {
   const int64_t by_min = (n_tok + kMinSplit - 1) / kMinSplit;
   const int64_t want = (kTargetWGs + units - 1) / units;
   int64_t ns = by_min < want ? by_min : want;
+  if (ns > sfi::kMaxSplits) ns = sfi::kMaxSplits;
   if (ns < 1) ns = 1;
   int64_t st = (n_tok + ns - 1) / ns;
   st = (st + tile - 1) / tile * tile;
@@ -112,10 +119,13 @@ Split plan_split(int64_t units, int64_t n_tok, int tile) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace of split partials: [rows, n_split, d] floats then [rows, n_split, 2].
+// Workspace of a split-K call: the arrival counters (fixed region at offset 0, so
+// calls of any shape can share one zero-filled workspace), then the partials
+// [rows, n_split, d] floats and [rows, n_split, 2] floats.
 size_t partial_bytes(int64_t rows, int n_split, int d) {
   if (n_split <= 1) return 0;
-  return align_up((size_t)rows * n_split * d * 4, 256) + align_up((size_t)rows * n_split * 2 * 4, 256);
+  return sfi::kCounterBytes + align_up((size_t)rows * n_split * d * 4, 256) +
+         align_up((size_t)rows * n_split * 2 * 4, 256);
 }
 
 Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
@@ -147,8 +157,9 @@ sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_
 void set_partials(sfi::AttnArgs& a, void* ws, int64_t rows, int d) {
   if (a.n_split <= 1) return;
   char* p = static_cast<char*>(ws);
-  a.part_o = reinterpret_cast<float*>(p);
-  a.part_ml = reinterpret_cast<float*>(p + align_up((size_t)rows * a.n_split * d * 4, 256));
+  a.counters = reinterpret_cast<int32_t*>(p);
+  a.part_o = reinterpret_cast<float*>(p + sfi::kCounterBytes);
+  a.part_ml = reinterpret_cast<float*>(p + sfi::kCounterBytes + align_up((size_t)rows * a.n_split * d * 4, 256));
 }
 
 sfi_status check_workspace(const void* ws, size_t have, size_t need) {
@@ -193,6 +204,8 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
     if (t_q * G > 64) return fail(SFI_ERR_UNSUPPORTED, "t_q * G must be <= 64 (got %d)", t_q * G);
     return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 is not available in this build");
   }
+  if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
+    return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
   const Split sp = plan_dense(shape, kv, t_q);
   const int64_t rows = (int64_t)shape->batch * t_q * shape->num_q_heads;
   SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
@@ -219,12 +232,7 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
     e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, false, shape->batch, st);
   else
     e = sfi::launch_verify(a, shape->head_dim, G, shape->batch, st);
-  if (e != hipSuccess) return hip_status(e, "attention launch");
-  if (sp.n > 1) {
-    e = sfi::launch_combine(a.part_o, a.part_ml, (int)rows, sp.n, shape->head_dim, out, lse, st);
-    if (e != hipSuccess) return hip_status(e, "combine launch");
-  }
-  return ok();
+  return hip_status(e, "attention launch");
 }
 
 sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t k,
@@ -296,6 +304,10 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
   if (!seq_lens || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens and n_compact must be non-NULL");
   SFI_TRY(check_budgets(n_sink, n_recent));
   if (cap < 1) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1");
+  if ((int64_t)cap + n_recent > kMaxTokens)
+    return fail(SFI_ERR_UNSUPPORTED, "cap + n_recent exceeds %lld tokens", (long long)kMaxTokens);
+  if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
+    return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
   const Split sp = plan_sparse(shape, cap, n_recent, kv);
   const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
   SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
@@ -321,12 +333,7 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipError_t e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, true, shape->batch, st);
-  if (e != hipSuccess) return hip_status(e, "sparse decode launch");
-  if (sp.n > 1) {
-    e = sfi::launch_combine(a.part_o, a.part_ml, (int)rows, sp.n, shape->head_dim, out, lse, st);
-    if (e != hipSuccess) return hip_status(e, "combine launch");
-  }
-  return ok();
+  return hip_status(e, "sparse decode launch");
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

@@ -72,6 +72,7 @@ def _dense(lib, shape, kv, q=FAKE, t_q=1, lens=FAKE, n_sink=4, n_recent=64, out=
     (lambda a: a.update(shape=_shape(B=0)), 1, "batch"),
     (lambda a: a.update(kv=_kv(page=32)), 2, "page_size"),
     (lambda a: a.update(kv=_kv(max_len=20000)), 1, "max_seq_len"),
+    (lambda a: a.update(kv=_kv(max_pages=70000, max_len=(1 << 20) + 16)), 2, "exceeds"),
     (lambda a: a.update(kv=_kv(k=MISALIGNED)), 1, "aligned"),
     (lambda a: a.update(kv=_kv(bt=0)), 1, "non-NULL"),
     (lambda a: a.update(q=0), 1, "q is NULL"),
@@ -154,12 +155,14 @@ def test_workspace_queries_match_the_plan(lib):
 
 
 @pytest.mark.parametrize("B,Hkv,n_tok", [(1, 8, 16384), (1, 8, 256), (16, 8, 32768), (4, 8, 65536),
-                                         (8, 8, 131072), (1, 1, 1), (3, 2, 3000), (64, 8, 100)])
+                                         (8, 8, 131072), (1, 1, 1), (3, 2, 3000), (64, 8, 100),
+                                         (1, 1, 1 << 20), (1, 1, 300000)])
 def test_split_plan_covers_every_token(B, Hkv, n_tok):
     st, ns = sfi.plan_splits(0, B=B, Hq=4 * Hkv, Hkv=Hkv, d=128, bf16=True, max_pages=(n_tok + 15) // 16,
                              num_pages=1, max_seq_len=n_tok)
     assert st % 64 == 0 and 64 <= st <= 4096
     assert ns * st >= n_tok and (ns - 1) * st < n_tok
+    assert 1 <= ns <= 256
     assert ns == 1 or st >= 256 or B * Hkv * ns >= 2048
 
 

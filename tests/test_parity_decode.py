@@ -207,7 +207,7 @@ def test_fast_step_single_key_returns_its_value_exactly(gpu_lib):
         c = make_case(132, name="s", B=1, Hq=4, Hkv=2, d=128, dtype=dtype, seq_lens=[64], n_sink=1, n_recent=0,
                       k_sel=1)
         dc = DevCase(c)
-        sel = np.full((2, 1), -1, np.int32)      # no selected token: compact = the single sink row
+        sel = np.full((1, 2, 1), -1, np.int32)   # no selected token: compact = the single sink row
         ck, cv, nc = gpu_lib.pack_compact(dc.k, dc.v, dc.bt, dc.lens, dev_array(sel), n_sink=1, cap=4,
                                           max_seq_len=dc.max_seq_len)
         out, lse = gpu_lib.sparse_decode_attn(dev_array(c.q[:, 0]), dc.k, dc.v, dc.bt, dc.lens, ck, cv, nc,
