@@ -6,10 +6,15 @@ decode layer in bf16 - batch 1, 16 query heads on 8 KV heads, head_dim 128,
 KV length 16384, page size 16, sink 4, recent 64.  One step is one pass of the
 whole t_q = 1 path on one batch:
 
-    slow step   dense attention + masked group logits        (main stream)
-    Selector    top-k per KV head, k = 1980 (12.5 % retention) (aux stream)
-    pack        gather-pack sink + selected into the compact buffer (aux stream)
-    fast step   sparse attention over compact + recent       (main stream, after pack)
+    slow step   dense attention + masked group logits
+    Selector    top-k per KV head, k = 1980 (12.5 % retention)
+    pack        gather-pack sink + selected into the compact buffer
+    fast step   sparse attention over compact + recent
+
+Within one layer these four calls depend on each other in order, so the step
+runs them on one stream (an auxiliary stream only pays off when the Selector and
+pack of layer i overlap the attention of layer i+1; pass --aux-stream to run
+them on a second stream anyway).
 
 `value` = algorithmic KV bytes of the step (dense K/V read, pack read + write,
 fast-step K/V read) / step time.  Inputs are resident in HBM before timing;
@@ -81,6 +86,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--aux-stream", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -104,7 +110,7 @@ def main():
     cap = n_sink + k_sel
     max_len = L
     main_s = torch.cuda.current_stream(dev)
-    aux_s = torch.cuda.Stream(device=dev)
+    aux_s = torch.cuda.Stream(device=dev) if args.aux_stream else main_s
 
     # per-replica outputs and buffers, all allocated before timing
     for ly in layers:
@@ -137,17 +143,19 @@ def main():
         if record:
             e1.record(main_s)
             dense_ev.append((e0, e1))
-        ready = torch.cuda.Event()
-        ready.record(main_s)
-        aux_s.wait_event(ready)
+        if aux_s is not main_s:
+            ready = torch.cuda.Event()
+            ready.record(main_s)
+            aux_s.wait_event(ready)
         sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"],
                         stream=aux_s)
         sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
                          max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
                          stream=aux_s)
-        packed = torch.cuda.Event()
-        packed.record(aux_s)
-        main_s.wait_event(packed)
+        if aux_s is not main_s:
+            packed = torch.cuda.Event()
+            packed.record(aux_s)
+            main_s.wait_event(packed)
         sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"], ly["cv"], ly["nc"],
                                n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=ly["fout"],
                                lse=ly["flse"], workspace=ws_sparse, stream=main_s)
@@ -188,7 +196,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: B=1, Hq=16, Hkv=8, d=128, page 16, "
                                "sink 4, recent 64, selected 1980 (12.5% retention); step = slow step "
-                               "(dense + logits) + Selector + pack (aux stream) + fast step",
+                               "(dense + logits) + Selector + pack + fast step"
+                               + (" (Selector and pack on a second stream)" if args.aux_stream else ""),
                    "global_batch": B, "seq_len": L, "replicas": R, "step_kv_bytes": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roof,

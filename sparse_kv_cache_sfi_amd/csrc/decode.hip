@@ -85,27 +85,41 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wave-wide reductions (all 64 lanes receive the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 // Split-K tail: the last work-group of (b, g) to finish merges all splits of the
-// group's G query heads in fixed split order (M = max m_s; out = sum 2^(m_s - M) o_s
-// / sum 2^(m_s - M) l_s; lse = (M + log2 of that sum) * ln 2; an empty split adds 0)
-// and returns the arrival counter to zero.  All (m, l) pairs are fetched at once
-// into LDS; each output element then streams its ns partials in batches of 8.
+// group's G query heads (M = max m_s; out = sum 2^(m_s - M) o_s / sum 2^(m_s - M)
+// l_s; lse = (M + log2 of that sum) * ln 2; an empty split adds 0) and returns the
+// arrival counter to zero.  Every step is parallel: all (m, l) pairs are fetched at
+// once, per-head max and sum are wave reductions, and each output element keeps
+// up to 32 partial loads in flight.  Summation orders are fixed, so results do not
+// depend on which work-group finishes last.
 template <int D, int G>
 __device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const int g, int* flag, float* tail) {
-  constexpr int NT = 256;
-  const int tid = threadIdx.x;
+  constexpr int NT = 256, WAVES = NT / kWave, BATCH = 32;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
   __syncthreads();
   if (tid == 0) {
     const int ticket = __hip_atomic_fetch_add(&a.counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_SYSTEM);
+                                              __HIP_MEMORY_SCOPE_AGENT);
     *flag = (ticket == a.n_split - 1) ? 1 : 0;
   }
   __syncthreads();
   if (*flag == 0) return;
   const int ns = a.n_split;
-  float* w_s = tail;                   // [G][ns]: m, then the weight 2^(m - M)
-  float* l_s = tail + G * kMaxSplits;  // [G][ns]
+  float* w_s = tail;                   // [G][kMaxSplits]: m, then the weight 2^(m - M)
+  float* l_s = tail + G * kMaxSplits;  // [G][kMaxSplits]
   float* M_h = tail + 2 * G * kMaxSplits;
   float* L_h = M_h + G;
   const int64_t row0 = (int64_t)b * a.rows_b + g * G;
@@ -116,18 +130,22 @@ __device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const
     l_s[h * kMaxSplits + s] = load_coherent(ml + 1);
   }
   __syncthreads();
-  if (tid < G) {
+  for (int h = w; h < G; h += WAVES) {
     float M = neg_inf();
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, w_s[tid * kMaxSplits + s]);
+    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, w_s[h * kMaxSplits + s]);
+    M = wave_max(M);
     float L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float m = w_s[tid * kMaxSplits + s];
+    for (int s = lane; s < ns; s += kWave) {
+      const float m = w_s[h * kMaxSplits + s];
       const float wt = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
-      w_s[tid * kMaxSplits + s] = wt;
-      L = fmaf(wt, l_s[tid * kMaxSplits + s], L);
+      w_s[h * kMaxSplits + s] = wt;
+      L = fmaf(wt, l_s[h * kMaxSplits + s], L);
     }
-    M_h[tid] = M;
-    L_h[tid] = L;
+    L = wave_sum(L);
+    if (lane == 0) {
+      M_h[h] = M;
+      L_h[h] = L;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += NT) {
@@ -135,12 +153,12 @@ __device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const
     const float* po = a.part_o + (row0 + h) * ns * D + e;
     const float* wh = w_s + h * kMaxSplits;
     float os = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float v[8];
+    for (int s0 = 0; s0 < ns; s0 += BATCH) {
+      float v[BATCH];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (s0 + j < ns) ? load_coherent(po + (int64_t)(s0 + j) * D) : 0.f;
+      for (int j = 0; j < BATCH; ++j) v[j] = (s0 + j < ns) ? load_coherent(po + (int64_t)(s0 + j) * D) : 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < BATCH; ++j)
         if (s0 + j < ns) os = fmaf(wh[s0 + j], v[j], os);
     }
     const float ls = L_h[h];
@@ -149,7 +167,7 @@ __device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const
     if (e == 0 && a.lse)
       a.lse[(int64_t)b * a.lse_stride_b + hq] = ls > 0.f ? (M_h[h] + log2f(ls)) * kLn2 : neg_inf();
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D, int G, bool SPARSE, bool SCORES>

@@ -103,7 +103,7 @@ struct Split {
 
 Split plan_split(int64_t units, int64_t n_tok, int tile) {
   constexpr int64_t kMinSplit = 256;
-  constexpr int64_t kTargetWGs = 2048;
+  constexpr int64_t kTargetWGs = 1024;
   if (n_tok <= 0) return {tile, 1};
   const int64_t by_min = (n_tok + kMinSplit - 1) / kMinSplit;
   const int64_t want = (kTargetWGs + units - 1) / units;
