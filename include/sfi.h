@@ -45,8 +45,9 @@
  *    such entries are skipped (attention) or written as zero rows (pack).
  *    seq_lens[b] is clamped to [0, min(max_seq_len, max_pages * P)].
  *  - Supported: d in {64, 128}; G in {1, 2, 4, 8}; P = 16; dtype F32 or BF16
- *    for t_q = 1; BF16 with t_q * G <= 64 for t_q in [2, 16].  Pointers to
- *    q, k, v, compact buffers, out and workspace must be 16-byte aligned.
+ *    for t_q = 1; BF16 with t_q * G <= 32 for t_q in [2, 16].  max_seq_len up
+ *    to 2^20 tokens (2^18 for t_q > 1).  Pointers to q, k, v, compact buffers,
+ *    out and workspace must be 16-byte aligned.
  */
 #ifndef SFI_H_
 #define SFI_H_

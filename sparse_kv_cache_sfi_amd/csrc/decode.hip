@@ -21,6 +21,7 @@
 // goes to the workspace, or straight to out/lse when there is one split.
 #include "common.h"
 #include "kernels.h"
+#include "split_tail.h"
 
 namespace sfi {
 
@@ -48,7 +49,7 @@ struct DecodeShape {
   static constexpr int U = (LPR == 16 && C == 1) ? 4 : 2;      // slots per iteration
   static constexpr int WAVES = 4;
   static constexpr int TILE = WAVES * U * ROWS;                // tokens per work-group iteration
-  static constexpr int TAIL = 2 * kMaxSplits * G * 4 + 2 * G * 4;   // split tail: (w, l) per split, M and L per head
+  static constexpr int TAIL = SplitTail<D>::bytes(G, kMaxSplits);
   static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4 + 16 + TAIL;
   static_assert(C >= 1, "row too short for the lane mapping");
 };
@@ -72,102 +73,6 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
   acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
   acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
   return acc;
-}
-
-// Split partials cross XCDs, whose L2 caches are not coherent with each other.
-// They are written and read with agent-scope atomic accesses (coherent at the
-// device level, no cache-wide write-back or invalidate), and the writer drains
-// its stores before it takes a ticket.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave-wide reductions (all 64 lanes receive the result).
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
-// Split-K tail: the last work-group of (b, g) to finish merges all splits of the
-// group's G query heads (M = max m_s; out = sum 2^(m_s - M) o_s / sum 2^(m_s - M)
-// l_s; lse = (M + log2 of that sum) * ln 2; an empty split adds 0) and returns the
-// arrival counter to zero.  Every step is parallel: all (m, l) pairs are fetched at
-// once, per-head max and sum are wave reductions, and each output element keeps
-// up to 32 partial loads in flight.  Summation orders are fixed, so results do not
-// depend on which work-group finishes last.
-template <int D, int G>
-__device__ __forceinline__ void split_tail(const AttnArgs& a, const int b, const int g, int* flag, float* tail) {
-  constexpr int NT = 256, WAVES = NT / kWave, BATCH = 32;
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const int ticket = __hip_atomic_fetch_add(&a.counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (ticket == a.n_split - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (*flag == 0) return;
-  const int ns = a.n_split;
-  float* w_s = tail;                   // [G][kMaxSplits]: m, then the weight 2^(m - M)
-  float* l_s = tail + G * kMaxSplits;  // [G][kMaxSplits]
-  float* M_h = tail + 2 * G * kMaxSplits;
-  float* L_h = M_h + G;
-  const int64_t row0 = (int64_t)b * a.rows_b + g * G;
-  for (int i = tid; i < G * ns; i += NT) {
-    const int h = i / ns, s = i % ns;
-    const float* ml = a.part_ml + ((row0 + h) * ns + s) * 2;
-    w_s[h * kMaxSplits + s] = load_coherent(ml);
-    l_s[h * kMaxSplits + s] = load_coherent(ml + 1);
-  }
-  __syncthreads();
-  for (int h = w; h < G; h += WAVES) {
-    float M = neg_inf();
-    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, w_s[h * kMaxSplits + s]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int s = lane; s < ns; s += kWave) {
-      const float m = w_s[h * kMaxSplits + s];
-      const float wt = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
-      w_s[h * kMaxSplits + s] = wt;
-      L = fmaf(wt, l_s[h * kMaxSplits + s], L);
-    }
-    L = wave_sum(L);
-    if (lane == 0) {
-      M_h[h] = M;
-      L_h[h] = L;
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += NT) {
-    const int h = idx / D, e = idx % D;
-    const float* po = a.part_o + (row0 + h) * ns * D + e;
-    const float* wh = w_s + h * kMaxSplits;
-    float os = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += BATCH) {
-      float v[BATCH];
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) v[j] = (s0 + j < ns) ? load_coherent(po + (int64_t)(s0 + j) * D) : 0.f;
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j)
-        if (s0 + j < ns) os = fmaf(wh[s0 + j], v[j], os);
-    }
-    const float ls = L_h[h];
-    const int hq = g * G + h;
-    a.out[(int64_t)b * a.out_stride_b + (int64_t)hq * D + e] = ls > 0.f ? os / ls : 0.f;
-    if (e == 0 && a.lse)
-      a.lse[(int64_t)b * a.lse_stride_b + hq] = ls > 0.f ? (M_h[h] + log2f(ls)) * kLn2 : neg_inf();
-  }
-  if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D, int G, bool SPARSE, bool SCORES>
@@ -459,7 +364,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       a.out[(int64_t)b * a.out_stride_b + (int64_t)hq * D + e] = ls > 0.f ? os / ls : 0.f;
       if (e == 0 && a.lse) a.lse[(int64_t)b * a.lse_stride_b + hq] = ls > 0.f ? (M + log2f(ls)) * kLn2 : neg_inf();
     } else {
-      const int64_t prow = ((int64_t)b * a.rows_b + hq) * a.n_split + split;
+      const int64_t prow = (int64_t)SplitTail<D>::row(a, b, g, G, h) * a.n_split + split;
       store_coherent(a.part_o + prow * D + e, os);
       if (e == 0) {
         store_coherent(a.part_ml + prow * 2, M);
@@ -468,7 +373,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   }
   if (a.n_split > 1)
-    split_tail<D, G>(a, b, g, reinterpret_cast<int*>(wml + WAVES * G * 2), wml + WAVES * G * 2 + 4);
+    SplitTail<D>::run(a, b, g, G, G, kMaxSplits, reinterpret_cast<int*>(wml + WAVES * G * 2),
+                      wml + WAVES * G * 2 + 4);
 }
 
 template <typename T, int D, int G, bool SPARSE, bool SCORES>

@@ -16,6 +16,10 @@ constexpr int kBtSlots = kMaxSplitTokens / 16 + 2;
 // Most splits per (request, KV head); the split tail keeps one weight per split
 // and head in LDS.
 constexpr int kMaxSplits = 256;
+// Most splits of a verification unit (its tail keeps t_q * G rows of weights).
+constexpr int kMaxVerifySplits = 64;
+// Most query rows (t_q * G) of one KV head in a verification call.
+constexpr int kMaxVerifyRows = 32;
 // Split-K arrival counters live at the start of every workspace that holds
 // partials: one int per (request, KV head), at most kMaxCounters of them.  They
 // must be zero before the first call; every call returns them to zero.

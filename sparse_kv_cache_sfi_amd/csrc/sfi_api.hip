@@ -101,14 +101,14 @@ struct Split {
   int n;
 };
 
-Split plan_split(int64_t units, int64_t n_tok, int tile) {
+Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits) {
   constexpr int64_t kMinSplit = 256;
   constexpr int64_t kTargetWGs = 1024;
   if (n_tok <= 0) return {tile, 1};
   const int64_t by_min = (n_tok + kMinSplit - 1) / kMinSplit;
   const int64_t want = (kTargetWGs + units - 1) / units;
   int64_t ns = by_min < want ? by_min : want;
-  if (ns > sfi::kMaxSplits) ns = sfi::kMaxSplits;
+  if (ns > max_splits) ns = max_splits;
   if (ns < 1) ns = 1;
   int64_t st = (n_tok + ns - 1) / ns;
   st = (st + tile - 1) / tile * tile;
@@ -129,8 +129,9 @@ size_t partial_bytes(int64_t rows, int n_split, int d) {
 }
 
 Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
-  const int tile = t_q > 1 ? sfi::kVerifyTile : sfi::kDecodeTile;
-  return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, tile);
+  if (t_q > 1)
+    return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
+  return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kDecodeTile);
 }
 
 Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
@@ -201,8 +202,11 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (t_q > 1) {
     if (shape->dtype != SFI_BF16) return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 needs bf16 inputs");
-    if (t_q * G > 64) return fail(SFI_ERR_UNSUPPORTED, "t_q * G must be <= 64 (got %d)", t_q * G);
-    return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 is not available in this build");
+    if (t_q * G > sfi::kMaxVerifyRows)
+      return fail(SFI_ERR_UNSUPPORTED, "t_q * G must be <= %d (got %d)", sfi::kMaxVerifyRows, t_q * G);
+    if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens)
+      return fail(SFI_ERR_UNSUPPORTED, "max_seq_len (%d) exceeds %lld tokens for t_q > 1", kv->max_seq_len,
+                  (long long)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens);
   }
   if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
     return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);

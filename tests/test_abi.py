@@ -86,7 +86,8 @@ def _dense(lib, shape, kv, q=FAKE, t_q=1, lens=FAKE, n_sink=4, n_recent=64, out=
     (lambda a: a.update(ws_bytes=10), 3, "workspace"),
     (lambda a: a.update(ws=0), 1, "workspace is NULL"),
     (lambda a: a.update(shape=_shape(dtype=0), t_q=4), 2, "bf16"),
-    (lambda a: a.update(shape=_shape(Hq=64, Hkv=8), t_q=16), 2, "<= 64"),
+    (lambda a: a.update(shape=_shape(Hq=64, Hkv=8), t_q=16), 2, "<= 32"),
+    (lambda a: a.update(shape=_shape(Hq=32, Hkv=8), t_q=9), 2, "<= 32"),
 ])
 def test_dense_rejects_bad_arguments(lib, mutate, status, msg):
     args = dict(shape=_shape(), kv=_kv())
