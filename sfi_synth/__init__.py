@@ -57,6 +57,17 @@ def _values(x: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_values(x) if dtype == "bf16" else np.asarray(x, dtype=np.float32)
 
 
+def _draw_pool(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, 1) values in storage form, drawn in order in chunks (the same stream as one
+    draw of the whole array) so that large pools never exist as float32."""
+    out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    flat = out.reshape(-1)
+    for i in range(0, flat.size, chunk):
+        n = min(chunk, flat.size - i)
+        flat[i:i + n] = _store(rng.standard_normal(n, dtype=np.float32), dtype)
+    return out
+
+
 # --------------------------------------------------------------------------- containers
 
 @dataclass
@@ -167,8 +178,8 @@ def make_case(seed: int, *, name: str, B: int, Hq: int, Hkv: int, d: int, dtype:
     bt, num_pages = _block_table(rng, cap, PAGE_SIZE, spare_pages)
     G = Hq // Hkv
     q = rng.standard_normal((B, t_q, Hq, d), dtype=np.float32)
-    k = rng.standard_normal((num_pages, Hkv, PAGE_SIZE, d), dtype=np.float32)
-    v = rng.standard_normal((num_pages, Hkv, PAGE_SIZE, d), dtype=np.float32)
+    k = _draw_pool(rng, (num_pages, Hkv, PAGE_SIZE, d), dtype)
+    v = _draw_pool(rng, (num_pages, Hkv, PAGE_SIZE, d), dtype)
     q_st = _store(q, dtype)
     qv = _values(q_st, dtype)
     planted: Dict[Tuple[int, int], np.ndarray] = {}
@@ -182,15 +193,13 @@ def make_case(seed: int, *, name: str, B: int, Hq: int, Hkv: int, d: int, dtype:
                 pos = np.sort(rng.choice(hi - lo, size=n, replace=False) + lo).astype(np.int64)
                 planted[(b, g)] = pos
                 qbar = qv[b, 0, g * G:(g + 1) * G, :].astype(np.float64).mean(axis=0)
-                key = (4.0 * qbar).astype(np.float32)
-                for p in pos:
-                    page = bt[b, p // PAGE_SIZE]
-                    k[page, g, p % PAGE_SIZE, :] = key
+                key = _store((4.0 * qbar).astype(np.float32), dtype)
+                k[bt[b, pos // PAGE_SIZE], g, pos % PAGE_SIZE, :] = key
     extra = None
     if extra_steps > 0:
         noise = rng.standard_normal((extra_steps, B, Hq, d), dtype=np.float32)
         extra = _store(qv[None, :, 0, :, :] + np.float32(extra_noise) * noise, dtype)
-    kv = PagedKV(dtype=dtype, k=_store(k, dtype), v=_store(v, dtype), block_table=bt)
+    kv = PagedKV(dtype=dtype, k=k, v=v, block_table=bt)
     return Case(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, d=d, t_q=t_q, q=q_st, kv=kv,
                 seq_lens=seq_lens, n_sink=n_sink, n_recent=n_recent, k_sel=k_sel,
                 scale=float(scale if scale is not None else 1.0 / np.sqrt(d)),

@@ -1,0 +1,382 @@
+// Split-K flash-decoding device code for one query token per request, on CDNA4 vector ALUs.
+//
+// Serves two calls:
+//  * the fast step (SFI page, Fig. 2: attention over sink + selected + recent;
+//    Fig. 3B: sink and selected stream from a contiguous compact buffer, recent
+//    tokens are read in place from paged KV), and
+//  * the slow step (Fig. 2: dense attention over the whole paged KV, which also
+//    writes the masked logits the Selector consumes).
+//
+// Work decomposition: one work-group (4 waves) per (split, KV head g, request b).
+// All G query heads of the group share every K/V row the work-group loads.
+// A K or V row is read by LPR = 8 or 16 lanes with 16-byte loads, so each load
+// instruction covers 64/LPR consecutive rows with full 128-byte lines; a lane
+// owns the same d/LPR dimensions of every row it touches.  Each wave streams
+// its own rows (no barrier in the loop) with a two-deep register pipeline:
+// the loads of iteration i+1 are in flight while iteration i is computed.
+// Per row: G dot products (v_dot2_f32_bf16 for bf16) reduced across the
+// row's lanes with DPP, an online softmax in log2 units whose reference maximum is
+// only raised when a score exceeds it by more than 8 (2^8 headroom in fp32),
+// and fp32 FMA accumulation of P*V.  The split's partial (max, sum, o) per head
+// goes to the workspace, or straight to out/lse when there is one split.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+#include "split_tail.h"
+
+namespace sfi {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kPerChunk = 8;
+};
+
+template <typename T, int D, int G>
+struct DecodeShape {
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
+  // Lanes per K/V row: 16 when the group is wide (fewer dimensions per lane keep the
+  // G accumulators in registers), else 8; never more lanes than 16-byte chunks.
+  static constexpr int LPR = (G >= 4 && ROW_BYTES >= 256) ? 16 : 8;
+  static constexpr int EPC = Elem<T>::kPerChunk;               // elements per 16-byte chunk
+  static constexpr int C = ROW_BYTES / (16 * LPR);             // chunks per lane per row
+  static constexpr int E = C * EPC;                            // elements owned per lane
+  static constexpr int ROWS = kWave / LPR;                     // rows per wave per slot
+  static constexpr int U = (LPR == 16 && C == 1) ? 4 : 2;      // slots per iteration
+  static constexpr int WAVES = 4;
+  static constexpr int TILE = WAVES * U * ROWS;                // tokens per work-group iteration
+  static constexpr int TAIL = SplitTail<D>::bytes(G, kMaxSplits);
+  static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4 + 16 + TAIL;
+  static_assert(C >= 1, "row too short for the lane mapping");
+};
+
+template <typename T>
+__device__ __forceinline__ float dot_chunk(const u32x4& q, const u32x4& k, float acc);
+
+template <>
+__device__ __forceinline__ float dot_chunk<uint16_t>(const u32x4& q, const u32x4& k, float acc) {
+  acc = dot2_bf16(q.x, k.x, acc);
+  acc = dot2_bf16(q.y, k.y, acc);
+  acc = dot2_bf16(q.z, k.z, acc);
+  acc = dot2_bf16(q.w, k.w, acc);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k, float acc) {
+  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  return acc;
+}
+
+template <typename T, int D, int G, bool SPARSE, bool SCORES>
+__device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, const int g, const int split,
+                                            const int q_row0, char* smem) {
+  using S = DecodeShape<T, D, G>;
+  constexpr int LPR = S::LPR, EPC = S::EPC, C = S::C, E = S::E, ROWS = S::ROWS, U = S::U;
+  constexpr int WAVES = S::WAVES, TILE = S::TILE, NT = WAVES * kWave;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave, lane = tid % kWave;
+  const int r = lane / LPR, sub = lane % LPR;
+
+  int* bt_s = reinterpret_cast<int*>(smem);
+  float* wo = reinterpret_cast<float*>(smem + kBtSlots * 4);
+  float* wml = wo + WAVES * G * D;
+
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
+  int n_c = 0, rs = 0;
+  if constexpr (SPARSE) {
+    n_c = clampi(a.n_compact[b], 0, a.cap);
+    rs = min(max(a.n_sink, L - a.n_recent), L);
+  }
+  const int n_tot = n_c + (L - rs);
+  const int t0 = split * a.split_tokens;
+  const int t1 = min(n_tot, t0 + a.split_tokens);
+
+  // Stage the block-table entries of this split's paged positions in LDS.
+  const int v_first = max(t0, n_c);
+  int pg_lo = 0, n_pg = 0;
+  if (t1 > v_first) {
+    pg_lo = (rs + v_first - n_c) >> 4;
+    n_pg = ((rs + t1 - 1 - n_c) >> 4) - pg_lo + 1;
+  }
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  for (int i = tid; i < n_pg; i += NT) {
+    const int e = bt_row[pg_lo + i];
+    bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
+  }
+  __syncthreads();
+
+  // This lane's slice of the G query vectors.
+  const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)q_row0 * a.Hq + g * G) * D;
+  u32x4 q[G][C];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      q[h][c] = *reinterpret_cast<const u32x4*>(qb + h * D + (c * LPR + sub) * EPC);
+
+  const T* kpool = reinterpret_cast<const T*>(a.k_pool);
+  const T* vpool = reinterpret_cast<const T*>(a.v_pool);
+  const T* ckb = kpool;
+  const T* cvb = vpool;
+  if constexpr (SPARSE) {
+    const int64_t base = ((int64_t)b * a.Hkv + g) * a.cap * D;
+    ckb = reinterpret_cast<const T*>(a.ck) + base;
+    cvb = reinterpret_cast<const T*>(a.cv) + base;
+  }
+  const int64_t page_elems = (int64_t)a.Hkv * kPage * D;
+  const int64_t head_off = (int64_t)g * kPage * D;
+
+  int clo = 0, chi = 0;
+  float* srow = nullptr;
+  if constexpr (SCORES) {
+    candidate_bounds(L, a.t_q, a.n_sink, a.n_recent, &clo, &chi);
+    srow = a.scores + ((int64_t)b * a.Hkv + g) * a.score_stride;
+  }
+
+  float m[G], l[G], o[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = neg_inf();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+  }
+
+  struct Buf {
+    u32x4 k[U][C];
+    u32x4 v[U][C];
+  };
+
+  // Where slot u of iteration `it` comes from: its position p, whether it lies in
+  // this split (in) and whether it is backed by a compact row or a valid page (ok).
+  auto locate = [&](int it, int u, int& vi, int& p, bool& in, bool& compact, int& pg, bool& ok) {
+    vi = t0 + it * TILE + (w * U + u) * ROWS + r;
+    in = vi < t1;
+    compact = SPARSE && vi < n_c;
+    p = compact ? vi : rs + vi - n_c;
+    const int slot = in && !compact ? (p >> 4) - pg_lo : 0;
+    pg = bt_s[slot];
+    ok = in && (compact || pg >= 0);
+  };
+
+  // Issue the loads of one iteration.  Every lane always loads (rows outside the
+  // split or behind an invalid page read row 0 of the pool and are masked), so the
+  // loop carries no conditionally-loaded registers.
+  auto issue = [&](int it, Buf& B) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int vi, p, pg;
+      bool in, compact, ok;
+      locate(it, u, vi, p, in, compact, pg, ok);
+      int64_t off = (int64_t)(pg < 0 ? 0 : pg) * page_elems + head_off + (int64_t)(p & 15) * D;
+      off = ok ? off : 0;
+      const T* kr = kpool + off;
+      const T* vr = vpool + off;
+      if constexpr (SPARSE) {
+        if (compact) {
+          kr = ckb + (int64_t)vi * D;
+          vr = cvb + (int64_t)vi * D;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        B.k[u][c] = *reinterpret_cast<const u32x4*>(kr + (c * LPR + sub) * EPC);
+        B.v[u][c] = *reinterpret_cast<const u32x4*>(vr + (c * LPR + sub) * EPC);
+      }
+    }
+  };
+
+  auto compute = [&](int it, const Buf& B) {
+    bool in_[U], ok_[U];
+    int pos_[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int vi, pg;
+      bool compact;
+      locate(it, u, vi, pos_[u], in_[u], compact, pg, ok_[u]);
+    }
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc = dot_chunk<T>(q[h][c], B.k[u][c], acc);
+        s[u][h] = group_sum<LPR>(acc);
+      }
+    if constexpr (SCORES) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (sub == 0 && in_[u]) {
+          float sc = 0.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc += s[u][h];
+          const int j = pos_[u];
+          srow[j] = (ok_[u] && j >= clo && j < chi) ? sc * a.scale : neg_inf();
+        }
+      }
+    }
+    bool need = false;
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) s[u][h] = ok_[u] ? s[u][h] * a.scale_log2 : neg_inf();
+      mx[h] = s[0][h];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx[h] = fmaxf(mx[h], s[u][h]);
+      need |= mx[h] > m[h] + 8.f;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], mx[h]);
+        const float al = (m[h] == neg_inf()) ? 0.f : exp2_fast(m[h] - mn);
+        l[h] *= al;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[h][e] *= al;
+        m[h] = mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float p[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        p[h] = (m[h] == neg_inf()) ? 0.f : exp2_fast(s[u][h] - m[h]);
+        l[h] += p[h];
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t wv[4] = {B.v[u][c].x, B.v[u][c].y, B.v[u][c].z, B.v[u][c].w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(wv[i]);
+            const float hi = bf16_hi(wv[i]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              o[h][c * EPC + 2 * i] = fmaf(p[h], lo, o[h][c * EPC + 2 * i]);
+              o[h][c * EPC + 2 * i + 1] = fmaf(p[h], hi, o[h][c * EPC + 2 * i + 1]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = __uint_as_float(wv[i]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) o[h][c * EPC + i] = fmaf(p[h], x, o[h][c * EPC + i]);
+          }
+        }
+      }
+    }
+  };
+
+  // Two-deep software pipeline; the prefetches are unconditional (see issue()).
+  const int n_it = (t1 > t0) ? (t1 - t0 + TILE - 1) / TILE : 0;
+  Buf A, Bb;
+  if (n_it > 0) {
+    // Scheduling barriers keep each refill below the last use of its buffer (so
+    // the buffers keep their registers across the back edge; a hoisted refill
+    // forces copies that wait on the loads) and all of a refill's loads ahead of
+    // the computation they overlap.
+    issue(0, A);
+    for (int it = 0; it < n_it; it += 2) {
+      issue(it + 1, Bb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, A);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(it + 2, A);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it + 1, Bb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if constexpr (SCORES) {
+    // Positions of this split past the request's end are not candidates.
+    const int f0 = max(t1, t0);
+    const int64_t f1 = (split == a.n_split - 1) ? a.score_stride
+                                                : min((int64_t)t0 + a.split_tokens, a.score_stride);
+    for (int64_t j = f0 + tid; j < f1; j += NT) srow[j] = neg_inf();
+  }
+
+  // Merge the row groups of this wave (lanes that share `sub`).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = m[h];
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float al = (m[h] == neg_inf()) ? 0.f : exp2_fast(m[h] - M);
+    float ls = l[h] * al;
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) ls += __shfl_xor(ls, off);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float x = o[h][e] * al;
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+      o[h][e] = x;
+    }
+    m[h] = M;
+    l[h] = ls;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) wo[(w * G + h) * D + (c * LPR + sub) * EPC + i] = o[h][c * EPC + i];
+      if (sub == 0) {
+        wml[(w * G + h) * 2] = m[h];
+        wml[(w * G + h) * 2 + 1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves and write the split's result.
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int h = idx / D, e = idx % D;
+    float M = neg_inf();
+#pragma unroll
+    for (int x = 0; x < WAVES; ++x) M = fmaxf(M, wml[(x * G + h) * 2]);
+    float ls = 0.f, os = 0.f;
+#pragma unroll
+    for (int x = 0; x < WAVES; ++x) {
+      const float mw = wml[(x * G + h) * 2];
+      const float al = (mw == neg_inf()) ? 0.f : exp2_fast(mw - M);
+      ls = fmaf(al, wml[(x * G + h) * 2 + 1], ls);
+      os = fmaf(al, wo[(x * G + h) * D + e], os);
+    }
+    const int64_t orow = SplitTail<D>::row(a, q_row0, g, G, h);
+    if (a.n_split == 1) {
+      a.out[orow * D + e] = ls > 0.f ? os / ls : 0.f;
+      if (e == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M + log2f(ls)) * kLn2 : neg_inf();
+    } else {
+      const int64_t prow = orow * a.part_stride + split;
+      store_coherent(a.part_o + prow * D + e, os);
+      if (e == 0) {
+        store_coherent(a.part_ml + prow * 2, M);
+        store_coherent(a.part_ml + prow * 2 + 1, ls);
+      }
+    }
+  }
+  if (a.n_split > 1)
+    SplitTail<D>::run(a, b, g, q_row0, G, G, kMaxSplits, reinterpret_cast<int*>(wml + WAVES * G * 2),
+                      wml + WAVES * G * 2 + 4);
+}
+
+}  // namespace sfi

@@ -34,8 +34,10 @@ constexpr int kMaxMixedBatch = 64;
 struct AttnArgs {
   int32_t Hq, Hkv;
   int32_t max_pages, num_pages, max_seq_len;
-  const void* q;          // request b's rows start at q + b * q_stride_b elements
-  int64_t q_stride_b;
+  // Query rows: request b's query token t is row (q_row0(b) + t) of q, out and lse,
+  // with q_row0(b) = b * t_q for single-kind calls (a per-request table for the
+  // mixed launch); head hq of that token is element row * Hq + hq.
+  const void* q;          // [rows, Hq, d]
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;
@@ -49,25 +51,24 @@ struct AttnArgs {
   float scale_log2;       // scale * log2(e)
   int32_t split_tokens, n_split;
   int32_t t_q;            // query tokens of the request (dense / verify)
-  float* out;             // request b's rows start at out + b * out_stride_b
-  int64_t out_stride_b;
-  float* lse;             // request b's rows start at lse + b * lse_stride_b (nullable)
-  int64_t lse_stride_b;
-  float* part_o;          // split partials [rows, n_split, d]; row = b * rows_b + r
-  float* part_ml;         // [rows, n_split, 2] = (max in log2 units, sum)
+  float* out;             // [rows, Hq, d]
+  float* lse;             // [rows, Hq] (nullable)
+  float* part_o;          // split partials [rows * Hq, part_stride, d]
+  float* part_ml;         // [rows * Hq, part_stride, 2] = (max in log2 units, sum)
+  int32_t part_stride;    // split slots per partial row (>= n_split)
   int32_t* counters;      // [B * Hkv] split arrival counters (zero between calls)
-  int32_t rows_b;         // partial rows per request (t_q * Hq)
   float* scores;          // [B, Hkv, score_stride] (nullable)
   int64_t score_stride;
 };
 
-// Per-request plan of the mixed launch.
+// Work list of the mixed launch (travels in kernel arguments).  Entry e serves
+// request req[e] with work-groups [wg_begin[e], wg_begin[e + 1]), Hkv * n_split[e]
+// of them; verifying requests come first (they are the longest).
 struct MixedPlan {
-  int32_t n_req;
-  int32_t n_wg;                         // total work-groups
-  int32_t wg_begin[kMaxMixedBatch + 1]; // first work-group of each request (ordered list)
-  int32_t req[kMaxMixedBatch];          // request served by each list entry
-  int32_t mode[kMaxMixedBatch];         // 0 draft, 1 verify
+  int32_t n_entries;
+  int32_t wg_begin[kMaxMixedBatch + 1];
+  int32_t req[kMaxMixedBatch];
+  int32_t mode[kMaxMixedBatch];         // 0 draft (fast step), 1 verify (dense, causal)
   int32_t t_q[kMaxMixedBatch];
   int32_t q_row0[kMaxMixedBatch];       // first query row of the request
   int32_t n_split[kMaxMixedBatch];
@@ -78,12 +79,7 @@ struct MixedPlan {
 hipError_t launch_decode(const AttnArgs& a, int dtype, int d, int G, bool sparse, int B,
                          hipStream_t stream);
 hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream);
-hipError_t launch_mixed(const AttnArgs& draft, const AttnArgs& verify, const MixedPlan& plan,
-                        int d, int G, hipStream_t stream);
-hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int n_split, int d,
-                          float* out, float* lse, hipStream_t stream);
-hipError_t launch_combine_mixed(const AttnArgs& draft, const AttnArgs& verify,
-                                const MixedPlan& plan, int d, hipStream_t stream);
+hipError_t launch_mixed(const AttnArgs& a, const MixedPlan& plan, int d, int G, hipStream_t stream);
 hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, const int32_t* seq_lens,
                          int t_q, int n_sink, int n_recent, int k, int32_t* sel,
                          hipStream_t stream);

@@ -156,6 +156,7 @@ sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_
 }
 
 void set_partials(sfi::AttnArgs& a, void* ws, int64_t rows, int d) {
+  a.part_stride = a.n_split;
   if (a.n_split <= 1) return;
   char* p = static_cast<char*>(ws);
   a.counters = reinterpret_cast<int32_t*>(p);
@@ -169,6 +170,74 @@ sfi_status check_workspace(const void* ws, size_t have, size_t need) {
   if (!ws) return fail(SFI_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
   if (!aligned16(ws)) return fail(SFI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   return SFI_OK;
+}
+
+// Work list of a mixed launch: verifying requests first, then drafting ones.
+struct MixedSetup {
+  sfi::MixedPlan plan;
+  int part_stride;   // largest split count of any entry
+  int rows;          // packed query rows (sum of t_q)
+};
+
+sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes, const int32_t* t_q,
+                      int32_t cap, int32_t n_recent, MixedSetup* ms) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!modes || !t_q) return fail(SFI_ERR_INVALID_ARG, "modes and t_q must be non-NULL host arrays");
+  const int B = shape->batch, G = shape->num_q_heads / shape->num_kv_heads;
+  if (B > sfi::kMaxMixedBatch) return fail(SFI_ERR_UNSUPPORTED, "mixed launch takes at most %d requests", sfi::kMaxMixedBatch);
+  if (shape->dtype != SFI_BF16) return fail(SFI_ERR_UNSUPPORTED, "mixed launch needs bf16 inputs");
+  if (cap < 1 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1 and n_recent >= 0");
+  if ((int64_t)cap + n_recent > kMaxTokens)
+    return fail(SFI_ERR_UNSUPPORTED, "cap + n_recent exceeds %lld tokens", (long long)kMaxTokens);
+  if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens)
+    return fail(SFI_ERR_UNSUPPORTED, "max_seq_len (%d) exceeds %lld tokens for verification", kv->max_seq_len,
+                (long long)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens);
+  int rows = 0;
+  for (int b = 0; b < B; ++b) {
+    if (modes[b] != 0 && modes[b] != 1) return fail(SFI_ERR_INVALID_ARG, "modes[%d] must be 0 or 1", b);
+    if (t_q[b] < 1 || t_q[b] > 16) return fail(SFI_ERR_INVALID_ARG, "t_q[%d] must be in [1, 16]", b);
+    if (modes[b] == 0 && t_q[b] != 1) return fail(SFI_ERR_INVALID_ARG, "drafting request %d must have t_q = 1", b);
+    if (modes[b] == 1 && t_q[b] * G > sfi::kMaxVerifyRows)
+      return fail(SFI_ERR_UNSUPPORTED, "t_q[%d] * G must be <= %d", b, sfi::kMaxVerifyRows);
+    rows += t_q[b];
+  }
+  const int64_t units = (int64_t)B * shape->num_kv_heads;
+  const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
+  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile);
+  const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
+  sfi::MixedPlan& p = ms->plan;
+  p = sfi::MixedPlan{};
+  int q_row0[sfi::kMaxMixedBatch];
+  for (int b = 0, r = 0; b < B; ++b) {
+    q_row0[b] = r;
+    r += t_q[b];
+  }
+  int e = 0, wg = 0, stride = 1;
+  for (int pass = 1; pass >= 0; --pass)
+    for (int b = 0; b < B; ++b) {
+      if (modes[b] != pass) continue;
+      const Split& sp = pass ? sp_v : sp_d;
+      p.req[e] = b;
+      p.mode[e] = pass;
+      p.t_q[e] = t_q[b];
+      p.q_row0[e] = q_row0[b];
+      p.n_split[e] = sp.n;
+      p.split_tokens[e] = sp.tokens;
+      p.wg_begin[e] = wg;
+      wg += shape->num_kv_heads * sp.n;
+      stride = sp.n > stride ? sp.n : stride;
+      ++e;
+    }
+  p.n_entries = e;
+  p.wg_begin[e] = wg;
+  ms->part_stride = stride;
+  ms->rows = rows;
+  return SFI_OK;
+}
+
+size_t mixed_workspace_bytes(const MixedSetup& ms, const sfi_shape* shape) {
+  return partial_bytes((int64_t)ms.rows * shape->num_q_heads, ms.part_stride, shape->head_dim);
 }
 
 }  // namespace
@@ -216,17 +285,13 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
 
   sfi::AttnArgs a = base_args(shape, kv, seq_lens);
   a.q = q;
-  a.q_stride_b = (int64_t)t_q * shape->num_q_heads * shape->head_dim;
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   a.split_tokens = sp.tokens;
   a.n_split = sp.n;
   a.t_q = t_q;
   a.out = out;
-  a.out_stride_b = (int64_t)t_q * shape->num_q_heads * shape->head_dim;
   a.lse = lse;
-  a.lse_stride_b = (int64_t)t_q * shape->num_q_heads;
-  a.rows_b = t_q * shape->num_q_heads;
   a.scores = scores;
   a.score_stride = score_stride;
   set_partials(a, workspace, rows, shape->head_dim);
@@ -318,7 +383,6 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
 
   sfi::AttnArgs a = base_args(shape, kv, seq_lens);
   a.q = q;
-  a.q_stride_b = (int64_t)shape->num_q_heads * shape->head_dim;
   a.ck = compact_k;
   a.cv = compact_v;
   a.cap = cap;
@@ -329,10 +393,7 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
   a.n_split = sp.n;
   a.t_q = 1;
   a.out = out;
-  a.out_stride_b = (int64_t)shape->num_q_heads * shape->head_dim;
   a.lse = lse;
-  a.lse_stride_b = shape->num_q_heads;
-  a.rows_b = shape->num_q_heads;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
@@ -342,8 +403,11 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,
                                          const int32_t* t_q, int32_t cap, int32_t n_recent, size_t* bytes) {
-  (void)shape; (void)kv; (void)modes; (void)t_q; (void)cap; (void)n_recent; (void)bytes;
-  return fail(SFI_ERR_UNSUPPORTED, "mixed launch not available in this build");
+  if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
+  MixedSetup ms;
+  SFI_TRY(plan_mixed(shape, kv, modes, t_q, cap, n_recent, &ms));
+  *bytes = mixed_workspace_bytes(ms, shape);
+  return ok();
 }
 
 sfi_status sfi_mixed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, const int32_t* modes,
@@ -351,10 +415,38 @@ sfi_status sfi_mixed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const 
                           const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
                           float* out, float* lse, float* scores, int64_t score_stride, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  (void)shape; (void)kv; (void)q; (void)modes; (void)t_q; (void)seq_lens; (void)n_sink; (void)n_recent;
-  (void)compact_k; (void)compact_v; (void)cap; (void)n_compact; (void)out; (void)lse; (void)scores;
-  (void)score_stride; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(SFI_ERR_UNSUPPORTED, "mixed launch not available in this build");
+  MixedSetup ms;
+  SFI_TRY(plan_mixed(shape, kv, modes, t_q, cap, n_recent, &ms));
+  SFI_TRY(check_ptr16(q, "q"));
+  SFI_TRY(check_ptr16(out, "out"));
+  SFI_TRY(check_ptr16(compact_k, "compact_k"));
+  SFI_TRY(check_ptr16(compact_v, "compact_v"));
+  if (!seq_lens || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens and n_compact must be non-NULL");
+  SFI_TRY(check_budgets(n_sink, n_recent));
+  if (scores && score_stride < kv->max_seq_len)
+    return fail(SFI_ERR_INVALID_ARG, "score_stride (%lld) must be >= max_seq_len (%d)", (long long)score_stride,
+                kv->max_seq_len);
+  if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
+    return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
+  SFI_TRY(check_workspace(workspace, workspace_bytes, mixed_workspace_bytes(ms, shape)));
+
+  sfi::AttnArgs a = base_args(shape, kv, seq_lens);
+  a.q = q;
+  a.ck = compact_k;
+  a.cv = compact_v;
+  a.cap = cap;
+  a.n_compact = n_compact;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_split = ms.part_stride;   // sizes the partial layout; every entry uses its own split count
+  set_partials(a, workspace, (int64_t)ms.rows * shape->num_q_heads, shape->head_dim);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const hipError_t e = sfi::launch_mixed(a, ms.plan, shape->head_dim, G, static_cast<hipStream_t>(stream));
+  return hip_status(e, "mixed launch");
 }
 
 sfi_status sfi_plan_splits(int32_t op, const sfi_shape* shape, const sfi_paged_kv* kv, int32_t t_q, int32_t cap,

@@ -31,8 +31,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // A unit (b, g) owns R = t_q * G output rows: row r = (t, h) with t = r / G,
-// h = r % G, stored at global row b * rows_b + t * Hq + g * G + h of out, lse and
-// the partials [rows, n_split, D] / [rows, n_split, 2].
+// h = r % G is head row (q_row0 + t) * Hq + g * G + h of out, lse and the partials
+// [.., part_stride, D] / [.., part_stride, 2].
 template <int D>
 struct SplitTail {
   static constexpr int NT = 256;
@@ -40,8 +40,8 @@ struct SplitTail {
 
   __host__ __device__ static constexpr int bytes(int R, int ns_max) { return (2 * R * ns_max + 2 * R) * 4; }
 
-  __device__ static int64_t row(const AttnArgs& a, int b, int g, int G, int r) {
-    return (int64_t)b * a.rows_b + (int64_t)(r / G) * a.Hq + g * G + r % G;
+  __device__ static int64_t row(const AttnArgs& a, int q_row0, int g, int G, int r) {
+    return (int64_t)(q_row0 + r / G) * a.Hq + g * G + r % G;
   }
 
   // Called by every work-group of the unit after it has stored its partials.
@@ -51,7 +51,8 @@ struct SplitTail {
   // counter to zero.  Every step is parallel: all (m, l) pairs are fetched at
   // once, per-row max and sum are wave reductions, and each output element keeps
   // up to BATCH partial loads in flight.  tail: LDS of bytes(R, ns_max).
-  __device__ static void run(const AttnArgs& a, int b, int g, int G, int R, int ns_max, int* flag, float* tail) {
+  __device__ static void run(const AttnArgs& a, int b, int g, int q_row0, int G, int R, int ns_max, int* flag,
+                             float* tail) {
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     constexpr int WAVES = NT / kWave;
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
@@ -70,7 +71,7 @@ struct SplitTail {
     float* L_r = M_r + R;
     for (int i = tid; i < R * ns; i += NT) {
       const int r = i / ns, s = i % ns;
-      const float* ml = a.part_ml + (row(a, b, g, G, r) * ns + s) * 2;
+      const float* ml = a.part_ml + (row(a, q_row0, g, G, r) * a.part_stride + s) * 2;
       w_s[r * ns_max + s] = load_coherent(ml);
       l_s[r * ns_max + s] = load_coherent(ml + 1);
     }
@@ -95,8 +96,8 @@ struct SplitTail {
     __syncthreads();
     for (int idx = tid; idx < R * D; idx += NT) {
       const int r = idx / D, e = idx % D;
-      const int64_t orow = row(a, b, g, G, r);
-      const float* po = a.part_o + orow * ns * D + e;
+      const int64_t orow = row(a, q_row0, g, G, r);
+      const float* po = a.part_o + orow * a.part_stride * D + e;
       const float* wr = w_s + r * ns_max;
       float os = 0.f;
       for (int s0 = 0; s0 < ns; s0 += BATCH) {

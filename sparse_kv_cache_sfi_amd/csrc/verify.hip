@@ -1,326 +1,13 @@
-// Multi-query causal attention on MFMA for t_q > 1 query tokens per request.
-//
-// Full-context verification of t_q draft tokens (SparseSpec-L abstract: drafts
-// are verified with full attention, whose per-head statistics are reused as the
-// importance signal) is a real dense contraction: the R = t_q * G query rows of
-// one KV head share every K/V row, so QK^T and PV run on the matrix cores.
-//
-// One work-group (4 waves) per (split, KV head g, request b); each wave takes
-// 32-token tiles of the split in turn.  Per tile:
-//   * the K and V rows (one or two 16-token pages) are loaded with coalesced
-//     16-byte loads into registers one tile ahead and parked in the wave's LDS;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (tokens x rows), so every lane
-//     owns one query row and 16 of the tile's tokens: the causal mask, the
-//     online softmax (log2 units, reference max raised only by > 8) and the row
-//     max need no cross-lane work beyond one swap between the lane halves;
-//   * O^T += V^T P^T on the same instruction.  The probabilities are split into
-//     bf16 hi + lo parts (two MFMAs) so the product keeps fp32-level accuracy;
-//     the token order of the contraction is chosen so that P^T comes straight
-//     from the S^T accumulator registers, and V^T is gathered from LDS;
-//   * optionally the masked logits summed over all R rows (the verification
-//     statistics) for every candidate token.
-// Waves are merged through LDS; splits through the shared split tail.
-#include "common.h"
-#include "kernels.h"
-#include "split_tail.h"
+// Kernels and launchers of the MFMA multi-query verification (t_q > 1).
+// The device code and its design notes are in verify_unit.h.
+#include "verify_unit.h"
 
 namespace sfi {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-
-template <int D>
-struct VerifyShape {
-  static constexpr int KS = D / 16;                         // QK^T k-steps of 16 dims
-  static constexpr int DB = D / 32;                         // 32-dim blocks of O^T
-  static constexpr int ROW_BYTES = D * 2;                   // bf16 row
-  static constexpr int LDS_ROW = ROW_BYTES + 16;            // padded LDS row stride
-  static constexpr int TILE = kVerifyTile;                  // 32 tokens
-  static constexpr int WAVES = 4;
-  static constexpr int CPR = ROW_BYTES / 16;                // 16-byte chunks per row
-  static constexpr int LOADS = TILE * CPR / kWave;          // loads per lane per tile per tensor
-  static constexpr int WAVE_LDS = 2 * TILE * LDS_ROW;       // K and V tiles of one wave
-  static constexpr int MERGE = WAVES * (32 * D + 64) * 4;   // per-wave O, m, l for the merge
-  static constexpr int TILES_LDS = WAVES * WAVE_LDS > MERGE ? WAVES * WAVE_LDS : MERGE;
-  static constexpr int TAIL = SplitTail<D>::bytes(32, kMaxVerifySplits);
-  static constexpr int BIG = TILES_LDS > TAIL ? TILES_LDS : TAIL;
-  static constexpr int SMEM = kBtSlots * 4 + 16 + BIG;
-  static_assert(LOADS >= 1, "tile too small");
-};
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-// Sum over the 32 lanes of each half-wave (rows of the S^T tile).
-__device__ __forceinline__ float half_sum(float x) {
-  x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  return x;
-}
-
-template <int D, bool SCORES>
-__device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, const int g, const int split, const int G,
-                                            char* smem) {
-  using S = VerifyShape<D>;
-  constexpr int KS = S::KS, DB = S::DB, LDS_ROW = S::LDS_ROW, TILE = S::TILE, WAVES = S::WAVES;
-  constexpr int CPR = S::CPR, LOADS = S::LOADS, NT = WAVES * kWave;
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  const int hb = lane >> 5, n = lane & 31;
-  const int R = a.t_q * G;
-
-  int* bt_s = reinterpret_cast<int*>(smem);
-  int* flag = bt_s + kBtSlots;
-  char* big = smem + kBtSlots * 4 + 16;
-  char* kt = big + w * S::WAVE_LDS;   // this wave's K tile, then its V tile
-  char* vt = kt + TILE * LDS_ROW;
-
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
-  const int t0 = split * a.split_tokens;
-  const int t1 = min(L, t0 + a.split_tokens);
-
-  int pg_lo = 0, n_pg = 0;
-  if (t1 > t0) {
-    pg_lo = t0 >> 4;
-    n_pg = ((t1 - 1) >> 4) - pg_lo + 1;
-  }
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  for (int i = tid; i < n_pg; i += NT) {
-    const int e = bt_row[pg_lo + i];
-    bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
-  }
-
-  // Query rows as the B operand: lane holds row n, dims [16 s + 8 hb, +8) of step s.
-  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_stride_b;
-  const int qt = n / G, qh = n % G;
-  const bool row_ok = n < R;
-  const uint16_t* qrow = qbase + ((int64_t)qt * a.Hq + g * G + qh) * D;
-  u32x4 qb[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    qb[s] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hb) : z;
-  }
-  // Query token t sits at position L - t_q + t and sees keys up to it.
-  const int lim = row_ok ? L - a.t_q + qt : -1;
-  __syncthreads();
-
-  int clo = 0, chi = 0;
-  float* srow = nullptr;
-  if constexpr (SCORES) {
-    candidate_bounds(L, a.t_q, a.n_sink, a.n_recent, &clo, &chi);
-    srow = a.scores + ((int64_t)b * a.Hkv + g) * a.score_stride;
-  }
-
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.v_pool);
-  const int64_t page_elems = (int64_t)a.Hkv * kPage * D;
-  const int64_t head_off = (int64_t)g * kPage * D;
-
-  const int n_tiles = (t1 > t0) ? (t1 - t0 + TILE - 1) / TILE : 0;
-  const int iters = (n_tiles + WAVES - 1) / WAVES;   // uniform across waves (barriers inside)
-
-  // Global loads of one tile: lane covers rows (i * kWave + lane) / CPR, chunk lane % CPR.
-  auto load_tile = [&](int it, u32x4 (&kr)[LOADS], u32x4 (&vr)[LOADS]) {
-    const int tb = t0 + (it * WAVES + w) * TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int rr = (i * kWave + lane) / CPR, ch = (i * kWave + lane) % CPR;
-      const int pos = tb + rr;
-      const bool in = pos < t1;
-      const int pg = bt_s[in ? (pos >> 4) - pg_lo : 0];
-      const int64_t off = (in && pg >= 0) ? (int64_t)pg * page_elems + head_off + (int64_t)(pos & 15) * D : 0;
-      kr[i] = *reinterpret_cast<const u32x4*>(kpool + off + ch * 8);
-      vr[i] = *reinterpret_cast<const u32x4*>(vpool + off + ch * 8);
-    }
-  };
-  auto park_tile = [&](const u32x4 (&kr)[LOADS], const u32x4 (&vr)[LOADS]) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int rr = (i * kWave + lane) / CPR, ch = (i * kWave + lane) % CPR;
-      *reinterpret_cast<u32x4*>(kt + rr * LDS_ROW + ch * 16) = kr[i];
-      *reinterpret_cast<u32x4*>(vt + rr * LDS_ROW + ch * 16) = vr[i];
-    }
-  };
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f;
-
-  if (iters > 0) {
-    u32x4 kr[LOADS], vr[LOADS];
-    load_tile(0, kr, vr);
-    park_tile(kr, vr);
-    __syncthreads();
-  }
-  for (int it = 0; it < iters; ++it) {
-    u32x4 kr[LOADS], vr[LOADS];
-    const bool more = it + 1 < iters;
-    if (more) load_tile(it + 1, kr, vr);   // consumed at the end of this iteration
-
-    const int tb = t0 + (it * WAVES + w) * TILE;
-    // Which of the tile's 32 tokens exist (inside the split, behind a valid page).
-    bool tok_ok;
-    {
-      const int pos = tb + n;
-      tok_ok = pos < t1 && bt_s[pos < t1 ? (pos >> 4) - pg_lo : 0] >= 0;
-    }
-    const uint64_t okmask = __ballot(tok_ok);
-
-    // S^T = K Q^T over the tile: lane (n, hb) -> token 8 (i / 4) + 4 hb + i % 4, row n.
-    f32x16 sacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + n * LDS_ROW + (16 * s + 8 * hb) * 2);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb[s]),
-                                                      sacc, 0, 0, 0);
-    }
-
-    if constexpr (SCORES) {
-      // Masked logits summed over all R rows (rows past R hold zero queries).
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float tot = half_sum(sacc[i]);
-        const int tok = 8 * (i / 4) + 4 * hb + (i % 4);
-        const int pos = tb + tok;
-        if (n == 0 && pos < t1) {
-          const bool ok = (okmask >> tok) & 1ull;
-          srow[pos] = (ok && pos >= clo && pos < chi) ? tot * a.scale : neg_inf();
-        }
-      }
-    }
-
-    float sv[16];
-    float mx = neg_inf();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = 8 * (i / 4) + 4 * hb + (i % 4);
-      const bool vis = ((okmask >> tok) & 1ull) && tb + tok <= lim;
-      sv[i] = vis ? sacc[i] * a.scale_log2 : neg_inf();
-      mx = fmaxf(mx, sv[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__any(mx > m_run + 8.f)) {
-      const float mn = fmaxf(m_run, mx);
-      const float al = (m_run == neg_inf()) ? 0.f : exp2_fast(m_run - mn);
-      l_run *= al;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= al;
-      m_run = mn;
-    }
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = (m_run == neg_inf()) ? 0.f : exp2_fast(sv[i] - m_run);
-      l_run += p[i];
-    }
-    // P^T as the B operand, hi and lo bf16 parts; k-index 8 hb + j of step s is the
-    // token held in accumulator register 8 s + j.
-    u32x4 phi[2], plo[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = p[8 * s + 2 * j], x1 = p[8 * s + 2 * j + 1];
-        hw[j] = pack_bf16x2(x0, x1);
-        const float h0 = bf16_lo(hw[j]), h1 = bf16_hi(hw[j]);
-        lw[j] = pack_bf16x2(x0 - h0, x1 - h1);
-      }
-      phi[s] = (u32x4){hw[0], hw[1], hw[2], hw[3]};
-      plo[s] = (u32x4){lw[0], lw[1], lw[2], lw[3]};
-    }
-    // O^T += V^T P^T: lane (dim 32 db + n, hb) gathers V at tokens 16 s + 8 (j / 4) + 4 hb + j % 4.
-    const uint16_t* vtu = reinterpret_cast<const uint16_t*>(vt);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint32_t va[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t_a = 16 * s + 8 * ((2 * j) / 4) + 4 * hb + (2 * j) % 4;
-          const int t_b = 16 * s + 8 * ((2 * j + 1) / 4) + 4 * hb + (2 * j + 1) % 4;
-          const uint32_t lo = vtu[(t_a * LDS_ROW) / 2 + 32 * db + n];
-          const uint32_t hi = vtu[(t_b * LDS_ROW) / 2 + 32 * db + n];
-          va[j] = lo | (hi << 16);
-        }
-        const bf16x8 vA = __builtin_bit_cast(bf16x8, (u32x4){va[0], va[1], va[2], va[3]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, phi[s]), oacc[db], 0, 0, 0);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, plo[s]), oacc[db], 0, 0, 0);
-      }
-    }
-    __syncthreads();   // every wave is done reading its tiles
-    if (more) {
-      park_tile(kr, vr);
-      __syncthreads();
-    }
-  }
-
-  // Merge the waves through LDS (the tile area is free now).
-  float* mo = reinterpret_cast<float*>(big);                // [WAVES][32][D]
-  float* mml = mo + WAVES * 32 * D;                         // [WAVES][32][2]
-  l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dim = 32 * db + 8 * (i / 4) + 4 * hb + (i % 4);
-      mo[(w * 32 + n) * D + dim] = oacc[db][i];
-    }
-  if (hb == 0) {
-    mml[(w * 32 + n) * 2] = m_run;
-    mml[(w * 32 + n) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < R * D; idx += NT) {
-    const int r = idx / D, e = idx % D;
-    float M = neg_inf();
-#pragma unroll
-    for (int x = 0; x < WAVES; ++x) M = fmaxf(M, mml[(x * 32 + r) * 2]);
-    float ls = 0.f, os = 0.f;
-#pragma unroll
-    for (int x = 0; x < WAVES; ++x) {
-      const float mw = mml[(x * 32 + r) * 2];
-      const float al = (mw == neg_inf()) ? 0.f : exp2_fast(mw - M);
-      ls = fmaf(al, mml[(x * 32 + r) * 2 + 1], ls);
-      os = fmaf(al, mo[(x * 32 + r) * D + e], os);
-    }
-    const int64_t orow = SplitTail<D>::row(a, b, g, G, r);
-    if (a.n_split == 1) {
-      a.out[orow * D + e] = ls > 0.f ? os / ls : 0.f;
-      if (e == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M + log2f(ls)) * kLn2 : neg_inf();
-    } else {
-      store_coherent(a.part_o + (orow * a.n_split + split) * D + e, os);
-      if (e == 0) {
-        store_coherent(a.part_ml + (orow * a.n_split + split) * 2, M);
-        store_coherent(a.part_ml + (orow * a.n_split + split) * 2 + 1, ls);
-      }
-    }
-  }
-  if constexpr (SCORES) {
-    const int f0 = max(t1, t0);
-    const int64_t f1 = (split == a.n_split - 1) ? a.score_stride : min((int64_t)t0 + a.split_tokens, a.score_stride);
-    for (int64_t j = f0 + tid; j < f1; j += NT) srow[j] = neg_inf();
-  }
-  if (a.n_split > 1) {
-    __syncthreads();   // the merge area becomes the tail's scratch
-    SplitTail<D>::run(a, b, g, G, R, kMaxVerifySplits, flag, reinterpret_cast<float*>(big));
-  }
-}
 
 template <int D, bool SCORES>
 __global__ __launch_bounds__(256) void verify_kernel(AttnArgs a, int G) {
   __shared__ __attribute__((aligned(16))) char smem[VerifyShape<D>::SMEM];
-  verify_unit<D, SCORES>(a, blockIdx.z, blockIdx.y, blockIdx.x, G, smem);
+  verify_unit<D, SCORES>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z * a.t_q, G, smem);
 }
 
 hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream) {
@@ -339,13 +26,6 @@ hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t str
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-hipError_t launch_mixed(const AttnArgs&, const AttnArgs&, const MixedPlan&, int, int, hipStream_t) {
-  return hipErrorNotSupported;
-}
-hipError_t launch_combine_mixed(const AttnArgs&, const AttnArgs&, const MixedPlan&, int, hipStream_t) {
-  return hipErrorNotSupported;
 }
 
 }  // namespace sfi

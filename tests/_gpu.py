@@ -57,7 +57,8 @@ def assert_close(got, ref, tol, what):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    err = np.abs(got - ref)
+    with np.errstate(invalid="ignore"):
+        err = np.where(got == ref, 0.0, np.abs(got - ref))   # equal infinities match
     bad = ~(err <= tol)
     assert not bad.any(), f"{what}: max err {np.nanmax(err):.3e} > {tol} at {np.argwhere(bad)[:5].tolist()}"
     return float(err.max()) if err.size else 0.0
