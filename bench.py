@@ -27,16 +27,51 @@ kernel's HBM roofline fraction, and the fp64 oracle's throughput on host cores.
 """
 import argparse
 import json
-import math
 import os
+import re
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode-attn effective KV GB/s (% HBM peak) + speedup vs dense at 16K"
+
+
+DECODE_SOURCES = ["sparse_kv_cache_sfi_amd/csrc/decode_unit.h", "sparse_kv_cache_sfi_amd/csrc/split_tail.h",
+                  "sparse_kv_cache_sfi_amd/csrc/decode.hip", "sparse_kv_cache_sfi_amd/csrc/common.h"]
+TRAFFIC_PROFILE = "profiles/decode_layer_16k_b1_hbm_bytes.txt"
+DENSE_KERNEL = "decode_kernel<unsigned short, 128, 2, false, true>"
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha1()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the slow-step kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what a plain copy of known size reads back),
+    or None when the summary is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    m = re.search(r"decode kernel source sha1\[:16\]: ([0-9a-f]+)", text)
+    if not m or m.group(1) != decode_source_hash():
+        return None, "kernel changed since the counters were taken"
+    for line in text.splitlines():
+        if DENSE_KERNEL in line:
+            read_mib, write_mib = (float(x) for x in line.split()[-2:])
+            return int(round((read_mib + write_mib) * 2 ** 20)), TRAFFIC_PROFILE
+    return None, "kernel not in counter summary"
 
 
 def log(msg):
@@ -87,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--aux-stream", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -183,10 +220,11 @@ def main():
     step_bytes = dense_kv + pack_bytes + fast_kv
     value = step_bytes / step_s / 1e9
     dense_alg = dense_kv + B * Hkv * L * 4            # K/V read + scores written
+    traffic, traffic_src = profiled_traffic()
     roof = {"kernel": "decode_kernel<bf16,d128,G2,dense+scores> (slow step)", "bound": "hbm",
             "achieved": dense_alg / dense_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
-            "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6}
+            "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_source": traffic_src, "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6}
     log(f"step {step_s * 1e6:.1f} us, {value:.0f} GB/s; dense kernel {dense_s * 1e6:.1f} us "
         f"= {roof['achieved']:.0f} GB/s ({100 * roof['frac']:.1f}% of peak)")
 
@@ -210,8 +248,20 @@ def main():
         result["sweep_b16"] = sweep(sfi, big, dev, main_s, 16, Hq, Hkv, d, L, n_sink, n_recent, None, None)
         del big
 
+    if not args.no_sweep:
+        log("64K refresh overlap")
+        result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
+        log("128K speculative mix")
+        result["specmix_128k"] = specmix(sfi, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, L, B, frac, n_sink, n_recent, step_bytes)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            sfi.stream_copy(src, dst)
+        torch.cuda.synchronize()
     print(json.dumps(result), flush=True)
 
 
@@ -281,6 +331,139 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
         del comp
     log("sweep " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows))
     return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows}
+
+
+def refresh_overlap(sfi, dev):
+    """Slow-step maintenance hidden behind the next layer (SFI page, Fig. 3A).  Layer i's slow step
+    (dense + logits, 4 requests x 64K, 32 query / 8 KV heads) is followed by its Selector (top-2048 per
+    KV head) and pack, and by layer i+1's attention (dense, or a fast step over 2308 tokens).  Serial:
+    all on one stream.  Overlapped: Selector + pack on a second stream while the main stream runs
+    layer i+1.  hidden = (serial - overlapped) / (Selector + pack)."""
+    import torch
+    from sfi_synth import refresh64k_case
+    c = refresh64k_case(4)
+    L, B, Hq, Hkv, d = 65536, c.B, c.Hq, c.Hkv, c.d
+    k, v, bt = upload(c.kv.k, dev), upload(c.kv.v, dev), upload(c.kv.block_table, dev)
+    lens, q = upload(c.seq_lens, dev), upload(c.q, dev)
+    q1 = upload(np.ascontiguousarray(c.q[:, 0]), dev)
+    del c
+    main_s = torch.cuda.current_stream(dev)
+    aux_s = torch.cuda.Stream(device=dev)
+    cap = 4 + 2048
+    outs = [torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev) for _ in range(2)]
+    lses = [torch.empty((B, 1, Hq), dtype=torch.float32, device=dev) for _ in range(2)]
+    scores = torch.empty((B, Hkv, L), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Hkv, 2048), dtype=torch.int32, device=dev)
+    ck = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    nc = torch.empty((B,), dtype=torch.int32, device=dev)
+    fo = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    fl = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_a = torch.zeros(sfi.workspace_size("dense", k_pool=k, block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                          max_seq_len=L) + 16, dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros_like(ws_a)
+    ws_f = torch.zeros(sfi.workspace_size("sparse", k_pool=k, block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                          max_seq_len=L, cap=cap, n_recent=256) + 16, dtype=torch.uint8, device=dev)
+    # prepare a compact buffer once so the fast-step partner has real input
+    sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[0], lse=lses[0],
+                              scores=scores, workspace=ws_a)
+    sfi.select_topk(scores, lens, k=2048, n_sink=4, n_recent=256, sel_idx=sel)
+    sfi.pack_compact(k, v, bt, lens, sel, n_sink=4, cap=cap, max_seq_len=L, compact_k=ck, compact_v=cv,
+                     n_compact=nc)
+    torch.cuda.synchronize()
+
+    def slow(stream):
+        sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[0],
+                                  lse=lses[0], scores=scores, workspace=ws_a, stream=stream)
+
+    def maint(stream):
+        sfi.select_topk(scores, lens, k=2048, n_sink=4, n_recent=256, sel_idx=sel, stream=stream)
+        sfi.pack_compact(k, v, bt, lens, sel, n_sink=4, cap=cap, max_seq_len=L, compact_k=ck, compact_v=cv,
+                         n_compact=nc, stream=stream)
+
+    def partner(kind, stream):
+        if kind == "dense":
+            sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, with_scores=False, out=outs[1],
+                                      lse=lses[1], workspace=ws_b, stream=stream)
+        else:
+            sfi.sparse_decode_attn(q1, k, v, bt, lens, ck, cv, nc, n_sink=4, n_recent=256, max_seq_len=L,
+                                   out=fo, lse=fl, workspace=ws_f, stream=stream)
+
+    n = 20
+    res = {"requests": B, "kv_len": L, "top_k": 2048, "launches": n}
+    res["slow_us"] = round(time_loop(lambda i: slow(main_s), n, main_s) * 1e6, 2)
+    res["select_pack_us"] = round(time_loop(lambda i: maint(main_s), n, main_s) * 1e6, 2)
+    for kind in ("dense", "fast"):
+        t_p = time_loop(lambda i: partner(kind, main_s), n, main_s)
+
+        def serial(i):
+            slow(main_s)
+            maint(main_s)
+            partner(kind, main_s)
+
+        def overlapped(i):
+            slow(main_s)
+            ev = torch.cuda.Event()
+            ev.record(main_s)
+            aux_s.wait_event(ev)
+            maint(aux_s)
+            partner(kind, main_s)
+            done = torch.cuda.Event()
+            done.record(aux_s)
+            main_s.wait_event(done)
+
+        t_s = time_loop(serial, n, main_s)
+        t_o = time_loop(overlapped, n, main_s)
+        m = res["select_pack_us"] * 1e-6
+        res[f"partner_{kind}"] = {"partner_us": round(t_p * 1e6, 2), "serial_us": round(t_s * 1e6, 2),
+                                  "overlapped_us": round(t_o * 1e6, 2),
+                                  "hidden_fraction": round(max(0.0, min(1.0, (t_s - t_o) / m)), 3)}
+    log(f"refresh overlap {res}")
+    return res
+
+
+def specmix(sfi, dev):
+    """4 drafting requests (fast step, 5 % retention) + 4 verifying requests (8 draft tokens, dense causal,
+    with statistics) at KV length 131072, 32 query / 8 KV heads: one mixed launch vs the two separate calls."""
+    import torch
+    from sfi_synth import specmix128k_case
+    c = specmix128k_case(5)
+    L, B, Hq, Hkv, d, T = 131072, c.B, c.Hq, c.Hkv, c.d, c.t_q
+    k, v, bt, lens = upload(c.kv.k, dev), upload(c.kv.v, dev), upload(c.kv.block_table, dev), upload(c.seq_lens, dev)
+    modes = c.modes.tolist()
+    k_sel = c.k_sel
+    cap = 4 + k_sel
+    rng = np.random.default_rng(3)
+    sel = np.sort(rng.integers(4, L - 256, size=(B, Hkv, k_sel)), axis=2).astype(np.int32)
+    ck, cv, nc = sfi.pack_compact(k, v, bt, lens, torch.from_numpy(sel).to(dev), n_sink=4, cap=cap, max_seq_len=L)
+    t_q = [1 if m == 0 else T for m in modes]
+    rows = np.concatenate([c.q[b, -1:] if modes[b] == 0 else c.q[b] for b in range(B)], axis=0)
+    qm = upload(rows, dev)
+    out = torch.empty((sum(t_q), Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((sum(t_q), Hq), dtype=torch.float32, device=dev)
+    sc = torch.empty((B, Hkv, L), dtype=torch.float32, device=dev)
+    ws = torch.zeros(sfi.workspace_size("mixed", k_pool=k, block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                        max_seq_len=L, cap=cap, n_recent=256, modes=modes, t_q_per_req=t_q) + 16,
+                     dtype=torch.uint8, device=dev)
+    main_s = torch.cuda.current_stream(dev)
+    n_draft = modes.count(0)
+    del c
+
+    def mixed(i):
+        sfi.mixed_attn(qm, k, v, bt, lens, modes, t_q, ck, cv, nc, n_sink=4, n_recent=256, max_seq_len=L,
+                       out=out, lse=lse, scores=sc, workspace=ws, stream=main_s)
+    n = 10
+    mixed(0)
+    t_m = time_loop(mixed, n, main_s)
+    kv_verify = (B - n_draft) * Hkv * L * 2 * d * 2
+    kv_draft = n_draft * Hkv * (cap + 256) * 2 * d * 2
+    flops = (B - n_draft) * Hkv * L * (T * (Hq // Hkv)) * 2 * d * 2       # QK^T and PV, dense causal bound
+    res = {"requests": B, "drafting": n_draft, "kv_len": L, "t_q": T, "mixed_us": round(t_m * 1e6, 1),
+           "kv_GBps": round((kv_verify + kv_draft) / t_m / 1e9, 1),
+           "pct_hbm_peak": round(100 * (kv_verify + kv_draft) / t_m / 1e9 / HBM_PEAK_GBS, 1),
+           "mfma_TFLOPs": round(flops / t_m / 1e12, 2), "mfma_pct_bf16_peak": round(100 * flops / t_m / 2.5e15, 2)}
+    log(f"specmix {res}")
+    return res
 
 
 def cpu_baseline(budget_s, L, B, frac, n_sink, n_recent, step_bytes):

@@ -162,10 +162,151 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   for (int i = k_eff + tid; i < k; i += kSelThreads) out[i] = -1;
 }
 
+// ---------------------------------------------------------------------------- register-resident variant
+// For rows of at most 1024 * V candidates: thread t keeps candidates
+// [lo + t V, lo + t V + V) as keys in registers, so the row is read once.  Three
+// radix passes take 12, 12 and 8 bits; the first digit (sign, exponent, three
+// mantissa bits) spreads float scores over many bins of one shared 4096-bin LDS
+// histogram, which keeps atomic contention low.
+
+constexpr int kHistBins = 4096;
+
+// Among the bins of this pass (histogram `hist`, nb bins), find the digit holding
+// the remaining-th largest matching key: pick[0] = digit, pick[1] = number of
+// matching keys with a larger digit.  Thread t owns bins nb-1-c*t ... nb-c*t-c.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int remaining, int* pick, int* scan_sh) {
+  const int tid = threadIdx.x;
+  const int c = nb / kSelThreads > 0 ? nb / kSelThreads : 1;
+  const bool owner = tid * c < nb;
+  int cnt[4] = {0, 0, 0, 0};
+  int tot_t = 0;
+  if (owner) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < c) {
+        cnt[i] = (int)hist[nb - 1 - c * tid - i];
+        tot_t += cnt[i];
+      }
+  }
+  int total;
+  int run = block_exclusive_scan(tot_t, &total, scan_sh);
+  if (owner) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < c) {
+        if (run < remaining && run + cnt[i] >= remaining) {
+          pick[0] = nb - 1 - c * tid - i;
+          pick[1] = run;
+        }
+        run += cnt[i];
+      }
+  }
+  __syncthreads();
+}
+
+template <int V>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __restrict__ scores, int Hkv,
+                                                                 int64_t stride, const int32_t* __restrict__ seq_lens,
+                                                                 int t_q, int n_sink, int n_recent, int k,
+                                                                 int32_t* __restrict__ sel) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ int scan_sh[kSelWaves + 1];
+  __shared__ int pick[2];
+  const int row = blockIdx.x;
+  const int b = row / Hkv;
+  const int tid = threadIdx.x;
+  const float* srow = scores + (int64_t)row * stride;
+  int32_t* out = sel + (int64_t)row * k;
+
+  const int L = max(seq_lens[b], 0);
+  int lo, hi;
+  candidate_bounds(L, t_q, n_sink, n_recent, &lo, &hi);
+  if ((int64_t)hi > stride) hi = (int)stride;
+  if (lo > hi) lo = hi;
+  const int n = hi - lo;
+  const int k_eff = min(k, n);
+  if (k_eff == n || k_eff == 0) {
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < n ? lo + i : -1;
+    return;
+  }
+
+  const int j0 = lo + tid * V;
+  const int nv = clampi(hi - j0, 0, V);   // this thread's candidates
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = v < nv ? order_key(srow[j0 + v]) : 0u;
+
+  constexpr int kShift[3] = {20, 8, 0};
+  constexpr int kBits[3] = {12, 12, 8};
+  uint32_t prefix = 0u, mask = 0u;
+  int remaining = k_eff;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass], nb = 1 << kBits[pass];
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (v < nv && (key[v] & mask) == prefix) atomicAdd(&hist[(key[v] >> shift) & dmask], 1u);
+    __syncthreads();
+    find_digit(hist, nb, remaining, pick, scan_sh);
+    remaining -= pick[1];
+    prefix |= (uint32_t)pick[0] << shift;
+    mask |= dmask << shift;
+    __syncthreads();
+  }
+
+  // Ordered collection: keys > prefix, and the first `remaining` keys == prefix.
+  const uint32_t T = prefix;
+  int ne = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) ne += (v < nv && key[v] == T) ? 1 : 0;
+  int tot_eq;
+  int eqi = block_exclusive_scan(ne, &tot_eq, scan_sh);
+  int ns = 0;
+  uint64_t take = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    bool t = false;
+    if (v < nv) {
+      if (key[v] > T) {
+        t = true;
+      } else if (key[v] == T) {
+        t = eqi < remaining;
+        ++eqi;
+      }
+    }
+    if (t) {
+      take |= 1ull << v;
+      ++ns;
+    }
+  }
+  int tot_sel;
+  int pos = block_exclusive_scan(ns, &tot_sel, scan_sh);
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (((take >> v) & 1ull) && pos < k) out[pos++] = j0 + v;
+  for (int i = k_eff + tid; i < k; i += kSelThreads) out[i] = -1;
+}
+
 hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, const int32_t* seq_lens,
                          int t_q, int n_sink, int n_recent, int k, int32_t* sel, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3(B * Hkv), dim3(kSelThreads), 0, stream, scores, Hkv, stride,
-                     seq_lens, t_q, n_sink, n_recent, k, sel);
+  // The widest candidate row any request can have decides the variant.
+  const int64_t span = stride - n_sink;
+  const dim3 grid(B * Hkv), block(kSelThreads);
+  if (span <= 16 * kSelThreads)
+    hipLaunchKernelGGL((select_reg_kernel<16>), grid, block, 0, stream, scores, Hkv, stride, seq_lens, t_q, n_sink,
+                       n_recent, k, sel);
+  else if (span <= 32 * kSelThreads)
+    hipLaunchKernelGGL((select_reg_kernel<32>), grid, block, 0, stream, scores, Hkv, stride, seq_lens, t_q, n_sink,
+                       n_recent, k, sel);
+  else if (span <= 64 * kSelThreads)
+    hipLaunchKernelGGL((select_reg_kernel<64>), grid, block, 0, stream, scores, Hkv, stride, seq_lens, t_q, n_sink,
+                       n_recent, k, sel);
+  else
+    hipLaunchKernelGGL(select_kernel, grid, block, 0, stream, scores, Hkv, stride, seq_lens, t_q, n_sink, n_recent,
+                       k, sel);
   return hipGetLastError();
 }
 

@@ -127,3 +127,12 @@ def test_refresh_64k_select_and_pack_match_oracle_on_sampled_rows(gpu_lib):
         rk, _, _ = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], 65536, c.n_sink,
                                   np.repeat(ref[None], c.Hkv, 0), cap)
         assert np.array_equal(gk[b, g], rk[g])
+
+
+@pytest.mark.parametrize("k", [7, 5000])
+def test_selector_rows_beyond_the_register_variant(gpu_lib, k):
+    """Rows longer than 65536 candidates (the verification statistics at 128K) take the streaming kernel."""
+    rng = np.random.default_rng(200 + k)
+    B, H, stride = 1, 2, 131072
+    sc = (np.round(rng.standard_normal((B, H, stride)) * 16) / 16).astype(np.float32)
+    _select_both(gpu_lib, sc, [131072], k, n_sink=4, n_recent=256, t_q=8)
