@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "LIB_PATH", "SfiError", "load", "dense_attn_with_stats", "select_topk", "pack_compact",
+    "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats", "select_topk", "pack_compact",
     "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
 ]
@@ -95,11 +95,53 @@ def load() -> ctypes.CDLL:
     return _lib
 
 
+_binding: Optional[dict] = None
+_HOST_ONLY = ("_workspace_size", "sfi_plan_splits")
+
+
 def _call(name: str, *args) -> None:
     lib = load()
+    if _binding is not None and not name.endswith(_HOST_ONLY):
+        _binding["calls"].append((name, args))   # bind(): record the launch instead of making it
+        return
     st = getattr(lib, name)(*args)
     if st != SFI_OK:
         raise SfiError(st, name, lib.sfi_last_error().decode())
+
+
+class BoundCall:
+    """One library launch with its arguments marshalled once (see bind()).  ``outputs``
+    is what the entry point returned; the object keeps every buffer it allocated alive."""
+
+    def __init__(self, name: str, args: tuple, outputs, keep: list):
+        self.name = name
+        self.outputs = outputs
+        self._fn = getattr(load(), name)
+        self._args = args
+        self._keep = keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != SFI_OK:
+            raise SfiError(st, self.name, load().sfi_last_error().decode())
+
+
+def bind(op, *args, **kwargs) -> BoundCall:
+    """Marshal one entry-point call (e.g. ``bind(sparse_decode_attn, q, ...)``) without making
+    it.  Calling the result makes that launch on the same tensors and stream with only the C
+    call's own cost on the host; host-side size queries run once, here.  Tensors passed in
+    must outlive the bound call; buffers the entry point allocates are kept by it."""
+    global _binding
+    _binding = {"calls": [], "keep": []}
+    try:
+        outputs = op(*args, **kwargs)
+        rec = _binding
+    finally:
+        _binding = None
+    if len(rec["calls"]) != 1:
+        raise ValueError(f"{getattr(op, '__name__', op)} does not make exactly one launch")
+    name, cargs = rec["calls"][0]
+    return BoundCall(name, cargs, outputs, rec["keep"])
 
 
 # --------------------------------------------------------------------------- marshalling helpers
@@ -158,7 +200,10 @@ def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Option
     if nbytes == 0:
         return None
     # Zero-filled: the split-K arrival counters at its start must read zero on first use.
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    if _binding is not None:
+        _binding["keep"].append(ws)
+    return ws
 
 
 def _nbytes(t: Optional[torch.Tensor]) -> int:

@@ -101,21 +101,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   const int t0 = split * a.split_tokens;
   const int t1 = min(n_tot, t0 + a.split_tokens);
 
-  // Stage the block-table entries of this split's paged positions in LDS.
-  const int v_first = max(t0, n_c);
-  int pg_lo = 0, n_pg = 0;
-  if (t1 > v_first) {
-    pg_lo = (rs + v_first - n_c) >> 4;
-    n_pg = ((rs + t1 - 1 - n_c) >> 4) - pg_lo + 1;
-  }
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  for (int i = tid; i < n_pg; i += NT) {
-    const int e = bt_row[pg_lo + i];
-    bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
-  }
-  __syncthreads();
-
-  // This lane's slice of the G query vectors.
+  // This lane's slice of the G query vectors (requested before the block-table
+  // staging below, so the two loads share one memory round trip).
   const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)q_row0 * a.Hq + g * G) * D;
   u32x4 q[G][C];
 #pragma unroll
@@ -123,6 +110,27 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
 #pragma unroll
     for (int c = 0; c < C; ++c)
       q[h][c] = *reinterpret_cast<const u32x4*>(qb + h * D + (c * LPR + sub) * EPC);
+
+  // Stage the block-table entries of this split's paged positions in LDS.  A dense
+  // split stages every page of its token range that the table holds, without
+  // waiting for the request's length (entries past the end are never used).
+  int pg_lo = 0, n_pg = 0;
+  if constexpr (SPARSE) {
+    const int v_first = max(t0, n_c);
+    if (t1 > v_first) {
+      pg_lo = (rs + v_first - n_c) >> 4;
+      n_pg = ((rs + t1 - 1 - n_c) >> 4) - pg_lo + 1;
+    }
+  } else {
+    pg_lo = t0 >> 4;
+    n_pg = max(0, min(((t0 + a.split_tokens - 1) >> 4) - pg_lo + 1, a.max_pages - pg_lo));
+  }
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  for (int i = tid; i < n_pg; i += NT) {
+    const int e = bt_row[pg_lo + i];
+    bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
+  }
+  __syncthreads();
 
   const T* kpool = reinterpret_cast<const T*>(a.k_pool);
   const T* vpool = reinterpret_cast<const T*>(a.v_pool);
@@ -369,8 +377,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       const int64_t prow = orow * a.part_stride + split;
       store_coherent(a.part_o + prow * D + e, os);
       if (e == 0) {
-        store_coherent(a.part_ml + prow * 2, M);
-        store_coherent(a.part_ml + prow * 2 + 1, ls);
+        store_coherent2(a.part_ml + prow * 2, M, ls);
       }
     }
   }

@@ -8,12 +8,14 @@
 //
 // One 1024-thread work-group per (request, KV head) row.  Scores become
 // order-preserving uint32 keys (-0.0 folded onto +0.0, so the key order is the
-// IEEE order).  Four 8-bit radix passes, most significant digit first, narrow
-// the key T of the k_eff-th largest element, each pass a per-wave LDS histogram
-// of the keys that still match the digits found so far (integer counts:
-// order-independent).  A final ordered pass takes every key > T and the
-// lowest-positioned keys == T, writing positions through two block-wide
-// exclusive scans, so the output is ascending and identical on every run.
+// IEEE order).  Radix passes, most significant digit first, narrow the key T of
+// the k_eff-th largest element, each pass an LDS histogram of the keys that
+// still match the digits found so far (integer counts: order-independent).  A
+// final ordered pass takes every key > T and the lowest-positioned keys == T,
+// writing positions in ascending order through block-wide exclusive scans, so
+// the output is identical on every run.  Rows of up to 65536 candidates keep
+// their keys in registers (three passes of 12, 12 and 8 bits, one scan in the
+// collection); longer rows stream from memory (four 8-bit passes).
 #include "common.h"
 #include "kernels.h"
 
@@ -171,10 +173,47 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 
 constexpr int kHistBins = 4096;
 
+// Exclusive prefix sums of two values per thread over the work-group, in thread
+// order (one set of barriers for both); *total receives the sums.  sh needs
+// kSelWaves + 1 entries.
+__device__ __forceinline__ int2 block_exclusive_scan2(int x, int y, int2* total, int2* sh) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int ux = __shfl_up(ix, off), uy = __shfl_up(iy, off);
+    if (lane >= off) {
+      ix += ux;
+      iy += uy;
+    }
+  }
+  if (lane == kWave - 1) sh[w] = make_int2(ix, iy);
+  __syncthreads();
+  if (w == 0) {
+    const int2 v = lane < kSelWaves ? sh[lane] : make_int2(0, 0);
+    int vx = v.x, vy = v.y;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int ux = __shfl_up(vx, off), uy = __shfl_up(vy, off);
+      if (lane >= off) {
+        vx += ux;
+        vy += uy;
+      }
+    }
+    if (lane < kSelWaves) sh[lane] = make_int2(vx - v.x, vy - v.y);
+    if (lane == kSelWaves - 1) sh[kSelWaves] = make_int2(vx, vy);
+  }
+  __syncthreads();
+  const int2 base = sh[w];
+  *total = sh[kSelWaves];
+  return make_int2(base.x + ix - x, base.y + iy - y);
+}
+
 // Among the bins of this pass (histogram `hist`, nb bins), find the digit holding
 // the remaining-th largest matching key: pick[0] = digit, pick[1] = number of
-// matching keys with a larger digit.  Thread t owns bins nb-1-c*t ... nb-c*t-c.
-__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int remaining, int* pick, int* scan_sh) {
+// matching keys with a larger digit.  Thread t owns bins nb-1-c*t ... nb-c*t-c;
+// it zeroes them once read, so the histogram is clear for the next pass.
+__device__ __forceinline__ void find_digit(uint32_t* hist, int nb, int remaining, int* pick, int* scan_sh) {
   const int tid = threadIdx.x;
   const int c = nb / kSelThreads > 0 ? nb / kSelThreads : 1;
   const bool owner = tid * c < nb;
@@ -185,6 +224,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int rem
     for (int i = 0; i < 4; ++i)
       if (i < c) {
         cnt[i] = (int)hist[nb - 1 - c * tid - i];
+        hist[nb - 1 - c * tid - i] = 0u;
         tot_t += cnt[i];
       }
   }
@@ -211,12 +251,15 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
                                                                  int32_t* __restrict__ sel) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ int scan_sh[kSelWaves + 1];
+  __shared__ int2 scan2_sh[kSelWaves + 1];
   __shared__ int pick[2];
   const int row = blockIdx.x;
   const int b = row / Hkv;
   const int tid = threadIdx.x;
   const float* srow = scores + (int64_t)row * stride;
   int32_t* out = sel + (int64_t)row * k;
+
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0u;
 
   const int L = max(seq_lens[b], 0);
   int lo, hi;
@@ -230,11 +273,25 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
     return;
   }
 
+  // Thread t holds candidates [lo + t V, lo + t V + V) as keys; padding never counts.
   const int j0 = lo + tid * V;
-  const int nv = clampi(hi - j0, 0, V);   // this thread's candidates
+  const int nv = clampi(hi - j0, 0, V);
   uint32_t key[V];
+  if ((lo & 3) == 0 && (stride & 3) == 0 && ((uintptr_t)scores & 15u) == 0) {
+    // 16-byte loads: a group of four starting below hi ends below stride.
 #pragma unroll
-  for (int v = 0; v < V; ++v) key[v] = v < nv ? order_key(srow[j0 + v]) : 0u;
+    for (int v = 0; v < V; v += 4) {
+      const float4 x = v < nv ? *reinterpret_cast<const float4*>(srow + j0 + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+      key[v] = order_key(x.x);
+      key[v + 1] = order_key(x.y);
+      key[v + 2] = order_key(x.z);
+      key[v + 3] = order_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) key[v] = v < nv ? order_key(srow[j0 + v]) : 0u;
+  }
+  __syncthreads();   // histogram cleared
 
   constexpr int kShift[3] = {20, 8, 0};
   constexpr int kBits[3] = {12, 12, 8};
@@ -244,8 +301,6 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = kShift[pass], nb = 1 << kBits[pass];
     const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int v = 0; v < V; ++v)
       if (v < nv && (key[v] & mask) == prefix) atomicAdd(&hist[(key[v] >> shift) & dmask], 1u);
@@ -254,39 +309,33 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
     remaining -= pick[1];
     prefix |= (uint32_t)pick[0] << shift;
     mask |= dmask << shift;
-    __syncthreads();
   }
 
-  // Ordered collection: keys > prefix, and the first `remaining` keys == prefix.
+  // Ordered collection: every key > T, and the first `remaining` keys == T in
+  // position order.  One two-value scan gives each thread the number of keys > T
+  // and == T held by lower threads, hence its first output slot.
   const uint32_t T = prefix;
-  int ne = 0;
-#pragma unroll
-  for (int v = 0; v < V; ++v) ne += (v < nv && key[v] == T) ? 1 : 0;
-  int tot_eq;
-  int eqi = block_exclusive_scan(ne, &tot_eq, scan_sh);
-  int ns = 0;
-  uint64_t take = 0;
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    bool t = false;
+    n_gt += (v < nv && key[v] > T) ? 1 : 0;
+    n_eq += (v < nv && key[v] == T) ? 1 : 0;
+  }
+  int2 tot;
+  const int2 ex = block_exclusive_scan2(n_gt, n_eq, &tot, scan2_sh);
+  int eqi = ex.y;
+  int pos = ex.x + min(ex.y, remaining);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
     if (v < nv) {
-      if (key[v] > T) {
-        t = true;
-      } else if (key[v] == T) {
+      bool t = key[v] > T;
+      if (key[v] == T) {
         t = eqi < remaining;
         ++eqi;
       }
-    }
-    if (t) {
-      take |= 1ull << v;
-      ++ns;
+      if (t && pos < k) out[pos++] = j0 + v;
     }
   }
-  int tot_sel;
-  int pos = block_exclusive_scan(ns, &tot_sel, scan_sh);
-#pragma unroll
-  for (int v = 0; v < V; ++v)
-    if (((take >> v) & 1ull) && pos < k) out[pos++] = j0 + v;
   for (int i = k_eff + tid; i < k; i += kSelThreads) out[i] = -1;
 }
 

@@ -101,11 +101,14 @@ struct Split {
   int n;
 };
 
-Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits) {
-  constexpr int64_t kMinSplit = 256;
+constexpr int64_t kMinSplitDense = 512;
+constexpr int64_t kMinSplitSparse = 256;
+
+Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits,
+                 int64_t min_split = kMinSplitDense) {
   constexpr int64_t kTargetWGs = 1024;
   if (n_tok <= 0) return {tile, 1};
-  const int64_t by_min = (n_tok + kMinSplit - 1) / kMinSplit;
+  const int64_t by_min = (n_tok + min_split - 1) / min_split;
   const int64_t want = (kTargetWGs + units - 1) / units;
   int64_t ns = by_min < want ? by_min : want;
   if (ns > max_splits) ns = max_splits;
@@ -136,7 +139,8 @@ Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
 
 Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile);
+  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile, sfi::kMaxSplits,
+                    kMinSplitSparse);
 }
 
 sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_t* seq_lens) {
@@ -153,6 +157,18 @@ sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_
   a.scale = s->scale;
   a.scale_log2 = s->scale * sfi::kLog2e;
   return a;
+}
+
+// The merge of a unit's partials addresses them with 32-bit byte offsets from its
+// first row: rows (t, h) of one unit lie (t_q - 1) * Hq + G rows apart at most.
+sfi_status check_unit_span(const sfi_shape* s, int t_q_max, int n_split) {
+  if (n_split <= 1) return SFI_OK;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int64_t span = ((int64_t)(t_q_max - 1) * s->num_q_heads + G) * n_split * s->head_dim * 4;
+  if (span > INT32_MAX)
+    return fail(SFI_ERR_UNSUPPORTED, "split partials of one (request, KV head) span %lld bytes (limit %d)",
+                (long long)span, INT32_MAX);
+  return SFI_OK;
 }
 
 void set_partials(sfi::AttnArgs& a, void* ws, int64_t rows, int d) {
@@ -204,7 +220,7 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
   }
   const int64_t units = (int64_t)B * shape->num_kv_heads;
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile);
+  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile, sfi::kMaxSplits, kMinSplitSparse);
   const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
   sfi::MixedPlan& p = ms->plan;
   p = sfi::MixedPlan{};
@@ -231,6 +247,9 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
     }
   p.n_entries = e;
   p.wg_begin[e] = wg;
+  int tq_max = 1;
+  for (int b = 0; b < B; ++b) tq_max = t_q[b] > tq_max ? t_q[b] : tq_max;
+  SFI_TRY(check_unit_span(shape, tq_max, stride));
   ms->part_stride = stride;
   ms->rows = rows;
   return SFI_OK;
@@ -281,6 +300,7 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
     return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
   const Split sp = plan_dense(shape, kv, t_q);
   const int64_t rows = (int64_t)shape->batch * t_q * shape->num_q_heads;
+  SFI_TRY(check_unit_span(shape, t_q, sp.n));
   SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
 
   sfi::AttnArgs a = base_args(shape, kv, seq_lens);
@@ -379,6 +399,7 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
     return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
   const Split sp = plan_sparse(shape, cap, n_recent, kv);
   const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
+  SFI_TRY(check_unit_span(shape, 1, sp.n));
   SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
 
   sfi::AttnArgs a = base_args(shape, kv, seq_lens);

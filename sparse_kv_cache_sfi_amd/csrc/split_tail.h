@@ -17,6 +17,22 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A split's (m, l) pair as one 8-byte access (p is 8-byte aligned).
+__device__ __forceinline__ void store_coherent2(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Buffer-resource word 3 for raw (unswizzled, untyped) buffers on CDNA, and the
+// cache-policy bit (sc1) that makes a buffer load coherent at device scope, as an
+// agent-scope atomic load is.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCoherentLoad = 16;
 
 // Wave-wide reductions (all 64 lanes receive the result).
 __device__ __forceinline__ float wave_max(float x) {
@@ -36,7 +52,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D>
 struct SplitTail {
   static constexpr int NT = 256;
-  static constexpr int BATCH = 32;
+  static constexpr int PRE = 16;   // float4 partial loads in flight per lane
 
   __host__ __device__ static constexpr int bytes(int R, int ns_max) { return (2 * R * ns_max + 2 * R) * 4; }
 
@@ -47,14 +63,21 @@ struct SplitTail {
   // Called by every work-group of the unit after it has stored its partials.
   // The last one to arrive merges the n_split partials of each row (M = max m_s;
   // out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s; lse = (M + log2 of that sum) *
-  // ln 2; an empty split adds 0), in fixed split order, and returns the arrival
-  // counter to zero.  Every step is parallel: all (m, l) pairs are fetched at
-  // once, per-row max and sum are wave reductions, and each output element keeps
-  // up to BATCH partial loads in flight.  tail: LDS of bytes(R, ns_max).
+  // ln 2; an empty split adds 0) and returns the arrival counter to zero.
+  //
+  // The merge sits on the critical path of every call and is run by one
+  // work-group, so it is built for few instructions and one memory round trip:
+  // outputs are handled as float4 groups, P consecutive lanes share a group and
+  // take splits p, p + P, ... (16-byte device-coherent loads), the first PRE
+  // loads of every lane are in flight together with all (m, l) pairs before
+  // anything waits, per-row max and sum are wave reductions, and the P lane sums
+  // are combined by a fixed xor tree.  Every sum has a fixed order, so the result
+  // does not depend on which work-group merges.  tail: LDS of bytes(R, ns_max).
   __device__ static void run(const AttnArgs& a, int b, int g, int q_row0, int G, int R, int ns_max, int* flag,
                              float* tail) {
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     constexpr int WAVES = NT / kWave;
+    constexpr int D4 = D / 4;
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (tid == 0) {
@@ -69,11 +92,37 @@ struct SplitTail {
     float* l_s = tail + R * ns_max;   // [R][ns_max]
     float* M_r = tail + 2 * R * ns_max;
     float* L_r = M_r + R;
+
+    // Lanes per float4 group: a power of two, at most a wave, filling the work-group.
+    const int n_grp = R * D4;
+    int P = 1;
+    while (P < kWave && 2 * P * n_grp <= NT) P *= 2;
+    const int grp0 = tid / P, p = tid % P;
+    // The unit's partial rows as one buffer resource (its base is uniform over the
+    // work-group); loads outside it return zero.
+    const int64_t row0 = row(a, q_row0, g, G, 0);
+    const int64_t row_span = row(a, q_row0, g, G, R - 1) - row0 + 1;
+    const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_o + row0 * a.part_stride * D, (short)0, (int)(row_span * a.part_stride * D * 4), kBufferRsrcWord3);
+    auto offset = [&](int grp, int s) {
+      const int r = grp / D4;
+      return (int)(((row(a, q_row0, g, G, r) - row0) * a.part_stride + s) * (D * 4) + (grp % D4) * 16);
+    };
+    auto load4 = [&](int off) { return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(part, off, 0, kCoherentLoad)); };
+
+    float4 first[PRE];
+    if (grp0 < n_grp) {
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) {
+        const int sj = p + P * j;
+        first[j] = sj < ns ? load4(offset(grp0, sj)) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
     for (int i = tid; i < R * ns; i += NT) {
       const int r = i / ns, s = i % ns;
-      const float* ml = a.part_ml + (row(a, q_row0, g, G, r) * a.part_stride + s) * 2;
-      w_s[r * ns_max + s] = load_coherent(ml);
-      l_s[r * ns_max + s] = load_coherent(ml + 1);
+      const float2 ml = load_coherent2(a.part_ml + (row(a, q_row0, g, G, r) * a.part_stride + s) * 2);
+      w_s[r * ns_max + s] = ml.x;
+      l_s[r * ns_max + s] = ml.y;
     }
     __syncthreads();
     for (int r = w; r < R; r += WAVES) {
@@ -94,23 +143,48 @@ struct SplitTail {
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < R * D; idx += NT) {
-      const int r = idx / D, e = idx % D;
-      const int64_t orow = row(a, q_row0, g, G, r);
-      const float* po = a.part_o + orow * a.part_stride * D + e;
+    for (int grp = grp0; grp < n_grp; grp += NT / P) {
+      const int r = grp / D4;
       const float* wr = w_s + r * ns_max;
-      float os = 0.f;
-      for (int s0 = 0; s0 < ns; s0 += BATCH) {
-        float v[BATCH];
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      auto add = [&](float wt, const float4& v) {
+        acc.x = fmaf(wt, v.x, acc.x);
+        acc.y = fmaf(wt, v.y, acc.y);
+        acc.z = fmaf(wt, v.z, acc.z);
+        acc.w = fmaf(wt, v.w, acc.w);
+      };
+      int j0 = 0;
+      if (grp == grp0) {
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) v[j] = (s0 + j < ns) ? load_coherent(po + (int64_t)(s0 + j) * D) : 0.f;
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j)
-          if (s0 + j < ns) os = fmaf(wr[s0 + j], v[j], os);
+        for (int j = 0; j < PRE; ++j)
+          if (p + P * j < ns) add(wr[p + P * j], first[j]);
+        j0 = PRE;
       }
-      const float ls = L_r[r];
-      a.out[orow * D + e] = ls > 0.f ? os / ls : 0.f;
-      if (e == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M_r[r] + log2f(ls)) * kLn2 : neg_inf();
+      for (; p + P * j0 < ns; j0 += PRE) {
+        float4 v[PRE];
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) {
+          const int sj = p + P * (j0 + j);
+          v[j] = sj < ns ? load4(offset(grp, sj)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < PRE; ++j)
+          if (p + P * (j0 + j) < ns) add(wr[p + P * (j0 + j)], v[j]);
+      }
+      for (int off = 1; off < P; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
+      }
+      if (p == 0) {
+        const int64_t orow = row(a, q_row0, g, G, r);
+        const int e4 = grp % D4;
+        const float ls = L_r[r];
+        *reinterpret_cast<float4*>(a.out + orow * D + e4 * 4) =
+            ls > 0.f ? make_float4(acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e4 == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M_r[r] + log2f(ls)) * kLn2 : neg_inf();
+      }
     }
     if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

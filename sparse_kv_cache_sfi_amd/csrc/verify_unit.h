@@ -302,8 +302,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     } else {
       store_coherent(a.part_o + (orow * a.part_stride + split) * D + e, os);
       if (e == 0) {
-        store_coherent(a.part_ml + (orow * a.part_stride + split) * 2, M);
-        store_coherent(a.part_ml + (orow * a.part_stride + split) * 2 + 1, ls);
+        store_coherent2(a.part_ml + (orow * a.part_stride + split) * 2, M, ls);
       }
     }
   }

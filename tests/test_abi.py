@@ -168,9 +168,9 @@ def test_split_plan_covers_every_token(B, Hkv, n_tok):
 
 
 def test_split_plan_of_the_16k_decode_layer():
-    # 1 request x 8 KV heads x 16384 tokens: 64 splits of 256 tokens -> 512 work-groups.
+    # 1 request x 8 KV heads x 16384 tokens: 32 splits of 512 tokens -> 256 work-groups.
     assert sfi.plan_splits(0, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
-                           max_seq_len=16384) == (256, 64)
+                           max_seq_len=16384) == (512, 32)
     # fast step, 1.6 % retention: 192 compact slots + 64 recent -> a single split
     assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=192, n_recent=64) == (256, 1)

@@ -84,6 +84,35 @@ def test_dense_without_scores_and_determinism(gpu_lib):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_bound_calls_repeat_the_direct_calls(gpu_lib):
+    """bind() marshals a call once; replaying it gives bit-identical results to the direct call."""
+    c = make_case(112, name="bind", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[3000, 1200], n_sink=4,
+                  n_recent=64, k_sel=200)
+    dc = DevCase(c)
+    o1, l1, s1 = gpu_lib.dense_attn_with_stats(dc.q[:, :1].contiguous(), dc.k, dc.v, dc.bt, dc.lens,
+                                               max_seq_len=dc.max_seq_len, n_sink=4, n_recent=64)
+    sel1 = gpu_lib.select_topk(s1, dc.lens, k=200, n_sink=4, n_recent=64)
+    o2, l2, s2 = torch.empty_like(o1), torch.empty_like(l1), torch.empty_like(s1)
+    sel2 = torch.empty_like(sel1)
+    ws = torch.zeros(gpu_lib.workspace_size("dense", k_pool=dc.k, block_table=dc.bt, Hq=16, dtype=torch.bfloat16,
+                                            max_seq_len=dc.max_seq_len), dtype=torch.uint8, device=DEV)
+    dense = gpu_lib.bind(gpu_lib.dense_attn_with_stats, dc.q[:, :1].contiguous(), dc.k, dc.v, dc.bt, dc.lens,
+                         max_seq_len=dc.max_seq_len, n_sink=4, n_recent=64, out=o2, lse=l2, scores=s2, workspace=ws)
+    select = gpu_lib.bind(gpu_lib.select_topk, s2, dc.lens, k=200, n_sink=4, n_recent=64, sel_idx=sel2)
+    for _ in range(2):
+        dense()
+        select()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(s1, s2) and torch.equal(sel1, sel2)
+    # Buffers the entry point allocates itself (outputs, workspace) stay with the bound call.
+    auto = gpu_lib.bind(gpu_lib.dense_attn_with_stats, dc.q[:, :1].contiguous(), dc.k, dc.v, dc.bt, dc.lens,
+                        max_seq_len=dc.max_seq_len, n_sink=4, n_recent=64)
+    auto()
+    torch.cuda.synchronize()
+    o3, l3, s3 = auto.outputs
+    assert torch.equal(o1, o3) and torch.equal(l1, l3) and torch.equal(s1, s3)
+
+
 def test_dense_is_invariant_to_physical_page_order(gpu_lib):
     c = make_case(111, name="i", B=1, Hq=8, Hkv=4, d=128, dtype="bf16", seq_lens=[1800], n_sink=4,
                   n_recent=32, k_sel=64, spare_pages=7)

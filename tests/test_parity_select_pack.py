@@ -32,8 +32,9 @@ def _select_both(sfi, scores_np, lens, k, n_sink, n_recent, t_q=1):
     return got
 
 
+@pytest.mark.parametrize("n_sink", [3, 4], ids=["unaligned_rows", "aligned_rows"])
 @pytest.mark.parametrize("k", [1, 2, 7, 64, 500, 999, 1000, 1001, 5000])
-def test_selector_crafted_ties(gpu_lib, k):
+def test_selector_crafted_ties(gpu_lib, k, n_sink):
     rng = np.random.default_rng(k)
     B, H, stride = 3, 4, 1100
     vals = np.array([-np.inf, -3.0, -1.5, -0.0, 0.0, 0.25, 1.0, 2.0, 1e30, np.inf], dtype=np.float32)
@@ -42,7 +43,7 @@ def test_selector_crafted_ties(gpu_lib, k):
     sc[2, 0, :] = -0.0                      # signed zeros only
     sc[2, 1, 500:] = 0.0
     lens = [1100, 900, 37]
-    _select_both(gpu_lib, sc, lens, k, n_sink=3, n_recent=5)
+    _select_both(gpu_lib, sc, lens, k, n_sink=n_sink, n_recent=5)
 
 
 @pytest.mark.parametrize("k", [1, 33, 2048, 20000])
