@@ -29,6 +29,8 @@
 namespace sfi {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+#define LDS_AS __attribute__((address_space(3)))
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
@@ -47,19 +49,15 @@ struct VerifyShape {
   static constexpr int TILES_LDS = WAVES * WAVE_LDS > MERGE ? WAVES * WAVE_LDS : MERGE;
   static constexpr int TAIL = SplitTail<D>::bytes(32, kMaxVerifySplits);
   static constexpr int BIG = TILES_LDS > TAIL ? TILES_LDS : TAIL;
-  static constexpr int SMEM = kBtSlots * 4 + 16 + BIG;
+  // The tiles start on a 128-byte boundary: 16-byte LDS accesses must be 16-byte
+  // aligned to run at full rate.
+  static constexpr int BIG_OFF = (kBtSlots * 4 + 16 + 127) / 128 * 128;
+  static constexpr int SMEM = BIG_OFF + BIG;
   static_assert(LOADS >= 1, "tile too small");
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-// Sum over the 32 lanes of each half-wave (rows of the S^T tile).
-__device__ __forceinline__ float half_sum(float x) {
-  x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  return x;
 }
 
 template <int D, bool SCORES>
@@ -74,7 +72,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
 
   int* bt_s = reinterpret_cast<int*>(smem);
   int* flag = bt_s + kBtSlots;
-  char* big = smem + kBtSlots * 4 + 16;
+  char* big = smem + S::BIG_OFF;
   char* kt = big + w * S::WAVE_LDS;   // this wave's K tile, then its V tile
   char* vt = kt + TILE * LDS_ROW;
 
@@ -184,16 +182,29 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     }
 
     if constexpr (SCORES) {
-      // Masked logits summed over all R rows (rows past R hold zero queries).
+      // Masked logits summed over all R rows (rows past R hold zero queries): a
+      // transposing butterfly over the 32 lanes of each half-wave halves the values a
+      // lane holds at every step, so lane n ends with the total of its register n / 2.
+      float v16[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float tot = half_sum(sacc[i]);
-        const int tok = 8 * (i / 4) + 4 * hb + (i % 4);
-        const int pos = tb + tok;
-        if (n == 0 && pos < t1) {
-          const bool ok = (okmask >> tok) & 1ull;
-          srow[pos] = (ok && pos >= clo && pos < chi) ? tot * a.scale : neg_inf();
+      for (int i = 0; i < 16; ++i) v16[i] = sacc[i];
+#pragma unroll
+      for (int w2 = 8; w2 >= 1; w2 >>= 1) {
+        const bool up = (n & (2 * w2)) != 0;   // this lane keeps the upper half of its values
+#pragma unroll
+        for (int i = 0; i < w2; ++i) {
+          const float keep = up ? v16[i + w2] : v16[i];
+          const float send = up ? v16[i] : v16[i + w2];
+          v16[i] = keep + __shfl_xor(send, 2 * w2);
         }
+      }
+      const float tot = v16[0] + __shfl_xor(v16[0], 1);
+      const int ri = n >> 1;
+      const int tok = 8 * (ri / 4) + 4 * hb + (ri % 4);
+      const int pos = tb + tok;
+      if ((n & 1) == 0 && pos < t1) {
+        const bool ok = (okmask >> tok) & 1ull;
+        srow[pos] = (ok && pos >= clo && pos < chi) ? tot * a.scale : neg_inf();
       }
     }
 
@@ -239,22 +250,21 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
       phi[s] = (u32x4){hw[0], hw[1], hw[2], hw[3]};
       plo[s] = (u32x4){lw[0], lw[1], lw[2], lw[3]};
     }
-    // O^T += V^T P^T: lane (dim 32 db + n, hb) gathers V at tokens 16 s + 8 (j / 4) + 4 hb + j % 4.
-    const uint16_t* vtu = reinterpret_cast<const uint16_t*>(vt);
+    // O^T += V^T P^T.  Lane (dim 32 db + n, hb) needs V at tokens 16 s + 8 h + 4 hb + 0..3
+    // for h = 0, 1: two transposing LDS reads, each filled by the 16-lane group the lane
+    // sits in (lane i of a group receives element i % 4 of the row that lane
+    // 4 j + i / 4 points at, for j = 0..3), so group lane s points at token
+    // 16 s + 8 h + 4 hb + s / 4, dims 32 db + 16 (group & 1) + 4 (s % 4) + 0..3.
+    const int tgrp = lane >> 4, tl = lane & 15;
+    const char* vbase = vt + (4 * hb + (tl >> 2)) * LDS_ROW + (16 * (tgrp & 1) + 4 * (tl & 3)) * 2;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        uint32_t va[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t_a = 16 * s + 8 * ((2 * j) / 4) + 4 * hb + (2 * j) % 4;
-          const int t_b = 16 * s + 8 * ((2 * j + 1) / 4) + 4 * hb + (2 * j + 1) % 4;
-          const uint32_t lo = vtu[(t_a * LDS_ROW) / 2 + 32 * db + n];
-          const uint32_t hi = vtu[(t_b * LDS_ROW) / 2 + 32 * db + n];
-          va[j] = lo | (hi << 16);
-        }
-        const bf16x8 vA = __builtin_bit_cast(bf16x8, (u32x4){va[0], va[1], va[2], va[3]});
+        const char* p0 = vbase + 16 * s * LDS_ROW + 64 * db;
+        const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0));
+        const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 8 * LDS_ROW));
+        const bf16x8 vA = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, phi[s]), oacc[db], 0, 0, 0);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, plo[s]), oacc[db], 0, 0, 0);
       }
