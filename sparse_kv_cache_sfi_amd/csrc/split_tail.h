@@ -49,9 +49,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 // A unit (b, g) owns R = t_q * G output rows: row r = (t, h) with t = r / G,
 // h = r % G is head row (q_row0 + t) * Hq + g * G + h of out, lse and the partials
 // [.., part_stride, D] / [.., part_stride, 2].
-template <int D>
+template <int D, int NT = 256>
 struct SplitTail {
-  static constexpr int NT = 256;
   static constexpr int PRE = 16;   // float4 partial loads in flight per lane
 
   __host__ __device__ static constexpr int bytes(int R, int ns_max) { return (2 * R * ns_max + 2 * R) * 4; }
