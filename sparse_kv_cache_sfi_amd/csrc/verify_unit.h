@@ -154,7 +154,6 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     u32x4 kr[LOADS], vr[LOADS];
     load_tile(0, kr, vr);
     park_tile(kr, vr);
-    __syncthreads();
   }
   for (int it = 0; it < iters; ++it) {
     u32x4 kr[LOADS], vr[LOADS];
@@ -269,12 +268,11 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, plo[s]), oacc[db], 0, 0, 0);
       }
     }
-    __syncthreads();   // every wave is done reading its tiles
-    if (more) {
-      park_tile(kr, vr);
-      __syncthreads();
-    }
+    // A wave reads only its own tiles and its LDS accesses take effect in program
+    // order, so the refill needs no barrier and the waves stream independently.
+    if (more) park_tile(kr, vr);
   }
+  __syncthreads();   // every wave is done with its tiles before the merge reuses the area
 
   // Merge the waves through LDS (the tile area is free now).
   float* mo = reinterpret_cast<float*>(big);                // [WAVES][32][D]
