@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--aux-stream", action="store_true")
+    ap.add_argument("--specmix-only", action="store_true",
+                    help="run only the 128K draft/verify mix (for counter collection) and print its figures")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
     args = ap.parse_args()
@@ -136,6 +138,9 @@ def main():
 
     sfi.load()
     dev = torch.device("cuda:0")
+    if args.specmix_only:
+        print(json.dumps({"specmix_128k": specmix(sfi, dev)}), flush=True)
+        return
     L, B, Hq, Hkv, d = 16384, 1, 16, 8, 128
     n_sink, n_recent = 4, 64
     frac = (1, 8)
@@ -246,6 +251,9 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roof,
     }
+
+    result["hip_graph"] = graph_steps(sfi, layers, dev, args.steps, step_bytes, k_sel, cap, n_sink, n_recent,
+                                      max_len, ws_dense, ws_sparse)
 
     if not args.no_sweep:
         result["sweep"] = sweep(sfi, layers, dev, main_s, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense, ws_sparse)
@@ -436,6 +444,56 @@ def refresh_overlap(sfi, dev):
                        "hidden_fraction": round(max(0.0, min(1.0, (t_s - t_o) / moved)), 3)}
         res[f"partner_{kind}"] = r
     log(f"refresh overlap {res}")
+    return res
+
+
+def graph_steps(sfi, layers, dev, steps, step_bytes, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
+    """The same step captured once per replica in a HIP graph and replayed: the GPU time of the
+    step without host launch cost or launch gaps between its four kernels.  The first replay's
+    fast-step output is checked against the eager step's."""
+    import torch
+    R = len(layers)
+    side = torch.cuda.Stream(device=dev)
+
+    def run(ly):
+        sfi.dense_attn_with_stats(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
+                                  n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
+                                  scores=ly["scores"], workspace=ws_dense)
+        sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"])
+        sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
+                         max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"])
+        sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"], ly["cv"], ly["nc"],
+                               n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=ly["fout"],
+                               lse=ly["flse"], workspace=ws_sparse)
+
+    torch.cuda.synchronize()
+    eager = layers[0]["fout"].clone()
+    layers[0]["fout"].zero_()
+    graphs = []
+    side.wait_stream(torch.cuda.current_stream(dev))
+    for ly in layers:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            run(ly)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    matches = bool(torch.equal(layers[0]["fout"], eager))
+    for i in range(2 * R):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % R].replay()
+    t1.record()
+    t1.synchronize()
+    step_s = t0.elapsed_time(t1) * 1e-3 / steps
+    res = {"ms_per_step": round(step_s * 1e3, 5), "value": round(step_bytes / step_s / 1e9, 2),
+           "pct_hbm_peak": round(100 * step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 2),
+           "replay_matches_eager": matches}
+    log(f"graph step {res}")
     return res
 
 
