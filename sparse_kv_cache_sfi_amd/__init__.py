@@ -23,7 +23,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats", "select_topk", "pack_compact",
+    "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats", "dense_attn_with_refresh",
+    "select_topk", "pack_compact",
     "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
 ]
@@ -45,6 +46,12 @@ class SfiPagedKV(ctypes.Structure):
                 ("page_size", c_int32), ("num_pages", c_int32), ("max_seq_len", c_int32)]
 
 
+class SfiRefresh(ctypes.Structure):
+    _fields_ = [("kv", SfiPagedKV), ("scores", c_void_p), ("score_stride", c_int64), ("n_sink", c_int32),
+                ("n_recent", c_int32), ("k", c_int32), ("sel_idx", c_void_p), ("compact_k", c_void_p),
+                ("compact_v", c_void_p), ("cap", c_int32), ("n_compact", c_void_p)]
+
+
 class SfiError(RuntimeError):
     def __init__(self, status: int, call: str, message: str):
         super().__init__(f"{call} failed with status {status}: {message}")
@@ -56,6 +63,8 @@ _SIGS = {
     "sfi_dense_attn_with_stats": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                   c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
     "sfi_dense_attn_workspace_size": [_SHAPE_P, _KV_P, c_int32, POINTER(c_size_t)],
+    "sfi_dense_attn_with_refresh": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                    c_void_p, c_int64, POINTER(SfiRefresh), c_void_p, c_size_t, c_void_p],
     "sfi_select_topk": [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32, c_int32, c_int32, c_int32,
                         c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, POINTER(c_size_t)],
@@ -266,6 +275,63 @@ def dense_attn_with_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
           seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), _ptr(scores), stride, _ptr(ws),
           _nbytes(ws), _stream(stream, dev))
     return out, lse, scores
+
+
+def dense_attn_with_refresh(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
+                            n_sink: int = 0, n_recent: int = 0, scale: Optional[float] = None,
+                            with_scores: bool = True, score_stride: Optional[int] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            r_k_pool: torch.Tensor, r_v_pool: torch.Tensor, r_block_table: torch.Tensor,
+                            r_max_seq_len: int, r_scores: torch.Tensor, r_n_sink: int, r_n_recent: int, k: int,
+                            cap: int = 0, sel_idx: Optional[torch.Tensor] = None,
+                            compact_k: Optional[torch.Tensor] = None, compact_v: Optional[torch.Tensor] = None,
+                            n_compact: Optional[torch.Tensor] = None, pack: bool = True, stream=None):
+    """Slow step of one layer (q [B, 1, Hq, d], as dense_attn_with_stats) with the Selector (and,
+    with pack=True, the pack) of the previous layer (its pools r_*, its logits r_scores
+    [B, Hkv, stride]) riding in the same launch.
+    -> (out, lse, scores, sel_idx, compact_k, compact_v, n_compact); the last three are None
+    when pack is False."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    _dev(r_scores, "r_scores")
+    B, t_q, Hq, d = q.shape
+    if t_q != 1:
+        raise ValueError("the refresh launch takes one query token per request")
+    Hkv = k_pool.shape[1]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    rkv = _kv(r_k_pool, r_v_pool, r_block_table, r_max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+    if with_scores and scores is None:
+        stride = int(score_stride if score_stride is not None else max_seq_len)
+        scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
+    stride = scores.shape[-1] if scores is not None else 0
+    if sel_idx is None:
+        sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    if pack:
+        if compact_k is None:
+            compact_k = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
+        if compact_v is None:
+            compact_v = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
+        if n_compact is None:
+            n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        compact_k = compact_v = n_compact = None
+    ref = SfiRefresh(rkv, r_scores.data_ptr(), r_scores.shape[-1], r_n_sink, r_n_recent, k, sel_idx.data_ptr(),
+                     _ptr(compact_k), _ptr(compact_v), cap, _ptr(n_compact))
+    need = c_size_t(0)
+    _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_dense_attn_with_refresh", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
+          seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), _ptr(scores), stride,
+          ctypes.byref(ref), _ptr(ws), _nbytes(ws), _stream(stream, dev))
+    return out, lse, scores, sel_idx, compact_k, compact_v, n_compact
 
 
 def select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, *, k: int, n_sink: int, n_recent: int,

@@ -324,6 +324,87 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
   return hip_status(e, "attention launch");
 }
 
+sfi_status sfi_dense_attn_with_refresh(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                       const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
+                                       float* lse, float* scores, int64_t score_stride, const sfi_refresh* refresh,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  SFI_TRY(check_ptr16(q, "q"));
+  SFI_TRY(check_ptr16(out, "out"));
+  if (!seq_lens) return fail(SFI_ERR_INVALID_ARG, "seq_lens is NULL");
+  SFI_TRY(check_budgets(n_sink, n_recent));
+  if (scores && score_stride < kv->max_seq_len)
+    return fail(SFI_ERR_INVALID_ARG, "score_stride (%lld) must be >= max_seq_len (%d)", (long long)score_stride,
+                kv->max_seq_len);
+  if (!refresh) return fail(SFI_ERR_INVALID_ARG, "refresh is NULL");
+  SFI_TRY(check_kv(&refresh->kv));
+  if (!refresh->scores || !refresh->sel_idx)
+    return fail(SFI_ERR_INVALID_ARG, "refresh scores and sel_idx must be non-NULL");
+  if (refresh->scores == scores) return fail(SFI_ERR_INVALID_ARG, "refresh scores must not be the launch's own scores");
+  const bool pack = refresh->compact_k != nullptr;
+  if (pack) {
+    SFI_TRY(check_ptr16(refresh->compact_k, "refresh compact_k"));
+    SFI_TRY(check_ptr16(refresh->compact_v, "refresh compact_v"));
+    if (!refresh->n_compact) return fail(SFI_ERR_INVALID_ARG, "refresh n_compact must be non-NULL when packing");
+  }
+  SFI_TRY(check_budgets(refresh->n_sink, refresh->n_recent));
+  if (refresh->score_stride < refresh->kv.max_seq_len || refresh->score_stride > INT32_MAX)
+    return fail(SFI_ERR_INVALID_ARG, "refresh score_stride (%lld) must be in [kv.max_seq_len, 2^31)",
+                (long long)refresh->score_stride);
+  if (refresh->k < 1 || refresh->k > sfi::kMaxRiderK)
+    return fail(SFI_ERR_UNSUPPORTED, "refresh k must be in [1, %d] (got %d)", sfi::kMaxRiderK, refresh->k);
+  if (pack && (int64_t)refresh->cap < (int64_t)refresh->n_sink + refresh->k)
+    return fail(SFI_ERR_INVALID_ARG, "refresh cap (%d) must be >= n_sink + k (%lld)", refresh->cap,
+                (long long)refresh->n_sink + refresh->k);
+  if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
+    return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const Split sp = plan_dense(shape, kv, 1);
+  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
+  SFI_TRY(check_unit_span(shape, 1, sp.n));
+  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
+  if ((int64_t)shape->batch * shape->num_kv_heads * (1 + sp.n) > INT32_MAX)
+    return fail(SFI_ERR_UNSUPPORTED, "grid too large");
+
+  sfi::AttnArgs a = base_args(shape, kv, seq_lens);
+  a.q = q;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.split_tokens = sp.tokens;
+  a.n_split = sp.n;
+  a.t_q = 1;
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  set_partials(a, workspace, rows, shape->head_dim);
+
+  sfi::RefreshArgs r{};
+  r.scores = refresh->scores;
+  r.score_stride = refresh->score_stride;
+  r.k_pool = refresh->kv.k;
+  r.v_pool = refresh->kv.v;
+  r.block_table = refresh->kv.block_table;
+  r.max_pages = refresh->kv.max_pages;
+  r.num_pages = refresh->kv.num_pages;
+  r.max_seq_len = refresh->kv.max_seq_len;
+  r.Hkv = shape->num_kv_heads;
+  r.seq_lens = seq_lens;
+  r.n_sink = refresh->n_sink;
+  r.n_recent = refresh->n_recent;
+  r.k = refresh->k;
+  r.sel = refresh->sel_idx;
+  r.ck = pack ? refresh->compact_k : nullptr;
+  r.cv = pack ? refresh->compact_v : nullptr;
+  r.cap = refresh->cap;
+  r.n_compact = refresh->n_compact;
+  r.rows = shape->batch * shape->num_kv_heads;
+  const hipError_t e = sfi::launch_dense_refresh(a, r, shape->dtype, shape->head_dim, G, shape->batch,
+                                                 static_cast<hipStream_t>(stream));
+  return hip_status(e, "attention + refresh launch");
+}
+
 sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t k,
                                           size_t* bytes) {
   if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");

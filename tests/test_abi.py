@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
-              "sfi_mixed_attn"):
+              "sfi_mixed_attn", "sfi_dense_attn_with_refresh"):
         assert n in names
 
 
@@ -125,6 +125,30 @@ def test_pack_rejects_bad_arguments(lib):
     assert call(sel=0) == 1
     assert call(k=0) == 1
     assert call(n_sink=-1) == 1
+
+
+def test_refresh_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def call(refresh=True, scores=FAKE + 0x100, **kw):
+        r = dict(kv=_kv(), scores=FAKE, score_stride=16384, n_sink=4, n_recent=64, k=1980, sel_idx=FAKE,
+                 compact_k=FAKE, compact_v=FAKE, cap=1984, n_compact=FAKE)
+        r.update(kw)
+        ref = sfi.SfiRefresh(**r)
+        return lib.sfi_dense_attn_with_refresh(ctypes.byref(shape), ctypes.byref(kv), FAKE, FAKE, 4, 64, FAKE, FAKE,
+                                               scores, 16384, ctypes.byref(ref) if refresh else None, FAKE, 1 << 40,
+                                               None)
+    assert call(refresh=False) == 1 and "refresh is NULL" in lib.sfi_last_error().decode()
+    assert call(scores=FAKE) == 1 and "must not be" in lib.sfi_last_error().decode()
+    assert call(k=8193) == 2 and "8192" in lib.sfi_last_error().decode()
+    assert call(k=0) == 2
+    assert call(cap=100) == 1 and "cap" in lib.sfi_last_error().decode()
+    assert call(sel_idx=0) == 1
+    assert call(n_compact=0) == 1
+    assert call(compact_k=MISALIGNED) == 1
+    assert call(score_stride=100) == 1 and "score_stride" in lib.sfi_last_error().decode()
+    assert call(n_recent=-1) == 1
+    assert call(kv=_kv(page=8)) == 2
 
 
 def test_sparse_rejects_bad_arguments(lib):
