@@ -262,6 +262,8 @@ def main():
         big = make_layers(1, L, 16, frac, dev, 5000)
         result["sweep_b16"] = sweep(sfi, big, dev, main_s, 16, Hq, Hkv, d, L, n_sink, n_recent, None, None)
         del big
+        log("long-context sweeps")
+        result["sweep_long"] = sweep_long(sfi, dev, main_s, Hq, Hkv, d, n_sink, n_recent)
 
     if not args.no_sweep:
         log("64K refresh overlap")
@@ -295,11 +297,12 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
     lses = [torch.empty((B, 1, Hq), dtype=torch.float32, device=dev) for _ in range(R)]
     n_rep = max(20, 400 // R * R)
 
+    dense_calls = [sfi.bind(sfi.dense_attn_with_stats, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"],
+                            max_seq_len=max_len, with_scores=False, out=outs[r], lse=lses[r], workspace=ws_dense,
+                            stream=stream) for r, ly in enumerate(layers)]
+
     def dense(i):
-        ly = layers[i % R]
-        sfi.dense_attn_with_stats(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
-                                  with_scores=False, out=outs[i % R], lse=lses[i % R], workspace=ws_dense,
-                                  stream=stream)
+        dense_calls[i % R]()
     for i in range(R):
         dense(i)
     t_dense = time_loop(dense, n_rep, stream)
@@ -328,12 +331,12 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
                                             dtype=torch.bfloat16, max_seq_len=max_len, cap=cap, n_recent=n_recent)
                          + 16, dtype=torch.uint8, device=dev)
 
+        fast_calls = [sfi.bind(sfi.sparse_decode_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ck, cv, nc,
+                               n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=o, lse=l, workspace=ws,
+                               stream=stream) for ly, (ck, cv, nc, o, l) in zip(layers, comp)]
+
         def fast(i):
-            ly = layers[i % R]
-            ck, cv, nc, o, l = comp[i % R]
-            sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ck, cv, nc, n_sink=n_sink,
-                                   n_recent=n_recent, max_seq_len=max_len, out=o, lse=l, workspace=ws,
-                                   stream=stream)
+            fast_calls[i % R]()
         for i in range(R):
             fast(i)
         t = time_loop(fast, n_rep, stream)
@@ -343,9 +346,41 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
                      "fast_GBps": round(kv / t / 1e9, 1), "fast_pct_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 1),
                      "dense_us": round(t_dense * 1e6, 2), "dense_GBps": round(dense_kv / t_dense / 1e9, 1),
                      "speedup": round(t_dense / t, 3), "speedup_x_r": round(t_dense / t * r, 3)})
-        del comp
-    log("sweep " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows))
+        del comp, fast_calls
+    log(f"sweep L={L} B={B} " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows))
     return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows}
+
+
+def gpu_layers(R, L, B, Hq, Hkv, d, dev, seed):
+    """Replicas of a decode layer drawn on the GPU (seeded N(0,1) bf16 Q/K/V, block tables that are
+    random permutations of the page pool): the long-context sweeps only time kernels, and drawing
+    hundreds of MiB per replica on the host would dominate the run."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    out = []
+    npg = B * L // 16
+    for _ in range(R):
+        k = torch.randn((npg, Hkv, 16, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        v = torch.randn((npg, Hkv, 16, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).reshape(B, L // 16)
+        q = torch.randn((B, 1, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        out.append(dict(k=k, v=v, bt=bt, lens=torch.full((B,), L, dtype=torch.int32, device=dev), q=q,
+                        q1=q[:, 0].contiguous()))
+    return out
+
+
+def sweep_long(sfi, dev, stream, Hq, Hkv, d, n_sink, n_recent):
+    """The batch-1 retention sweep at longer contexts (32K, 64K, 128K)."""
+    import torch
+    res = {}
+    for L in (32768, 65536, 131072):
+        R = max(2, (1 << 30) // (Hkv * L * 2 * d * 2))      # >= 1 GiB of K/V across replicas
+        layers = gpu_layers(R, L, 1, Hq, Hkv, d, dev, 7000 + L)
+        res[str(L)] = sweep(sfi, layers, dev, stream, 1, Hq, Hkv, d, L, n_sink, n_recent, None, None)
+        del layers
+        torch.cuda.empty_cache()
+    return res
 
 
 def refresh_overlap(sfi, dev):

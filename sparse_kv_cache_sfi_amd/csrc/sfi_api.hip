@@ -93,21 +93,19 @@ sfi_status check_budgets(int32_t n_sink, int32_t n_recent) {
   return SFI_OK;
 }
 
-// Split-K plan: enough work-groups to fill the chip, but at least kMinSplit tokens
-// per split, at most kMaxSplitTokens, at most kMaxSplits splits, rounded to the
-// decode tile.
+// Split-K plan: about one work-group per CU (256), but splits of at least
+// 256 tokens (512 once a unit has 8192 or more: the merge of many splits costs more
+// than the parallelism gains), at most kMaxSplitTokens, at most max_splits splits,
+// rounded to the kernel's tile.
 struct Split {
   int tokens;
   int n;
 };
 
-constexpr int64_t kMinSplitDense = 512;
-constexpr int64_t kMinSplitSparse = 256;
-
-Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits,
-                 int64_t min_split = kMinSplitDense) {
-  constexpr int64_t kTargetWGs = 1024;
+Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits) {
+  constexpr int64_t kTargetWGs = 256;
   if (n_tok <= 0) return {tile, 1};
+  const int64_t min_split = n_tok >= 8192 ? 512 : 256;
   const int64_t by_min = (n_tok + min_split - 1) / min_split;
   const int64_t want = (kTargetWGs + units - 1) / units;
   int64_t ns = by_min < want ? by_min : want;
@@ -139,8 +137,7 @@ Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
 
 Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile, sfi::kMaxSplits,
-                    kMinSplitSparse);
+  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile);
 }
 
 sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_t* seq_lens) {
@@ -220,7 +217,7 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
   }
   const int64_t units = (int64_t)B * shape->num_kv_heads;
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile, sfi::kMaxSplits, kMinSplitSparse);
+  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile);
   const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
   sfi::MixedPlan& p = ms->plan;
   p = sfi::MixedPlan{};
