@@ -24,9 +24,18 @@ FLAGS = [
 ]
 
 
+# The MFMA kernels keep their accumulators in architectural VGPRs: in the accumulation
+# register form the online-softmax rescale copies every accumulator to VGPRs and back on
+# every iteration, and the register budget then allows one wave per SIMD instead of two.
+FILE_FLAGS = {
+    "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "mixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in p.stderr.splitlines() if noise not in l)

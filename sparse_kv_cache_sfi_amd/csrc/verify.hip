@@ -4,28 +4,37 @@
 
 namespace sfi {
 
-template <int D, bool SCORES>
-__global__ __launch_bounds__(256) void verify_kernel(AttnArgs a, int G) {
+template <int D, int G, bool SCORES>
+__global__ __launch_bounds__(256) void verify_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[VerifyShape<D>::SMEM];
   verify_unit<D, SCORES>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z * a.t_q, G, smem);
 }
 
-hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream) {
+template <int D, int G>
+static hipError_t launch_g(const AttnArgs& a, int B, hipStream_t stream) {
   const dim3 grid(a.n_split, a.Hkv, B), block(256);
-  if (d == 128) {
-    if (a.scores)
-      hipLaunchKernelGGL((verify_kernel<128, true>), grid, block, 0, stream, a, G);
-    else
-      hipLaunchKernelGGL((verify_kernel<128, false>), grid, block, 0, stream, a, G);
-  } else if (d == 64) {
-    if (a.scores)
-      hipLaunchKernelGGL((verify_kernel<64, true>), grid, block, 0, stream, a, G);
-    else
-      hipLaunchKernelGGL((verify_kernel<64, false>), grid, block, 0, stream, a, G);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (a.scores)
+    hipLaunchKernelGGL((verify_kernel<D, G, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((verify_kernel<D, G, false>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const AttnArgs& a, int G, int B, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_g<D, 1>(a, B, stream);
+    case 2: return launch_g<D, 2>(a, B, stream);
+    case 4: return launch_g<D, 4>(a, B, stream);
+    case 8: return launch_g<D, 8>(a, B, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream) {
+  if (d == 128) return launch_d<128>(a, G, B, stream);
+  if (d == 64) return launch_d<64>(a, G, B, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sfi

@@ -52,7 +52,10 @@ struct VerifyShape {
   // The tiles start on a 128-byte boundary: 16-byte LDS accesses must be 16-byte
   // aligned to run at full rate.
   static constexpr int BIG_OFF = (kBtSlots * 4 + 16 + 127) / 128 * 128;
-  static constexpr int SMEM = BIG_OFF + BIG;
+  // The 32 query rows (the B operand of S^T) live in LDS, shared by the waves, rather
+  // than in 32 registers per lane: that keeps the kernel within two waves per SIMD.
+  static constexpr int Q_OFF = BIG_OFF + BIG;
+  static constexpr int SMEM = Q_OFF + 32 * LDS_ROW;
   static_assert(LOADS >= 1, "tile too small");
 };
 
@@ -91,16 +94,20 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
   }
 
-  // Query rows as the B operand: lane holds row n, dims [16 s + 8 hb, +8) of step s.
-  const int qt = n / G, qh = n % G;
-  const bool row_ok = n < R;
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(q_row0 + qt) * a.Hq + g * G + qh) * D;
-  u32x4 qb[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    qb[s] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hb) : z;
+  // Query rows r = (t, h) into LDS, zero rows past R (they contribute nothing).
+  char* q_s = smem + S::Q_OFF;
+  for (int i = tid; i < 32 * CPR; i += NT) {
+    const int r = i / CPR, ch = i % CPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      const uint16_t* qr =
+          reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(q_row0 + r / G) * a.Hq + g * G + r % G) * D;
+      v = *reinterpret_cast<const u32x4*>(qr + ch * 8);
+    }
+    *reinterpret_cast<u32x4*>(q_s + r * LDS_ROW + ch * 16) = v;
   }
+  const int qt = n / G;
+  const bool row_ok = n < R;
   // Query token t sits at position L - t_q + t and sees keys up to it.
   const int lim = row_ok ? L - a.t_q + qt : -1;
   __syncthreads();
@@ -175,8 +182,10 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
+      // B operand: lane holds query row n, dims [16 s + 8 hb, +8).
       const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + n * LDS_ROW + (16 * s + 8 * hb) * 2);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb[s]),
+      const u32x4 qb = *reinterpret_cast<const u32x4*>(q_s + n * LDS_ROW + (16 * s + 8 * hb) * 2);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb),
                                                       sacc, 0, 0, 0);
     }
 
