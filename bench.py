@@ -268,6 +268,8 @@ def main():
     if not args.no_sweep:
         log("64K refresh overlap")
         result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
+        log("refresh schedule on drifting support")
+        result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
         log("128K speculative mix")
         result["specmix_128k"] = specmix(sfi, dev)
 
@@ -380,6 +382,86 @@ def sweep_long(sfi, dev, stream, Hq, Hkv, d, n_sink, n_recent):
         res[str(L)] = sweep(sfi, layers, dev, stream, 1, Hq, Hkv, d, L, n_sink, n_recent, None, None)
         del layers
         torch.cuda.empty_cache()
+    return res
+
+
+def refresh_schedule_c3(sfi, dev, steps=64, period=16):
+    """Fixed-interval slow steps on the batched decode workload (16 requests, 32 query / 8 KV heads,
+    lengths uniform in [16K, 32K], sink 4, selected 1024, recent 256) whose 256 planted heavy hitters
+    per (request, KV head) persist for 16 query steps, then shift.  For each refresh interval: the
+    amortised time per decode step of the batch, and the recall of the current support (the share of
+    the planted keys inside the selected set the step attends over) by steps since the last refresh.
+    The data are drawn on the GPU (seeded); the schedule is sparse_kv_cache_sfi_amd.schedule."""
+    import torch
+    from sparse_kv_cache_sfi_amd.schedule import RefreshSchedule
+    B, Hq, Hkv, d, n_sink, n_recent, k, hh = 16, 32, 8, 128, 4, 256, 1024, 256
+    G = Hq // Hkv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    L0 = torch.randint(16384, 32769, (B,), generator=gen, device=dev).cpu()
+    cap_tok = L0 + steps
+    pages = (cap_tok + 15) // 16
+    num_pages, max_pages = int(pages.sum()), int(pages.max())
+    perm = torch.randperm(num_pages, generator=gen, device=dev).to(torch.int32)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32, device=dev)
+    off = 0
+    for b in range(B):
+        bt[b, :int(pages[b])] = perm[off:off + int(pages[b])]
+        off += int(pages[b])
+    kp = torch.randn((num_pages, Hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16)
+    vp = torch.randn((num_pages, Hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16)
+    E = (steps + period - 1) // period
+    u = torch.randn((E, B, Hkv, d), generator=gen, device=dev)
+    support = torch.empty((E, B, Hkv, hh), dtype=torch.int64, device=dev)
+    for b in range(B):
+        lo, hi = n_sink, int(L0[b]) - n_recent
+        for g in range(Hkv):
+            pos = torch.randperm(hi - lo, generator=gen, device=dev)[:E * hh] + lo
+            for e in range(E):
+                pe = torch.sort(pos[e * hh:(e + 1) * hh]).values
+                support[e, b, g] = pe
+                kp[bt[b, pe // 16].long(), g, pe % 16, :] = (4.0 * u[e, b, g]).to(torch.bfloat16)
+    epoch = torch.arange(steps, device=dev) // period
+    q_steps = (u[epoch][:, :, torch.arange(Hq, device=dev) // G, :]
+               + 0.25 * torch.randn((steps, B, Hq, d), generator=gen, device=dev)).to(torch.bfloat16)
+    max_len = int(max_pages * 16)
+    q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    lens = torch.empty((B,), dtype=torch.int32, device=dev)
+    lens_steps = [(L0 + t + 1).to(torch.int32).to(dev) for t in range(steps)]
+    res = {"requests": B, "kv_len_range": [16384, 32768], "steps": steps, "support_period": period,
+           "planted_per_head": hh, "selected": k, "intervals": {}}
+    for interval in (1, 4, 8, 16, 32, steps):
+        sched = RefreshSchedule(kp, vp, bt, q, lens, max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, k=k,
+                                interval=interval)
+        # recall pass (host reads between steps)
+        by_age = {}
+        for t in range(steps):
+            q.copy_(q_steps[t])
+            lens.copy_(lens_steps[t])
+            sched.step()
+            if t % interval:
+                cur = support[t // period]                                   # [B, Hkv, hh]
+                hit = (cur.unsqueeze(-1) == sched.sel.long().unsqueeze(-2)).any(-1).float().mean().item()
+                by_age.setdefault(t % interval, []).append(hit)
+        # timed pass
+        sched.t = 0
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for t in range(steps):
+            q.copy_(q_steps[t])
+            lens.copy_(lens_steps[t])
+            sched.step()
+        t1.record()
+        t1.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        ages = sorted(by_age)
+        res["intervals"][str(interval)] = {
+            "us_per_step": round(us, 1), "slow_steps": (steps + interval - 1) // interval,
+            "fast_step_recall_mean": round(float(np.mean([x for a in ages for x in by_age[a]])), 4) if ages else None,
+            "recall_by_steps_since_refresh": {str(a): round(float(np.mean(by_age[a])), 4) for a in ages}}
+        del sched
+    log(f"refresh schedule {res}")
     return res
 
 

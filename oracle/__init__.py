@@ -43,4 +43,5 @@ from .sfi_oracle import (  # noqa: F401
     pack_compact,
     sparse_decode,
     mixed,
+    refresh_loop,
 )

@@ -260,3 +260,43 @@ def mixed(modes: Sequence[int], t_q: Sequence[int], q_rows: Sequence[np.ndarray]
                              n_sink, n_recent, stride, kv_dtype, groups)
             res.append((o, l, S))
     return res
+
+
+# --------------------------------------------------------------------------- refresh schedule
+
+def refresh_loop(q_steps: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.ndarray,
+                 L0: int, Hkv: int, n_sink: int, n_recent: int, k: int, interval: int, scale: float,
+                 cap: int, kv_dtype: str = "f32", scores_at=None):
+    """One request's decode steps with a slow step every ``interval`` steps and fast steps
+    between (SFI page, Fig. 2 and its caption: slow steps perform dense attention and refresh
+    the selected memory from the masked logits; fast steps attend over sink + selected +
+    recent; the pages' own trigger is a sentence boundary, here a fixed interval).
+
+    Step t decodes the token at position L0 + t, so its length is L = L0 + t + 1; its queries
+    are q_steps[t] [Hq, d].  A slow step (t % interval == 0) outputs dense attention over
+    [0, L), forms the candidate logits, selects per KV head and packs the compact buffer.  A
+    fast step attends over that compact buffer and the recent window at its own L.
+    ``scores_at(t)`` may return the [Hkv, >= L] logits to select from (the fp32 values a
+    device produced); by default the function's own logits are used.
+
+    Returns per step (out [Hq, d], lse [Hq], sel [Hkv, k] or None, logits or None).
+    """
+    res = []
+    ck = cv = None
+    n_c = 0
+    for t in range(len(q_steps)):
+        q = np.asarray(q_steps[t], dtype=np.float64)
+        L = L0 + t + 1
+        if t % interval == 0:
+            out, lse = dense_attention(q[None], k_pool, v_pool, block_table_row, L, scale, Hkv, kv_dtype)
+            S = group_scores(q[None], k_pool, block_table_row, L, scale, Hkv, n_sink, n_recent, L, kv_dtype)
+            S_sel = S if scores_at is None else scores_at(t)
+            lo, hi = candidate_range(L, 1, n_sink, n_recent)
+            sel = np.stack([select_topk(S_sel[g], lo, hi, k) for g in range(Hkv)])
+            ck, cv, n_c = pack_compact(k_pool, v_pool, block_table_row, L, n_sink, sel, cap)
+            res.append((out[0], lse[0], sel, S))
+        else:
+            out, lse = sparse_decode(q, ck, cv, n_c, k_pool, v_pool, block_table_row, L, n_sink, n_recent,
+                                     scale, kv_dtype)
+            res.append((out, lse, None, None))
+    return res

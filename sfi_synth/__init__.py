@@ -27,7 +27,7 @@ PAGE_SIZE = 16
 __all__ = [
     "PAGE_SIZE", "bf16_bits", "bf16_values", "PagedKV", "Case",
     "make_case", "tiny_case", "qwen06b_decode_case", "qwen8b_batched_case",
-    "refresh64k_case", "specmix128k_case", "retention_budget", "RETENTIONS",
+    "refresh64k_case", "specmix128k_case", "retention_budget", "RETENTIONS", "DriftCase", "drifting_case",
 ]
 
 
@@ -268,3 +268,62 @@ def specmix128k_case(seed: int = 5, B: int = 8, L: int = 131072, t_q: int = 8,
                   hh_per_head=max(1, round(0.02 * (L - t_q + 1 - n_sink - n_recent))))
     c.modes = np.array([0] * n_draft + [1] * (B - n_draft), dtype=np.int32)
     return c
+
+
+# --------------------------------------------------------------------------- drifting support
+
+@dataclass
+class DriftCase:
+    """A decode run whose heavy hitters persist for ``period`` query steps, then shift.
+
+    ``case`` holds the pools (sized for every step's token) with ``seq_lens`` = L0, the
+    lengths before the first step.  Step t decodes the token at position L0 + t, whose
+    K/V already sit in the pool, so the request length at step t is L0 + t + 1.
+    ``q_steps`` [steps, B, Hq, d] are the queries (storage form) and ``support``
+    [epochs, B, Hkv, hh] the planted positions of each epoch (sorted)."""
+    case: Case
+    steps: int
+    period: int
+    q_steps: np.ndarray
+    support: np.ndarray
+
+    def q_step_values(self) -> np.ndarray:
+        return _values(self.q_steps, self.case.dtype)
+
+
+def drifting_case(seed: int, *, B: int, Hq: int, Hkv: int, d: int, dtype: str, L0, steps: int,
+                  period: int, hh: int, n_sink: int, n_recent: int, k_sel: int,
+                  noise: float = 0.25) -> DriftCase:
+    """Heavy hitters that persist across ``period`` consecutive query steps, then shift.
+
+    Epoch e = t // period has, per (request b, KV head g), a direction u ~ N(0, 1)^d and
+    ``hh`` positions drawn without replacement from [n_sink, L0_b - n_recent) (disjoint
+    from every other epoch's); their keys are set to 4 u.  The queries of step t are
+    u_e(t),b,g(h) + noise * N(0, 1) for every query head h of group g.  Draw order: the
+    pools (as make_case with no planting), then per epoch the directions and positions,
+    then the query noise."""
+    L0 = np.broadcast_to(np.asarray(L0, dtype=np.int32), (B,)).copy()
+    c = make_case(seed, name="drift", B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, seq_lens=L0,
+                  capacity=[int(x) + steps for x in L0], n_sink=n_sink, n_recent=n_recent, k_sel=k_sel)
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    G = Hq // Hkv
+    E = (steps + period - 1) // period
+    u = rng.standard_normal((E, B, Hkv, d), dtype=np.float32)
+    support = np.zeros((E, B, Hkv, hh), dtype=np.int64)
+    bt = c.kv.block_table
+    for b in range(B):
+        lo, hi = n_sink, int(L0[b]) - n_recent
+        if hi - lo < E * hh:
+            raise ValueError("not enough candidate positions for the planted support")
+        for g in range(Hkv):
+            pos = rng.choice(hi - lo, size=E * hh, replace=False) + lo
+            for e in range(E):
+                pe = np.sort(pos[e * hh:(e + 1) * hh]).astype(np.int64)
+                support[e, b, g] = pe
+                key = _store((4.0 * u[e, b, g]).astype(np.float32), dtype)
+                c.kv.k[bt[b, pe // PAGE_SIZE], g, pe % PAGE_SIZE, :] = key
+    eps = rng.standard_normal((steps, B, Hq, d), dtype=np.float32)
+    epoch = np.arange(steps) // period
+    dirs = u[epoch][:, :, np.repeat(np.arange(Hkv), G), :]          # [steps, B, Hq, d]
+    q_steps = _store(dirs + np.float32(noise) * eps, dtype)
+    return DriftCase(case=c, steps=steps, period=period, q_steps=q_steps, support=support)

@@ -362,6 +362,56 @@ def test_mixed_dispatches_per_request():
     assert np.array_equal(res[1][0], o1) and res[1][2].shape == (2, 256)
 
 
+# --------------------------------------------------------------------------- refresh schedule
+
+def _drift(seed=31, q_gain=1.0, hh=12):
+    from sfi_synth import drifting_case
+    dc = drifting_case(seed, B=1, Hq=4, Hkv=2, d=64, dtype="f32", L0=[700], steps=40, period=16, hh=hh,
+                       n_sink=4, n_recent=32, k_sel=24, noise=0.0)
+    c = dc.case
+    q = dc.q_step_values()[:, 0] * q_gain          # [steps, Hq, d]
+    return dc, c, q
+
+
+def test_refresh_loop_every_step_is_dense_attention_on_scatter_built_kv():
+    """interval = 1: every step is a slow step, i.e. dense attention over [0, L0 + t + 1)."""
+    dc, c, q = _drift()
+    res = O.refresh_loop(q[:6], c.kv.k, c.kv.v, c.kv.block_table[0], 700, c.Hkv, 4, 32, 24, 1, c.scale, 4 + 24)
+    for t, (out, lse, sel, S) in enumerate(res):
+        L = 700 + t + 1
+        assert sel is not None and S is not None
+        for h in range(c.Hq):
+            Kl = _logical(c.kv.k, c.kv.block_table[0], L, h // 2)
+            Vl = _logical(c.kv.v, c.kv.block_table[0], L, h // 2)
+            np.testing.assert_allclose(out[h], _sdpa(q[t, h][None], Kl, Vl, c.scale)[0], rtol=0, atol=1e-12)
+
+
+def test_refresh_loop_fast_steps_match_dense_while_the_support_holds_all_mass():
+    """Queries 30x larger make every key outside the epoch's planted support weigh exactly
+    zero in fp64 (logit gaps > 745).  A fast step after a refresh in the same epoch then
+    equals dense attention; after an epoch shift without refresh it does not."""
+    dc, c, q = _drift(q_gain=30.0)
+    res = O.refresh_loop(q, c.kv.k, c.kv.v, c.kv.block_table[0], 700, c.Hkv, 4, 32, 24, 8, c.scale, 4 + 24)
+    for t, (out, lse, sel, S) in enumerate(res):
+        L = 700 + t + 1
+        dense, dlse = O.dense_attention(q[t][None], c.kv.k, c.kv.v, c.kv.block_table[0], L, c.scale, c.Hkv)
+        last_refresh = t - t % 8
+        same_epoch = last_refresh // dc.period == t // dc.period
+        if same_epoch:
+            np.testing.assert_allclose(out, dense[0], rtol=0, atol=1e-10)
+        else:
+            assert np.abs(out - dense[0]).max() > 0.1, t
+
+
+def test_refresh_loop_selects_the_current_support_after_a_refresh():
+    dc, c, q = _drift()
+    res = O.refresh_loop(q, c.kv.k, c.kv.v, c.kv.block_table[0], 700, c.Hkv, 4, 32, 24, 8, c.scale, 4 + 24)
+    for t in range(0, 40, 8):
+        sel = res[t][2]
+        for g in range(c.Hkv):
+            assert set(dc.support[t // dc.period, 0, g].tolist()) <= set(sel[g].tolist()), (t, g)
+
+
 def test_oracle_is_independent_of_the_product():
     here = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle")
     for fn in os.listdir(here):
