@@ -44,4 +44,5 @@ from .sfi_oracle import (  # noqa: F401
     sparse_decode,
     mixed,
     refresh_loop,
+    append_token,
 )

@@ -262,6 +262,24 @@ def mixed(modes: Sequence[int], t_q: Sequence[int], q_rows: Sequence[np.ndarray]
     return res
 
 
+# --------------------------------------------------------------------------- KV append
+
+def append_token(k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.ndarray, L: int,
+                 k_new: np.ndarray, v_new: np.ndarray, page_size: int = 16):
+    """Pools after storing the decoded token's K/V (k_new, v_new: [Hkv, d] stored rows) at
+    position L - 1 of one request, the slot a fast step then reads in place as its newest
+    recent token (SFI page, Fig. 3B).  A position behind an invalid block-table entry is
+    not stored.  Returns copies of the two pools."""
+    k2, v2 = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    if L < 1:
+        return k2, v2
+    page = int(block_table_row[(L - 1) // page_size])
+    if 0 <= page < k_pool.shape[0]:
+        k2[page, :, (L - 1) % page_size, :] = k_new
+        v2[page, :, (L - 1) % page_size, :] = v_new
+    return k2, v2
+
+
 # --------------------------------------------------------------------------- refresh schedule
 
 def refresh_loop(q_steps: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.ndarray,

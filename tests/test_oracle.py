@@ -362,6 +362,29 @@ def test_mixed_dispatches_per_request():
     assert np.array_equal(res[1][0], o1) and res[1][2].shape == (2, 256)
 
 
+# --------------------------------------------------------------------------- KV append
+
+def test_append_token_stores_one_row_and_a_dominant_new_key_returns_its_value():
+    c = make_case(41, name="ap", B=1, Hq=4, Hkv=2, d=64, dtype="f32", seq_lens=[300], capacity=[310], n_sink=4,
+                  n_recent=16, k_sel=8)
+    rng = np.random.default_rng(3)
+    L = 305                                      # decoding position 304
+    q = c.q_values()[0, 0]
+    k_new = np.stack([40.0 * q[g * 2:(g + 1) * 2].mean(axis=0) for g in range(2)]).astype(np.float32)
+    v_new = rng.standard_normal((2, 64)).astype(np.float32)
+    k2, v2 = O.append_token(c.kv.k, c.kv.v, c.kv.block_table[0], L, k_new, v_new)
+    for g in range(2):
+        np.testing.assert_array_equal(O.paged_rows(k2, c.kv.block_table[0], g, [L - 1])[0], k_new[g])
+        np.testing.assert_array_equal(O.paged_rows(v2, c.kv.block_table[0], g, [L - 1])[0], v_new[g])
+    changed = np.argwhere(np.any(k2 != c.kv.k, axis=-1))
+    assert len(changed) == 2 and np.all(changed[:, 2] == (L - 1) % PAGE_SIZE)
+    # the new key dominates every query of its group: the fast step returns its value
+    ck, cv, n_c = O.pack_compact(k2, v2, c.kv.block_table[0], L, 4, np.full((2, 8), -1, np.int32), 12)
+    out, _ = O.sparse_decode(q, ck, cv, n_c, k2, v2, c.kv.block_table[0], L, 4, 16, c.scale)
+    for h in range(4):
+        np.testing.assert_allclose(out[h], v_new[h // 2], rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- refresh schedule
 
 def _drift(seed=31, q_gain=1.0, hh=12):
