@@ -268,6 +268,8 @@ def main():
     if not args.no_sweep:
         log("64K refresh overlap")
         result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
+        log("fused KV append + fast step")
+        result["append_fast"] = append_fast(sfi, dev, main_s)
         log("refresh schedule on drifting support")
         result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
         log("128K speculative mix")
@@ -380,6 +382,80 @@ def sweep_long(sfi, dev, stream, Hq, Hkv, d, n_sink, n_recent):
         R = max(2, (1 << 30) // (Hkv * L * 2 * d * 2))      # >= 1 GiB of K/V across replicas
         layers = gpu_layers(R, L, 1, Hq, Hkv, d, dev, 7000 + L)
         res[str(L)] = sweep(sfi, layers, dev, stream, 1, Hq, Hkv, d, L, n_sink, n_recent, None, None)
+        del layers
+        torch.cuda.empty_cache()
+    return res
+
+
+def append_fast(sfi, dev, stream, Hq=16, Hkv=8, d=128, n_sink=4, n_recent=64):
+    """Fast step with the decoded token's K/V stored in the same launch
+    (sfi_sparse_decode_append_attn) against the plain fast step, and against the
+    unfused order: the same store as two indexed copies into the pools, then the plain
+    fast step.  16K-token requests at batch 1 and 16, at 1/64 and 1/8 retention."""
+    import numpy as np
+    import torch
+    from sfi_synth import retention_budget
+    res = []
+    rng = np.random.default_rng(11)
+    for B in (1, 16):
+        L = 16384
+        R = max(2, (1 << 30) // (B * Hkv * L * 2 * d * 2))
+        layers = gpu_layers(R, L, B, Hq, Hkv, d, dev, 9100 + B)
+        n_rep = max(40, 400 // R * R)
+        for frac in ((1, 64), (1, 8)):
+            k = retention_budget(L, frac, n_sink, n_recent)
+            cap = n_sink + k
+            ws = torch.zeros(sfi.workspace_size("sparse", k_pool=layers[0]["k"], block_table=layers[0]["bt"],
+                                                Hq=Hq, dtype=torch.bfloat16, max_seq_len=L, cap=cap,
+                                                n_recent=n_recent) + 16, dtype=torch.uint8, device=dev)
+            plain, fused, stores = [], [], []
+            for ly in layers:
+                sel = np.stack([np.sort(rng.choice(np.arange(n_sink, L - n_recent), k, replace=False))
+                                for _ in range(B * Hkv)]).astype(np.int32).reshape(B, Hkv, k)
+                ck, cv, nc = sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], torch.from_numpy(sel).to(dev),
+                                              n_sink=n_sink, cap=cap, max_seq_len=L, stream=stream)
+                kn = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+                vn = torch.randn((B, Hkv, d), device=dev).to(torch.bfloat16)
+                o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+                l = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+                common = dict(n_sink=n_sink, n_recent=n_recent, max_seq_len=L, out=o, lse=l, workspace=ws,
+                              stream=stream)
+                args = (ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ck, cv, nc)
+                plain.append(sfi.bind(sfi.sparse_decode_attn, *args, **common))
+                fused.append(sfi.bind(sfi.sparse_decode_attn, *args, k_new=kn, v_new=vn, **common))
+                pg = ly["bt"][torch.arange(B, device=dev), (ly["lens"] - 1) // 16].long()
+                row = ((ly["lens"] - 1) % 16).long()
+                stores.append((ly["k"], ly["v"], pg, row, kn, vn))
+
+            def store(i):
+                kp, vp, pg, row, kn, vn = stores[i % R]
+                kp[pg, :, row, :] = kn
+                vp[pg, :, row, :] = vn
+
+            def run_plain(i):
+                plain[i % R]()
+
+            def run_fused(i):
+                fused[i % R]()
+
+            def run_sep(i):
+                store(i)
+                plain[i % R]()
+            with torch.cuda.stream(stream):
+                for f in (run_plain, run_fused, run_sep):
+                    for i in range(R):
+                        f(i)
+                t = {n: time_loop(f, n_rep, stream) for n, f in
+                     (("plain", run_plain), ("fused", run_fused), ("store_then_fast", run_sep),
+                      ("store_only", store))}
+            kv = B * Hkv * (cap + n_recent) * 2 * d * 2
+            res.append({"batch": B, "kv_len": L, "retention": f"{frac[0]}/{frac[1]}", "selected": k,
+                        **{f"{n}_us": round(v * 1e6, 2) for n, v in t.items()},
+                        "fused_GBps": round(kv / t["fused"] / 1e9, 1),
+                        "fused_saving_pct": round(100 * (1 - t["fused"] / t["store_then_fast"]), 1)})
+            log(f"append B={B} {frac[0]}/{frac[1]}: fused {t['fused'] * 1e6:.2f} us, plain {t['plain'] * 1e6:.2f}, "
+                f"store+fast {t['store_then_fast'] * 1e6:.2f}")
+            del plain, fused, stores, ws
         del layers
         torch.cuda.empty_cache()
     return res

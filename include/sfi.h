@@ -245,6 +245,25 @@ SFI_API sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, cons
                                             int32_t cap, int32_t n_recent, size_t* bytes);
 
 /*
+ * Fast step with KV append: the token being decoded (position seq_lens[b] - 1)
+ * has its K/V in k_new / v_new [B, Hkv, d] (pool dtype, 16-byte aligned).  The
+ * launch stores them into that position's page of kv.k / kv.v (which must be
+ * writable device memory) and attends exactly as sfi_sparse_decode_attn would
+ * after that store; the new row is read from k_new / v_new, so the result does
+ * not depend on the store.  The recent tokens are read in place from paged KV
+ * (SFI page, Fig. 3B); appending in the same launch saves the separate append
+ * launch before every fast step.  A position whose block-table entry is invalid
+ * is neither stored nor attended.  Arguments and workspace otherwise as
+ * sfi_sparse_decode_attn.
+ */
+SFI_API sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                         const void* q, const void* k_new, const void* v_new,
+                                         const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                         const void* compact_k, const void* compact_v, int32_t cap,
+                                         const int32_t* n_compact, float* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Drafting and verifying requests in one launch (ASPIRE abstract: a unified
  * mixed forward lets drafting and verifying requests share one batched
  * pass; SparseSpec-L abstract: drafts attend over a sparse, recallable KV

@@ -73,6 +73,9 @@ _SIGS = {
     "sfi_sparse_decode_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_sparse_decode_workspace_size": [_SHAPE_P, _KV_P, c_int32, c_int32, POINTER(c_size_t)],
+    "sfi_sparse_decode_append_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                      c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p],
     "sfi_mixed_attn": [_SHAPE_P, _KV_P, c_void_p, POINTER(c_int32), POINTER(c_int32), c_void_p, c_int32,
                        c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                        c_void_p, c_size_t, c_void_p],
@@ -375,9 +378,19 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
                        seq_lens: torch.Tensor, compact_k: torch.Tensor, compact_v: torch.Tensor,
                        n_compact: torch.Tensor, *, n_sink: int, n_recent: int, max_seq_len: int,
                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Fast step: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq])."""
+                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                       k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None):
+    """Fast step: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq]).  With k_new / v_new
+    [B, Hkv, d] (the decoded token's K/V) the launch also stores them into the pools at
+    position seq_lens[b] - 1 (sfi_sparse_decode_append_attn)."""
     _dev(q, "q")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, n)
+            if t.dtype != k_pool.dtype or tuple(t.shape) != (q.shape[0], k_pool.shape[1], q.shape[2]):
+                raise ValueError(f"{n} must be [B, Hkv, d] in the pool dtype")
     _dev(compact_k, "compact_k")
     _dev(compact_v, "compact_v")
     _i32(seq_lens, "seq_lens")
@@ -395,9 +408,15 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
     _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), cap, n_recent,
           ctypes.byref(need))
     ws = _workspace(need.value, workspace, dev)
-    _call("sfi_sparse_decode_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
-          n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(),
-          _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
+    if k_new is None:
+        _call("sfi_sparse_decode_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
+              n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
+              out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
+    else:
+        _call("sfi_sparse_decode_append_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
+              k_new.data_ptr(), v_new.data_ptr(), seq_lens.data_ptr(), n_sink, n_recent, compact_k.data_ptr(),
+              compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
+              _stream(stream, dev))
     return out, lse
 
 

@@ -77,7 +77,7 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
   return acc;
 }
 
-template <typename T, int D, int G, bool SPARSE, bool SCORES>
+template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, const int g, const int split,
                                             const int q_row0, char* smem) {
   using S = DecodeShape<T, D, G>;
@@ -143,6 +143,26 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   }
   const int64_t page_elems = (int64_t)a.Hkv * kPage * D;
   const int64_t head_off = (int64_t)g * kPage * D;
+  const T* knew = nullptr;
+  const T* vnew = nullptr;
+  if constexpr (APPEND) {
+    // The new token (position L - 1) is attended from the arguments; the last split's
+    // work-group also stores it into its page (no other work-group reads that row).
+    knew = reinterpret_cast<const T*>(a.k_new) + ((int64_t)b * a.Hkv + g) * D;
+    vnew = reinterpret_cast<const T*>(a.v_new) + ((int64_t)b * a.Hkv + g) * D;
+    constexpr int CH = D * (int)sizeof(T) / 16;
+    if (split == a.n_split - 1 && L > 0 && tid < 2 * CH) {
+      const int pg = bt_row[(L - 1) >> 4];
+      if (pg >= 0 && pg < a.num_pages) {
+        const int64_t off = (int64_t)pg * page_elems + head_off + (int64_t)((L - 1) & 15) * D;
+        const int c = tid % CH;
+        const T* src = tid < CH ? knew : vnew;
+        T* dst = const_cast<T*>(tid < CH ? kpool : vpool) + off;
+        *reinterpret_cast<u32x4*>(dst + c * (16 / (int)sizeof(T))) =
+            *reinterpret_cast<const u32x4*>(src + c * (16 / (int)sizeof(T)));
+      }
+    }
+  }
 
   int clo = 0, chi = 0;
   float* srow = nullptr;
@@ -194,6 +214,12 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
         if (compact) {
           kr = ckb + (int64_t)vi * D;
           vr = cvb + (int64_t)vi * D;
+        }
+      }
+      if constexpr (APPEND) {
+        if (ok && !compact && p == L - 1) {
+          kr = knew;
+          vr = vnew;
         }
       }
 #pragma unroll

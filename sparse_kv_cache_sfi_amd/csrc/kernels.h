@@ -59,6 +59,10 @@ struct AttnArgs {
   int32_t* counters;      // [B * Hkv] split arrival counters (zero between calls)
   float* scores;          // [B, Hkv, score_stride] (nullable)
   int64_t score_stride;
+  // Fast step with append: request b's token at position L_b - 1 arrives here
+  // ([B, Hkv, d], pool dtype); the launch writes it into its page and attends to it.
+  const void* k_new;
+  const void* v_new;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves

@@ -458,10 +458,14 @@ sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_pa
   return ok();
 }
 
-sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
-                                  const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, const void* compact_k,
-                                  const void* compact_v, int32_t cap, const int32_t* n_compact, float* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sfi_status sparse_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, const void* k_new,
+                       const void* v_new, const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                       const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
+                       float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
   SFI_TRY(check_ptr16(q, "q"));
@@ -493,11 +497,36 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
   a.t_q = 1;
   a.out = out;
   a.lse = lse;
+  a.k_new = k_new;
+  a.v_new = v_new;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipError_t e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, true, shape->batch, st);
   return hip_status(e, "sparse decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                  const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, const void* compact_k,
+                                  const void* compact_v, int32_t cap, const int32_t* n_compact, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_call(shape, kv, q, nullptr, nullptr, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
+                     n_compact, out, lse, workspace, workspace_bytes, stream);
+}
+
+sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                         const void* k_new, const void* v_new, const int32_t* seq_lens,
+                                         int32_t n_sink, int32_t n_recent, const void* compact_k,
+                                         const void* compact_v, int32_t cap, const int32_t* n_compact, float* out,
+                                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  SFI_TRY(check_ptr16(k_new, "k_new"));
+  SFI_TRY(check_ptr16(v_new, "v_new"));
+  return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
+                     n_compact, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
-              "sfi_mixed_attn", "sfi_dense_attn_with_refresh"):
+              "sfi_mixed_attn", "sfi_dense_attn_with_refresh", "sfi_sparse_decode_append_attn"):
         assert n in names
 
 
@@ -163,6 +163,19 @@ def test_sparse_rejects_bad_arguments(lib):
     assert call(cap=0) == 1
     assert call(n_recent=-1) == 1
     assert call(out=0) == 1
+    assert call(ws_bytes=1) == 3
+
+
+def test_sparse_append_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def call(kn=FAKE, vn=FAKE, q=FAKE, ws_bytes=1 << 40):
+        return lib.sfi_sparse_decode_append_attn(ctypes.byref(shape), ctypes.byref(kv), q, kn, vn, FAKE, 4, 64, FAKE,
+                                                 FAKE, 2048, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(kn=0) == 1 and "k_new is NULL" in lib.sfi_last_error().decode()
+    assert call(vn=0) == 1 and "v_new is NULL" in lib.sfi_last_error().decode()
+    assert call(kn=MISALIGNED) == 1 and "aligned" in lib.sfi_last_error().decode()
+    assert call(q=MISALIGNED) == 1
     assert call(ws_bytes=1) == 3
 
 
