@@ -32,33 +32,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // Exclusive prefix sum of one value per thread over the work-group, in thread
-// order; *total receives the sum.  sh needs kSelWaves + 1 ints.
+// order; *total receives the sum.  One barrier: each wave scans its lanes, publishes
+// its total in sh (kSelWaves ints), and every thread then adds up the totals of the
+// lower waves itself.  Two calls that share sh need a barrier between them (every
+// caller has one).
 __device__ __forceinline__ int block_exclusive_scan(int x, int* total, int* sh) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_inclusive_sum(x);
   if (lane == kWave - 1) sh[w] = incl;
   __syncthreads();
-  if (w == 0) {
-    const int v = lane < kSelWaves ? sh[lane] : 0;
-    int vi = v;
+  int before = 0, tot = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(vi, off);
-      if (lane >= off) vi += y;
-    }
-    if (lane < kSelWaves) sh[lane] = vi - v;
-    if (lane == kSelWaves - 1) sh[kSelWaves] = vi;
+  for (int i = 0; i < kSelWaves; ++i) {
+    const int v = sh[i];
+    before += i < w ? v : 0;
+    tot += v;
   }
-  __syncthreads();
-  const int res = sh[w] + incl - x;
-  *total = sh[kSelWaves];
-  __syncthreads();
-  return res;
+  *total = tot;
+  return before + incl - x;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores, int Hkv,
@@ -67,6 +58,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
                                                              int32_t* __restrict__ sel) {
   __shared__ uint32_t hist[kSelWaves][256];
   __shared__ int scan_sh[kSelWaves + 1];
+  __shared__ int scan_sh2[kSelWaves + 1];   // the collection's second scan (no barrier between the two)
   __shared__ int pick[2];
   const int row = blockIdx.x;
   const int b = row / Hkv;
@@ -154,7 +146,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
       ns += t ? 1 : 0;
     }
     int tot_sel;
-    int pos = base + block_exclusive_scan(ns, &tot_sel, scan_sh);
+    int pos = base + block_exclusive_scan(ns, &tot_sel, scan_sh2);
 #pragma unroll
     for (int v = 0; v < kSelPerThread; ++v)
       if (take[v] && pos < k) out[pos++] = j0 + v;
@@ -174,39 +166,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 constexpr int kHistBins = 4096;
 
 // Exclusive prefix sums of two values per thread over the work-group, in thread
-// order (one set of barriers for both); *total receives the sums.  sh needs
-// kSelWaves + 1 entries.
+// order, with one barrier for both (as block_exclusive_scan); *total receives the
+// sums.  sh needs kSelWaves entries.
 __device__ __forceinline__ int2 block_exclusive_scan2(int x, int y, int2* total, int2* sh) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  int ix = x, iy = y;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int ux = __shfl_up(ix, off), uy = __shfl_up(iy, off);
-    if (lane >= off) {
-      ix += ux;
-      iy += uy;
-    }
-  }
+  const int ix = wave_inclusive_sum(x), iy = wave_inclusive_sum(y);
   if (lane == kWave - 1) sh[w] = make_int2(ix, iy);
   __syncthreads();
-  if (w == 0) {
-    const int2 v = lane < kSelWaves ? sh[lane] : make_int2(0, 0);
-    int vx = v.x, vy = v.y;
+  int bx = 0, by = 0, tx = 0, ty = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int ux = __shfl_up(vx, off), uy = __shfl_up(vy, off);
-      if (lane >= off) {
-        vx += ux;
-        vy += uy;
-      }
-    }
-    if (lane < kSelWaves) sh[lane] = make_int2(vx - v.x, vy - v.y);
-    if (lane == kSelWaves - 1) sh[kSelWaves] = make_int2(vx, vy);
+  for (int i = 0; i < kSelWaves; ++i) {
+    const int2 v = sh[i];
+    bx += i < w ? v.x : 0;
+    by += i < w ? v.y : 0;
+    tx += v.x;
+    ty += v.y;
   }
-  __syncthreads();
-  const int2 base = sh[w];
-  *total = sh[kSelWaves];
-  return make_int2(base.x + ix - x, base.y + iy - y);
+  *total = make_int2(tx, ty);
+  return make_int2(bx + ix - x, by + iy - y);
 }
 
 // Among the bins of this pass (histogram `hist`, nb bins), find the digit holding
@@ -324,7 +301,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   int2 tot;
   const int2 ex = block_exclusive_scan2(n_gt, n_eq, &tot, scan2_sh);
   int eqi = ex.y;
-  int pos = ex.x + min(ex.y, remaining);
+  int pos = ex.x + max(0, min(ex.y, remaining));
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     if (v < nv) {
