@@ -9,14 +9,14 @@ What it computes, with the passages it follows (SFI page =
 thelatestinai.com/papers/2603.12038, "Slow-Fast Inference: Training-Free
 Inference Acceleration via Within-Sentence Support Stability"):
 
-* ``dense_attention``  - the slow step "performs dense attention" (SFI page,
+* ``dense_attention``  - the slow step attends densely over the whole context (SFI page,
   Fig. 2 caption), plain softmax attention over every visible key; with
   ``t_q > 1`` it is the full-context causal verification of draft tokens
   (SparseSpec-L abstract, page 1 and page 3).
 * ``group_scores``     - the masked attention logits the slow step collects over
   the allowed candidate set (SFI page, Fig. 2 caption), one row per KV head,
   summed over the query heads (and query tokens) that share that KV head
-  ("per-head attention statistics", SparseSpec-L abstract).
+  (the per-head attention statistics of the SparseSpec-L abstract).
 * ``select_topk``      - the Selector that refreshes the selected memory from
   those logits (SFI page, Abstract and Fig. 2): exact top-k, lowest index wins
   ties, output in ascending position order.
@@ -25,8 +25,14 @@ Inference Acceleration via Within-Sentence Support Stability"):
 * ``sparse_decode``    - the fast step: attention over the managed sparse state
   sink + selected + recent (Fig. 2), with sink and selected read from the
   compact buffer and recent read in place from paged KV (Fig. 3B).
+* ``indexed_decode``   - the fast step with sink, selected and recent rows all read
+  in place from paged KV through the block table (attention restricted to an index
+  set).
+* ``draft_refresh_loop`` - draft steps of a layer stack whose designated layer
+  attends densely and refreshes the selected set every step (ASPIRE abstract,
+  page 1: intra-draft refresh layer).
 * ``mixed``            - drafting and verifying requests in one batched call
-  (ASPIRE abstract, page 1: "unified mixed forward").
+  (ASPIRE abstract, page 1: one mixed forward pass for both kinds).
 
 The pages print no worked example, so no value here is pinned to a number on
 the pages; every function is pinned instead by closed forms, library routines,
@@ -45,4 +51,6 @@ from .sfi_oracle import (  # noqa: F401
     mixed,
     refresh_loop,
     append_token,
+    indexed_decode,
+    draft_refresh_loop,
 )

@@ -125,8 +125,8 @@ def group_scores(q: np.ndarray, k_pool: np.ndarray, block_table_row: np.ndarray,
                  page_size: int = 16) -> np.ndarray:
     """Masked logits handed to the Selector, one row per KV head.
 
-    SFI page, Fig. 2 caption: the slow step "collects masked attention logits
-    over the allowed candidate set".  Row g holds, for each candidate position
+    SFI page, Fig. 2 caption: the slow step gathers the attention logits of the
+    candidate set, masked elsewhere.  Row g holds, for each candidate position
     j, the logits scale * q . k_j summed over every query head of group g and
     every query token of the call (per-head statistics of verification,
     SparseSpec-L abstract); positions outside the candidate set hold -inf.
@@ -230,6 +230,77 @@ def sparse_decode(q: np.ndarray, ck: np.ndarray, cv: np.ndarray, n_compact: int,
         out[g * G:(g + 1) * G] = o
         lse[g * G:(g + 1) * G] = l
     return out, lse
+
+
+def _valid_page(block_table_row: np.ndarray, pos: int, num_pages: int, page_size: int) -> bool:
+    e = int(block_table_row[pos // page_size])
+    return 0 <= e < num_pages
+
+
+def indexed_decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.ndarray, L: int,
+                   n_sink: int, n_recent: int, sel: np.ndarray, scale: float, kv_dtype: str = "f32",
+                   page_size: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """Fast step over sink + selected + recent with every row read in place from paged KV
+    (attention restricted to an index set; SFI page, Fig. 2 for the three parts).  For KV
+    head g the attended positions are, in this order: [0, min(n_sink, L)), the entries of
+    sel[g] that lie in [0, L) (negative entries are padding), then the recent range.  A
+    position behind an invalid block-table entry is skipped.  q: [Hq, d] values;
+    sel: [Hkv, k].  Returns out [Hq, d] and lse [Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    num_pages = k_pool.shape[0]
+    rs, re = recent_range(L, n_sink, n_recent)
+    out = np.empty((Hq, d))
+    lse = np.empty(Hq)
+    for g in range(Hkv):
+        chosen = [int(s) for s in np.asarray(sel[g]) if 0 <= int(s) < L]
+        pos = list(range(min(n_sink, L))) + chosen + list(range(rs, re))
+        pos = np.asarray([p for p in pos if _valid_page(block_table_row, p, num_pages, page_size)], dtype=np.int64)
+        K = _widen(paged_rows(k_pool, block_table_row, g, pos, page_size), kv_dtype)
+        V = _widen(paged_rows(v_pool, block_table_row, g, pos, page_size), kv_dtype)
+        o, l = softmax_attention(q[g * G:(g + 1) * G], K, V, scale)
+        out[g * G:(g + 1) * G] = o
+        lse[g * G:(g + 1) * G] = l
+    return out, lse
+
+
+def draft_refresh_loop(q_steps: np.ndarray, pools: Sequence[Tuple[np.ndarray, np.ndarray]],
+                       block_table_row: np.ndarray, L0: int, n_sink: int, n_recent: int, k: int, refresh_layer: int,
+                       sel0: np.ndarray, scale: float, kv_dtype: str = "f32", scores_at=None):
+    """Draft steps of a stack of layers with an intra-draft refresh layer (ASPIRE
+    abstract, page 1: full attention at one designated layer during drafting refreshes
+    the sparse context at every draft step).  Reading: the designated layer attends
+    densely and its masked group logits give, through the Selector, the selected set
+    that every other layer attends over (sink + selected + recent, read in place);
+    layers before the designated one use the previous step's set, layers after it the
+    new one.  Step t decodes position L0 + t (length L0 + t + 1), whose K/V is in the pools.
+
+    q_steps: [T, n_layers, Hq, d] values; pools[l] = (k_pool, v_pool); sel0: [Hkv, k],
+    the set before the first step.  scores_at(t), when given, supplies step t's logits
+    [Hkv, n] (the device's own, so selections can be compared bit for bit).
+    Returns per step a list over layers of (out [Hq, d], lse [Hq]) and the selection
+    [Hkv, k] made at that step."""
+    sel = np.array(sel0, dtype=np.int64, copy=True)
+    Hkv = pools[0][0].shape[1]
+    res = []
+    for t in range(q_steps.shape[0]):
+        L = L0 + t + 1
+        outs = []
+        for layer, (kp, vp) in enumerate(pools):
+            q = q_steps[t, layer]
+            if layer == refresh_layer:
+                o, l = dense_attention(q[None], kp, vp, block_table_row, L, scale, Hkv, kv_dtype=kv_dtype)
+                outs.append((o[0], l[0]))
+                S = scores_at(t) if scores_at is not None else \
+                    group_scores(q[None], kp, block_table_row, L, scale, Hkv, n_sink, n_recent, L, kv_dtype=kv_dtype)
+                lo, hi = candidate_range(L, 1, n_sink, n_recent)
+                sel = np.stack([select_topk(S[g], lo, hi, k) for g in range(Hkv)])
+            else:
+                outs.append(indexed_decode(q, kp, vp, block_table_row, L, n_sink, n_recent, sel, scale, kv_dtype))
+        res.append((outs, sel.copy()))
+    return res
 
 
 # --------------------------------------------------------------------------- mixed draft / verify

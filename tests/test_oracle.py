@@ -435,6 +435,129 @@ def test_refresh_loop_selects_the_current_support_after_a_refresh():
             assert set(dc.support[t // dc.period, 0, g].tolist()) <= set(sel[g].tolist()), (t, g)
 
 
+# --------------------------------------------------------------------------- indexed fast step, draft refresh
+
+def _positions_sdpa(q_rows, pool_k, pool_v, bt_row, L, g, pos, scale):
+    """SDPA over the scatter-built logical rows at an explicit position list."""
+    Kl = _logical(pool_k, bt_row, L, g)[pos]
+    Vl = _logical(pool_v, bt_row, L, g)[pos]
+    return _sdpa(q_rows, Kl, Vl, scale)
+
+
+def test_indexed_decode_over_every_candidate_is_dense_attention():
+    c = make_case(51, name="ix", B=1, Hq=4, Hkv=2, d=64, dtype="f32", seq_lens=[333], n_sink=4, n_recent=16, k_sel=8)
+    L, bt = 333, c.kv.block_table[0]
+    lo, hi = O.candidate_range(L, 1, 4, 16)
+    sel = np.stack([np.arange(lo, hi)] * 2).astype(np.int32)
+    q = c.q_values()[0, 0]
+    out, _ = O.indexed_decode(q, c.kv.k, c.kv.v, bt, L, 4, 16, sel, c.scale)
+    for g in range(2):
+        ref = _positions_sdpa(q[2 * g:2 * g + 2], c.kv.k, c.kv.v, bt, L, g, np.arange(L), c.scale)
+        np.testing.assert_allclose(out[2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
+
+
+def test_indexed_decode_skips_padding_out_of_range_entries_and_invalid_pages():
+    c = make_case(52, name="ix", B=1, Hq=4, Hkv=2, d=64, dtype="f32", seq_lens=[400], capacity=[480], n_sink=4,
+                  n_recent=16, k_sel=8)
+    L = 400
+    bt = c.kv.block_table[0].copy()
+    bt[10] = -1                                    # positions 160..175 unusable
+    sel = np.array([[7, 165, 200, 450, -1, -1], [12, 40, 399 + 30, 300, -1, 171]], np.int32)
+    q = c.q_values()[0, 0]
+    out, _ = O.indexed_decode(q, c.kv.k, c.kv.v, bt, L, 4, 16, sel, c.scale)
+    kept = {0: [7, 200], 1: [12, 40, 300]}         # 165 / 171 sit on the dropped page, 450 / 429 are past L
+    for g in range(2):
+        pos = np.array([0, 1, 2, 3] + kept[g] + list(range(384, 400)))
+        ref = _positions_sdpa(q[2 * g:2 * g + 2], c.kv.k, c.kv.v, bt, L, g, pos, c.scale)
+        np.testing.assert_allclose(out[2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
+
+
+def test_indexed_decode_equals_pack_then_compact_fast_step():
+    c = make_case(53, name="ix", B=1, Hq=8, Hkv=2, d=64, dtype="bf16", seq_lens=[900], n_sink=4, n_recent=32,
+                  k_sel=40)
+    L, bt = 900, c.kv.block_table[0]
+    rng = np.random.default_rng(5)
+    sel = np.stack([np.sort(rng.choice(np.arange(4, 868), 40, replace=False)) for _ in range(2)]).astype(np.int32)
+    q = c.q_values()[0, 0]
+    a, la = O.indexed_decode(q, c.kv.k, c.kv.v, bt, L, 4, 32, sel, c.scale, kv_dtype="bf16")
+    ck, cv, n_c = O.pack_compact(c.kv.k, c.kv.v, bt, L, 4, sel, 44)
+    b, lb = O.sparse_decode(q, ck, cv, n_c, c.kv.k, c.kv.v, bt, L, 4, 32, c.scale, kv_dtype="bf16")
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-13)
+
+
+def _layers(c, n, seed):
+    rng = np.random.default_rng(seed)
+    pools = [(c.kv.k, c.kv.v)]
+    for _ in range(n - 1):
+        pools.append((rng.standard_normal(c.kv.k.shape).astype(np.float32),
+                      rng.standard_normal(c.kv.v.shape).astype(np.float32)))
+    return pools
+
+
+def test_draft_refresh_layer_attends_densely_and_selects_its_top_k():
+    c = make_case(54, name="dr", B=1, Hq=4, Hkv=2, d=32, dtype="f32", seq_lens=[300], capacity=[310], n_sink=4,
+                  n_recent=16, k_sel=12)
+    bt, L0, k = c.kv.block_table[0], 299, 12
+    pools = _layers(c, 3, 1)
+    q = np.random.default_rng(2).standard_normal((3, 3, 4, 32))
+    sel0 = np.full((2, k), -1, np.int32)
+    res = O.draft_refresh_loop(q, pools, bt, L0, 4, 16, k, 1, sel0, c.scale)
+    for t, (outs, sel) in enumerate(res):
+        L = L0 + t + 1
+        kp, vp = pools[1]
+        for g in range(2):
+            Kl = _logical(kp, bt, L, g)
+            ref = _sdpa(q[t, 1, 2 * g:2 * g + 2], Kl, _logical(vp, bt, L, g), c.scale)
+            np.testing.assert_allclose(outs[1][0][2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
+            # brute force: group-summed logits over the candidates, best k by (score desc, position asc)
+            cand = range(4, L - 16)
+            sc = {j: sum(float(q[t, 1, h] @ Kl[j]) for h in (2 * g, 2 * g + 1)) for j in cand}
+            best = sorted(cand, key=lambda j: (-sc[j], j))[:k]
+            assert sel[g].tolist() == sorted(best), (t, g)
+
+
+def test_draft_refresh_layers_before_the_refresh_layer_use_the_previous_set():
+    c = make_case(55, name="dr", B=1, Hq=4, Hkv=2, d=32, dtype="f32", seq_lens=[300], capacity=[310], n_sink=4,
+                  n_recent=16, k_sel=10)
+    bt, L0, k = c.kv.block_table[0], 299, 10
+    pools = _layers(c, 3, 3)
+    q = np.random.default_rng(4).standard_normal((4, 3, 4, 32))
+    sel0 = np.stack([np.arange(4, 14), np.arange(20, 30)]).astype(np.int32)
+    res = O.draft_refresh_loop(q, pools, bt, L0, 4, 16, k, 1, sel0, c.scale)
+    prev = sel0
+    for t, (outs, sel) in enumerate(res):
+        L = L0 + t + 1
+        assert not np.array_equal(prev, sel)       # the set moves, so the two layers see different sets
+        for layer, use in ((0, prev), (2, sel)):
+            kp, vp = pools[layer]
+            for g in range(2):
+                pos = np.array(list(range(4)) + use[g].tolist() + list(range(L - 16, L)))
+                ref = _positions_sdpa(q[t, layer, 2 * g:2 * g + 2], kp, vp, bt, L, g, pos, c.scale)
+                np.testing.assert_allclose(outs[layer][0][2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
+        prev = sel
+
+
+def test_draft_refresh_at_full_retention():
+    """k covers every candidate: a layer after the refresh layer is dense attention; a layer
+    before it misses exactly the position that left the recent window since the last refresh."""
+    c = make_case(56, name="dr", B=1, Hq=4, Hkv=2, d=32, dtype="f32", seq_lens=[200], capacity=[210], n_sink=4,
+                  n_recent=16, k_sel=8)
+    bt, L0 = c.kv.block_table[0], 199
+    pools = _layers(c, 3, 5)
+    q = np.random.default_rng(6).standard_normal((3, 3, 4, 32))
+    k = 200
+    sel0 = np.stack([np.r_[np.arange(4, 183), -np.ones(21, int)]] * 2).astype(np.int32)   # the candidates at L = 199
+    res = O.draft_refresh_loop(q, pools, bt, L0, 4, 16, k, 1, sel0, c.scale)
+    for t, (outs, _) in enumerate(res):
+        L = L0 + t + 1
+        for layer, pos in ((2, np.arange(L)), (0, np.setdiff1d(np.arange(L), [L - 17]))):
+            kp, vp = pools[layer]
+            for g in range(2):
+                ref = _positions_sdpa(q[t, layer, 2 * g:2 * g + 2], kp, vp, bt, L, g, pos, c.scale)
+                np.testing.assert_allclose(outs[layer][0][2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
+
+
 def test_oracle_is_independent_of_the_product():
     here = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle")
     for fn in os.listdir(here):
