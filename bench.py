@@ -270,6 +270,8 @@ def main():
         result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
         log("fused KV append + fast step")
         result["append_fast"] = append_fast(sfi, dev, main_s)
+        log("draft steps with an intra-draft refresh layer")
+        result["draft_refresh"] = draft_refresh_c3(sfi, dev)
         log("refresh schedule on drifting support")
         result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
         log("128K speculative mix")
@@ -538,6 +540,104 @@ def refresh_schedule_c3(sfi, dev, steps=64, period=16):
             "recall_by_steps_since_refresh": {str(a): round(float(np.mean(by_age[a])), 4) for a in ages}}
         del sched
     log(f"refresh schedule {res}")
+    return res
+
+
+def draft_refresh_c3(sfi, dev, n_layers=8, reps=40):
+    """Draft steps of an 8-layer stack at the batched decode shape (16 requests, 32 query / 8 KV heads,
+    lengths uniform in [16K, 32K], sink 4, selected 1024, recent 256) with an intra-draft refresh layer
+    (ASPIRE abstract): layer 0 runs dense attention + logits + Selector at every draft step and the other
+    layers attend over sink + the new set + recent.  Per draft step of the batch:
+      indexed: the other layers read the set in place (sfi_sparse_decode_indexed_attn; DraftRefresh);
+      pack:    each other layer packs the set into its compact buffer, then runs the compact fast step;
+      stale:   no refresh layer, every layer a compact fast step over a fixed set;
+      dense:   every layer dense attention (the autoregressive step).
+    Also the refresh chain alone and one fast layer of each kind.  Data drawn on the GPU (seeded)."""
+    import torch
+    from sparse_kv_cache_sfi_amd.schedule import DraftRefresh
+    B, Hq, Hkv, d, n_sink, n_recent, k = 16, 32, 8, 128, 4, 256, 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    L = torch.randint(16384, 32769, (B,), generator=gen, device=dev).cpu()
+    pages = (L + 15) // 16
+    num_pages, max_pages = int(pages.sum()), int(pages.max())
+    perm = torch.randperm(num_pages, generator=gen, device=dev).to(torch.int32)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32, device=dev)
+    off = 0
+    for b in range(B):
+        bt[b, :int(pages[b])] = perm[off:off + int(pages[b])]
+        off += int(pages[b])
+    pools = [(torch.randn((num_pages, Hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16),
+              torch.randn((num_pages, Hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+             for _ in range(n_layers)]
+    q = torch.randn((n_layers, B, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    lens = L.to(torch.int32).to(dev)
+    max_len = max_pages * 16
+    stream = torch.cuda.current_stream(dev)
+    drv = DraftRefresh(pools, bt, q, lens, max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, k=k,
+                       refresh_layer=0, stream=stream)
+    drv.step()                                   # a first refresh: the set every variant starts from
+    torch.cuda.synchronize()
+    cap = n_sink + k
+    ws_d = torch.zeros(sfi.workspace_size("dense", k_pool=pools[0][0], block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                          max_seq_len=max_len) + 16, dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(sfi.workspace_size("sparse", k_pool=pools[0][0], block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                          max_seq_len=max_len, cap=cap, n_recent=n_recent) + 16,
+                       dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, d), **f32)
+    lse = torch.empty((B, Hq), **f32)
+    out4, lse3 = out.view(B, 1, Hq, d), lse.view(B, 1, Hq)
+    scores = torch.empty((B, Hkv, max_len), **f32)
+    sel = drv.sel.clone()
+    comp = [(torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev),
+             torch.empty((B,), dtype=torch.int32, device=dev)) for _ in range(n_layers)]
+    dense, fast, pack, indexed = [], [], [], []
+    for l, (kp, vp) in enumerate(pools):
+        ck, cv, nc = comp[l]
+        dense.append(sfi.bind(sfi.dense_attn_with_stats, q[l].view(B, 1, Hq, d), kp, vp, bt, lens,
+                              max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, out=out4, lse=lse3,
+                              scores=scores, workspace=ws_d, stream=stream))
+        pack.append(sfi.bind(sfi.pack_compact, kp, vp, bt, lens, sel, n_sink=n_sink, cap=cap, max_seq_len=max_len,
+                             compact_k=ck, compact_v=cv, n_compact=nc, stream=stream))
+        fast.append(sfi.bind(sfi.sparse_decode_attn, q[l], kp, vp, bt, lens, ck, cv, nc, n_sink=n_sink,
+                             n_recent=n_recent, max_seq_len=max_len, out=out, lse=lse, workspace=ws_s, stream=stream))
+        indexed.append(sfi.bind(sfi.sparse_decode_indexed_attn, q[l], kp, vp, bt, lens, sel, n_sink=n_sink,
+                                n_recent=n_recent, max_seq_len=max_len, out=out, lse=lse, workspace=ws_s,
+                                stream=stream))
+    dense_plain = [sfi.bind(sfi.dense_attn_with_stats, q[l].view(B, 1, Hq, d), kp, vp, bt, lens, max_seq_len=max_len,
+                            with_scores=False, out=out4, lse=lse3, workspace=ws_d, stream=stream)
+                   for l, (kp, vp) in enumerate(pools)]
+    select = sfi.bind(sfi.select_topk, scores, lens, k=k, n_sink=n_sink, n_recent=n_recent, sel_idx=sel,
+                      stream=stream)
+    for c in pack:
+        c()
+
+    def run(calls):
+        def f(i):
+            for c in calls:
+                c()
+        return f
+    steps = {
+        "indexed": lambda i: drv.step(),
+        "pack": run([dense[0], select] + [c for l in range(1, n_layers) for c in (pack[l], fast[l])]),
+        "stale": run(fast),
+        "dense": run(dense_plain),
+        "refresh_chain": run([dense[0], select]),
+        "fast_layer_indexed": run([indexed[1]]),
+        "fast_layer_compact": run([fast[1]]),
+        "pack_layer": run([pack[1]]),
+    }
+    res = {"requests": B, "kv_len_range": [16384, 32768], "layers": n_layers, "refresh_layer": 0, "selected": k,
+           "recent": n_recent, "kv_tokens": int(L.sum())}
+    for name, f in steps.items():
+        for i in range(3):
+            f(i)
+        res[name + "_us"] = round(time_loop(f, reps, stream) * 1e6, 1)
+    log(f"draft refresh {res}")
+    del pools, comp
+    torch.cuda.empty_cache()
     return res
 
 

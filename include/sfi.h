@@ -264,6 +264,32 @@ SFI_API sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const s
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fast step over an index set read in place (sink + selected + recent, SFI page,
+ * Fig. 2; the selected set shared by the layers of a draft step that an intra-draft
+ * refresh layer refreshes, ASPIRE abstract).  Every row is read from paged KV through
+ * the block table, so no compact buffer is packed.  For request b and KV head g the
+ * attended positions are, in order: [0, min(n_sink, L_b)), every entry of
+ * sel_idx[b, g, 0:k] that lies in [0, L_b) (negative entries are padding), then
+ * [max(n_sink, L_b - n_recent), L_b).  A position behind an invalid block-table
+ * entry is skipped.  With the entries of sel_idx valid, the result equals
+ * sfi_pack_compact followed by sfi_sparse_decode_attn bit for bit.
+ *
+ *   sel_idx  int32 [B, Hkv, k], device, e.g. the output of sfi_select_topk; k >= 0
+ *            (sel_idx may be NULL when k is 0).
+ *   k_new, v_new  both NULL, or the decoded token's K/V [B, Hkv, d] (16-byte aligned)
+ *            stored and attended as in sfi_sparse_decode_append_attn.
+ *   workspace  as sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent).
+ *   Other arguments as sfi_sparse_decode_attn.  Errors: SFI_ERR_INVALID_ARG for a
+ *   NULL sel_idx with k > 0, negative k or an unpaired k_new / v_new; SFI_ERR_UNSUPPORTED when
+ *   num_pages * 16 exceeds INT32_MAX.
+ */
+SFI_API sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                          const void* k_new, const void* v_new, const int32_t* seq_lens,
+                                          int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
+                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
  * Drafting and verifying requests in one launch (ASPIRE abstract: a unified
  * mixed forward lets drafting and verifying requests share one batched
  * pass; SparseSpec-L abstract: drafts attend over a sparse, recallable KV

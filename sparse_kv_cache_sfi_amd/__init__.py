@@ -76,6 +76,8 @@ _SIGS = {
     "sfi_sparse_decode_append_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p],
+    "sfi_sparse_decode_indexed_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_mixed_attn": [_SHAPE_P, _KV_P, c_void_p, POINTER(c_int32), POINTER(c_int32), c_void_p, c_int32,
                        c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                        c_void_p, c_size_t, c_void_p],
@@ -417,6 +419,47 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
               k_new.data_ptr(), v_new.data_ptr(), seq_lens.data_ptr(), n_sink, n_recent, compact_k.data_ptr(),
               compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
               _stream(stream, dev))
+    return out, lse
+
+
+def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                               block_table: torch.Tensor, seq_lens: torch.Tensor, sel_idx: torch.Tensor, *,
+                               n_sink: int, n_recent: int, max_seq_len: int, scale: Optional[float] = None,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None,
+                               k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None):
+    """Fast step over the positions sel_idx [B, Hkv, k] lists (plus sink and recent), every row
+    read in place from paged KV: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq])
+    (sfi_sparse_decode_indexed_attn).  k_new / v_new as in sparse_decode_attn."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    _i32(sel_idx, "sel_idx")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, n)
+            if t.dtype != k_pool.dtype or tuple(t.shape) != (q.shape[0], k_pool.shape[1], q.shape[2]):
+                raise ValueError(f"{n} must be [B, Hkv, d] in the pool dtype")
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("sel_idx must be [B, Hkv, k]")
+    k = sel_idx.shape[2]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = c_size_t(0)
+    _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), n_sink + k, n_recent,
+          ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_sparse_decode_indexed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), _ptr(k_new),
+          _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, out.data_ptr(), _ptr(lse),
+          _ptr(ws), _nbytes(ws), _stream(stream, dev))
     return out, lse
 
 

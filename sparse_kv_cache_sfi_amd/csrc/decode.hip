@@ -4,16 +4,21 @@
 
 namespace sfi {
 
-template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false>
+template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false, bool INDEXED = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[DecodeShape<T, D, G>::SMEM];
-  decode_unit<T, D, G, SPARSE, SCORES, APPEND>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z, smem);
+  using S = DecodeShape<T, D, G>;
+  __shared__ __attribute__((aligned(16))) char smem[INDEXED ? S::SMEM_IDX : S::SMEM];
+  decode_unit<T, D, G, SPARSE, SCORES, APPEND, INDEXED>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z, smem);
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const AttnArgs& a, bool sparse, int B, hipStream_t stream) {
   const dim3 grid(a.n_split, a.Hkv, B), block(256);
-  if (sparse && a.k_new)
+  if (sparse && a.sel_k >= 0 && a.k_new)
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, true, true>), grid, block, 0, stream, a);
+  else if (sparse && a.sel_k >= 0)
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, false, true>), grid, block, 0, stream, a);
+  else if (sparse && a.k_new)
     hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, true>), grid, block, 0, stream, a);
   else if (sparse)
     hipLaunchKernelGGL((decode_kernel<T, D, G, true, false>), grid, block, 0, stream, a);

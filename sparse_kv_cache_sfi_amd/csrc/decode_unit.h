@@ -53,6 +53,10 @@ struct DecodeShape {
   static constexpr int TILE = WAVES * U * ROWS;                // tokens per work-group iteration
   static constexpr int TAIL = SplitTail<D>::bytes(G, kMaxSplits);
   static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4 + 16 + TAIL;
+  // The index-set fast step also stages its split's sink and selected rows as page
+  // slots (page * 16 + row, or -1), one int per token.
+  static constexpr int IDX_OFF = (SMEM + 15) / 16 * 16;
+  static constexpr int SMEM_IDX = IDX_OFF + kMaxSplitTokens * 4;
   static_assert(C >= 1, "row too short for the lane mapping");
 };
 
@@ -77,7 +81,7 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
   return acc;
 }
 
-template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false>
+template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false, bool INDEXED = false>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, const int g, const int split,
                                             const int q_row0, char* smem) {
   using S = DecodeShape<T, D, G>;
@@ -92,9 +96,17 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   float* wml = wo + WAVES * G * D;
 
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
-  int n_c = 0, rs = 0;
+  static_assert(!INDEXED || (SPARSE && !SCORES), "the index-set path is a fast step");
+  int n_c = 0, rs = 0, ns = 0;
   if constexpr (SPARSE) {
-    n_c = clampi(a.n_compact[b], 0, a.cap);
+    if constexpr (INDEXED) {
+      // Virtual rows: the sink, then every entry of the selection row (padding and
+      // entries outside [0, L) are masked rows), then the recent tokens.
+      ns = min(a.n_sink, L);
+      n_c = ns + a.sel_k;
+    } else {
+      n_c = clampi(a.n_compact[b], 0, a.cap);
+    }
     rs = min(max(a.n_sink, L - a.n_recent), L);
   }
   const int n_tot = n_c + (L - rs);
@@ -130,13 +142,43 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     const int e = bt_row[pg_lo + i];
     bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
   }
+  int* slot_s = nullptr;
+  if constexpr (INDEXED) {
+    // Resolve the split's sink and selected rows to page slots: first every position
+    // (sink rows are their own index, selected rows come from the selection), then
+    // every block-table entry, so the staging costs two memory round trips.
+    slot_s = reinterpret_cast<int*>(smem + S::IDX_OFF);
+    const int cnt = min(t1, n_c) - t0;
+    const int32_t* sel_row = a.sel + ((int64_t)b * a.Hkv + g) * a.sel_k;
+    constexpr int PER = kMaxSplitTokens / NT;
+    int pos[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * NT;
+      const int vi = t0 + i;
+      pos[j] = -1;
+      if (i < cnt) pos[j] = vi < ns ? vi : sel_row[vi - ns];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * NT;
+      if (i < cnt) {
+        int sl = -1;
+        if (pos[j] >= 0 && pos[j] < L) {
+          const int e = bt_row[pos[j] >> 4];
+          if (e >= 0 && e < a.num_pages) sl = e * kPage + (pos[j] & 15);
+        }
+        slot_s[i] = sl;
+      }
+    }
+  }
   __syncthreads();
 
   const T* kpool = reinterpret_cast<const T*>(a.k_pool);
   const T* vpool = reinterpret_cast<const T*>(a.v_pool);
   const T* ckb = kpool;
   const T* cvb = vpool;
-  if constexpr (SPARSE) {
+  if constexpr (SPARSE && !INDEXED) {
     const int64_t base = ((int64_t)b * a.Hkv + g) * a.cap * D;
     ckb = reinterpret_cast<const T*>(a.ck) + base;
     cvb = reinterpret_cast<const T*>(a.cv) + base;
@@ -191,6 +233,16 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     vi = t0 + it * TILE + (w * U + u) * ROWS + r;
     in = vi < t1;
     compact = SPARSE && vi < n_c;
+    if constexpr (INDEXED) {
+      if (compact) {
+        // an index-set row: its page slot was staged (p & 15 is the row in the page)
+        const int sl = in ? slot_s[vi - t0] : -1;
+        p = sl;
+        pg = sl >> 4;
+        ok = in && sl >= 0;
+        return;
+      }
+    }
     p = compact ? vi : rs + vi - n_c;
     const int slot = in && !compact ? (p >> 4) - pg_lo : 0;
     pg = bt_s[slot];
@@ -210,7 +262,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       off = ok ? off : 0;
       const T* kr = kpool + off;
       const T* vr = vpool + off;
-      if constexpr (SPARSE) {
+      if constexpr (SPARSE && !INDEXED) {
         if (compact) {
           kr = ckb + (int64_t)vi * D;
           vr = cvb + (int64_t)vi * D;

@@ -63,6 +63,11 @@ struct AttnArgs {
   // ([B, Hkv, d], pool dtype); the launch writes it into its page and attends to it.
   const void* k_new;
   const void* v_new;
+  // Fast step over an index set (sel_k >= 0; -1 otherwise): sel [B, Hkv, sel_k]
+  // positions whose rows are read in place through the block table instead of from
+  // compact buffers (sel may be NULL when sel_k is 0).
+  const int32_t* sel;
+  int32_t sel_k;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves

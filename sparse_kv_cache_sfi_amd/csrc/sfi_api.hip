@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <string>
 
@@ -153,6 +155,7 @@ sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_
   a.seq_lens = seq_lens;
   a.scale = s->scale;
   a.scale_log2 = s->scale * sfi::kLog2e;
+  a.sel_k = -1;   // not an index-set call
   return a;
 }
 
@@ -462,18 +465,28 @@ sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_pa
 
 namespace {
 
+// The fast step.  Sink and selected rows come from compact buffers, or, when sel_k is
+// >= 0, from paged KV at the positions sel lists (cap is then n_sink + sel_k).
 sfi_status sparse_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, const void* k_new,
                        const void* v_new, const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
                        const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
-                       float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                       const int32_t* sel, int32_t sel_k, float* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
   SFI_TRY(check_ptr16(q, "q"));
   SFI_TRY(check_ptr16(out, "out"));
-  SFI_TRY(check_ptr16(compact_k, "compact_k"));
-  SFI_TRY(check_ptr16(compact_v, "compact_v"));
-  if (!seq_lens || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens and n_compact must be non-NULL");
+  if (!seq_lens) return fail(SFI_ERR_INVALID_ARG, "seq_lens is NULL");
   SFI_TRY(check_budgets(n_sink, n_recent));
+  if (sel_k >= 0) {
+    if ((int64_t)kv->num_pages * sfi::kPage > INT32_MAX)
+      return fail(SFI_ERR_UNSUPPORTED, "num_pages (%d) too large for 32-bit page slots", kv->num_pages);
+    cap = (int32_t)std::min<int64_t>((int64_t)n_sink + sel_k, INT32_MAX);
+  } else {
+    SFI_TRY(check_ptr16(compact_k, "compact_k"));
+    SFI_TRY(check_ptr16(compact_v, "compact_v"));
+    if (!n_compact) return fail(SFI_ERR_INVALID_ARG, "n_compact is NULL");
+  }
   if (cap < 1) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1");
   if ((int64_t)cap + n_recent > kMaxTokens)
     return fail(SFI_ERR_UNSUPPORTED, "cap + n_recent exceeds %lld tokens", (long long)kMaxTokens);
@@ -499,6 +512,8 @@ sfi_status sparse_call(const sfi_shape* shape, const sfi_paged_kv* kv, const voi
   a.lse = lse;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.sel = sel;
+  a.sel_k = sel_k;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
@@ -515,7 +530,7 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
                                   const void* compact_v, int32_t cap, const int32_t* n_compact, float* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_call(shape, kv, q, nullptr, nullptr, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
-                     n_compact, out, lse, workspace, workspace_bytes, stream);
+                     n_compact, nullptr, -1, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
@@ -526,7 +541,23 @@ sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged
   SFI_TRY(check_ptr16(k_new, "k_new"));
   SFI_TRY(check_ptr16(v_new, "v_new"));
   return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
-                     n_compact, out, lse, workspace, workspace_bytes, stream);
+                     n_compact, nullptr, -1, out, lse, workspace, workspace_bytes, stream);
+}
+
+sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                          const void* k_new, const void* v_new, const int32_t* seq_lens,
+                                          int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
+                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (k < 0) return fail(SFI_ERR_INVALID_ARG, "k must be >= 0");
+  if (!sel_idx && k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
+  if (!k_new != !v_new) return fail(SFI_ERR_INVALID_ARG, "k_new and v_new must both be NULL or both be set");
+  if (k_new) {
+    SFI_TRY(check_ptr16(k_new, "k_new"));
+    SFI_TRY(check_ptr16(v_new, "v_new"));
+  }
+  return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, nullptr, nullptr, 0, nullptr, sel_idx,
+                     k, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

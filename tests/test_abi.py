@@ -30,7 +30,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
-              "sfi_mixed_attn", "sfi_dense_attn_with_refresh", "sfi_sparse_decode_append_attn"):
+              "sfi_mixed_attn", "sfi_dense_attn_with_refresh", "sfi_sparse_decode_append_attn",
+              "sfi_sparse_decode_indexed_attn"):
         assert n in names
 
 
@@ -177,6 +178,23 @@ def test_sparse_append_rejects_bad_arguments(lib):
     assert call(kn=MISALIGNED) == 1 and "aligned" in lib.sfi_last_error().decode()
     assert call(q=MISALIGNED) == 1
     assert call(ws_bytes=1) == 3
+
+
+def test_sparse_indexed_rejects_bad_arguments(lib):
+    shape = _shape()
+
+    def call(sel=FAKE, k=64, kn=None, vn=None, q=FAKE, ws_bytes=1 << 40, kv=None, out=FAKE):
+        kv = kv or _kv()
+        return lib.sfi_sparse_decode_indexed_attn(ctypes.byref(shape), ctypes.byref(kv), q, kn, vn, FAKE, 4, 64, sel,
+                                                  k, out, FAKE, FAKE, ws_bytes, None)
+    assert call(sel=0) == 1 and "sel_idx is NULL" in lib.sfi_last_error().decode()
+    assert call(k=-1) == 1 and "k must be" in lib.sfi_last_error().decode()
+    assert call(kn=FAKE) == 1 and "both" in lib.sfi_last_error().decode()
+    assert call(kn=MISALIGNED, vn=FAKE) == 1 and "aligned" in lib.sfi_last_error().decode()
+    assert call(q=MISALIGNED) == 1
+    assert call(out=0) == 1
+    assert call(k=20000, ws_bytes=1) == 3          # several splits: partials needed
+    assert call(kv=_kv(num_pages=1 << 27)) == 2 and "slots" in lib.sfi_last_error().decode()
 
 
 def test_workspace_queries_match_the_plan(lib):
