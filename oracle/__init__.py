@@ -28,6 +28,9 @@ Inference Acceleration via Within-Sentence Support Stability"):
 * ``indexed_decode``   - the fast step with sink, selected and recent rows all read
   in place from paged KV through the block table (attention restricted to an index
   set).
+* ``head_scores`` / ``indexed_decode_heads`` - per-query-head selection: the
+  slow step's logits kept per query head, and the fast step with one set per query
+  head (the per-head statistics of the SparseSpec-L abstract, not summed).
 * ``draft_refresh_loop`` - draft steps of a layer stack whose designated layer
   attends densely and refreshes the selected set every step (ASPIRE abstract,
   page 1: intra-draft refresh layer).
@@ -52,5 +55,7 @@ from .sfi_oracle import (  # noqa: F401
     refresh_loop,
     append_token,
     indexed_decode,
+    head_scores,
+    indexed_decode_heads,
     draft_refresh_loop,
 )

@@ -266,6 +266,53 @@ def indexed_decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_
     return out, lse
 
 
+def head_scores(q: np.ndarray, k_pool: np.ndarray, block_table_row: np.ndarray, L: int, scale: float, Hkv: int,
+                n_sink: int, n_recent: int, stride: int, kv_dtype: str = "f32", page_size: int = 16) -> np.ndarray:
+    """Masked logits kept per query head (the per-head statistics of the SparseSpec-L
+    abstract, not summed over the group): row h holds scale * q_h . k_j for each candidate
+    position j of the slow step (SFI page, Fig. 2) and -inf elsewhere; query head h reads
+    KV head h // G.  q: [Hq, d] values (one query token).  Returns [Hq, stride] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq = q.shape[0]
+    G = Hq // Hkv
+    lo, hi = candidate_range(L, 1, n_sink, n_recent)
+    S = np.full((Hq, stride), -np.inf)
+    if hi <= lo:
+        return S
+    pos = np.arange(lo, hi)
+    for h in range(Hq):
+        K = _widen(paged_rows(k_pool, block_table_row, h // G, pos, page_size), kv_dtype)
+        S[h, lo:hi] = scale * (K @ q[h])
+    return S
+
+
+def indexed_decode_heads(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.ndarray,
+                         L: int, n_sink: int, n_recent: int, sel: np.ndarray, scale: float, kv_dtype: str = "f32",
+                         page_size: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """Fast step with one selected set per query head: query head h attends over sink +
+    the valid entries of sel[h] + recent of KV head h // G, every row read in place (as
+    indexed_decode, with the set chosen per head).  q: [Hq, d] values; sel: [Hq, k].
+    Returns out [Hq, d] and lse [Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    num_pages = k_pool.shape[0]
+    rs, re = recent_range(L, n_sink, n_recent)
+    out = np.empty((Hq, d))
+    lse = np.empty(Hq)
+    for h in range(Hq):
+        chosen = [int(s) for s in np.asarray(sel[h]) if 0 <= int(s) < L]
+        pos = list(range(min(n_sink, L))) + chosen + list(range(rs, re))
+        pos = np.asarray([p for p in pos if _valid_page(block_table_row, p, num_pages, page_size)], dtype=np.int64)
+        K = _widen(paged_rows(k_pool, block_table_row, h // G, pos, page_size), kv_dtype)
+        V = _widen(paged_rows(v_pool, block_table_row, h // G, pos, page_size), kv_dtype)
+        o, l = softmax_attention(q[h:h + 1], K, V, scale)
+        out[h] = o[0]
+        lse[h] = l[0]
+    return out, lse
+
+
 def draft_refresh_loop(q_steps: np.ndarray, pools: Sequence[Tuple[np.ndarray, np.ndarray]],
                        block_table_row: np.ndarray, L0: int, n_sink: int, n_recent: int, k: int, refresh_layer: int,
                        sel0: np.ndarray, scale: float, kv_dtype: str = "f32", scores_at=None):

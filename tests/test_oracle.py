@@ -558,6 +558,51 @@ def test_draft_refresh_at_full_retention():
                 np.testing.assert_allclose(outs[layer][0][2 * g:2 * g + 2], ref, rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- per-query-head selection
+
+def test_head_scores_are_per_head_dot_products_over_the_candidates():
+    c = make_case(57, name="hs", B=1, Hq=8, Hkv=2, d=32, dtype="bf16", seq_lens=[260], n_sink=4, n_recent=16,
+                  k_sel=8)
+    L, bt = 260, c.kv.block_table[0]
+    q = c.q_values()[0, 0]
+    S = O.head_scores(q, c.kv.k, bt, L, c.scale, 2, 4, 16, 300, kv_dtype="bf16")
+    assert np.all(np.isneginf(S[:, :4])) and np.all(np.isneginf(S[:, 244:]))
+    for h in range(8):
+        Kl = torch.from_numpy(bf16_values(_logical(c.kv.k, bt, L, h // 4)).astype(np.float64))
+        ref = (Kl @ torch.from_numpy(q[h].astype(np.float64))).numpy() * c.scale
+        np.testing.assert_allclose(S[h, 4:244], ref[4:244], rtol=0, atol=1e-12)
+    # their sum over a group is the group's logit row
+    Sg = O.group_scores(q[None], c.kv.k, bt, L, c.scale, 2, 4, 16, 300, kv_dtype="bf16")
+    np.testing.assert_allclose(S.reshape(2, 4, 300).sum(axis=1)[:, 4:244], Sg[:, 4:244], rtol=0, atol=1e-11)
+
+
+def test_per_head_sets_equal_to_the_group_set_give_the_group_fast_step():
+    c = make_case(58, name="hs", B=1, Hq=8, Hkv=2, d=32, dtype="f32", seq_lens=[500], n_sink=4, n_recent=16,
+                  k_sel=20)
+    L, bt = 500, c.kv.block_table[0]
+    rng = np.random.default_rng(9)
+    sel = np.stack([np.sort(rng.choice(np.arange(4, 484), 20, replace=False)) for _ in range(2)]).astype(np.int32)
+    q = c.q_values()[0, 0]
+    a, la = O.indexed_decode_heads(q, c.kv.k, c.kv.v, bt, L, 4, 16, np.repeat(sel, 4, axis=0), c.scale)
+    b, lb = O.indexed_decode(q, c.kv.k, c.kv.v, bt, L, 4, 16, sel, c.scale)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-13)
+
+
+def test_per_head_fast_step_attends_each_heads_own_positions():
+    c = make_case(59, name="hs", B=1, Hq=4, Hkv=1, d=32, dtype="f32", seq_lens=[300], n_sink=4, n_recent=16,
+                  k_sel=6)
+    L, bt = 300, c.kv.block_table[0]
+    rng = np.random.default_rng(10)
+    sel = np.stack([np.r_[np.sort(rng.choice(np.arange(4, 284), 5, replace=False)), -1] for _ in range(4)])
+    q = c.q_values()[0, 0]
+    out, _ = O.indexed_decode_heads(q, c.kv.k, c.kv.v, bt, L, 4, 16, sel.astype(np.int32), c.scale)
+    for h in range(4):
+        pos = np.array([0, 1, 2, 3] + sel[h, :5].tolist() + list(range(284, 300)))
+        ref = _positions_sdpa(q[h:h + 1], c.kv.k, c.kv.v, bt, L, 0, pos, c.scale)
+        np.testing.assert_allclose(out[h:h + 1], ref, rtol=0, atol=1e-12)
+
+
 def test_oracle_is_independent_of_the_product():
     here = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle")
     for fn in os.listdir(here):
