@@ -270,6 +270,8 @@ def main():
         result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
         log("fused KV append + fast step")
         result["append_fast"] = append_fast(sfi, dev, main_s)
+        log("per-query-head selection")
+        result["head_selection"] = head_selection(sfi, dev)
         log("draft steps with an intra-draft refresh layer")
         result["draft_refresh"] = draft_refresh_c3(sfi, dev)
         log("refresh schedule on drifting support")
@@ -637,6 +639,87 @@ def draft_refresh_c3(sfi, dev, n_layers=8, reps=40):
         res[name + "_us"] = round(time_loop(f, reps, stream) * 1e6, 1)
     log(f"draft refresh {res}")
     del pools, comp
+    torch.cuda.empty_cache()
+    return res
+
+
+def head_selection(sfi, dev, reps=100):
+    """Per-query-head selection against the group-summed selection of the pages' design, at 4 requests x
+    16K tokens, 32 query / 8 KV heads (G = 4), sink 4, recent 64.  Every query head has 32 planted keys of
+    its own (0.7 x its query: logits near 8 against N(0, 1) for the rest, about four fifths of its softmax
+    mass), so the heads of a group disagree on what matters.  For each budget: the error
+    of the fast step against the dense output of the same queries (relative L2 per query head, mean and
+    max), and the time of each stage: slow step (group vs per-head logits), Selector (B*Hkv vs B*Hq rows),
+    fast step (shared set vs one set per query head; per head reads G times the selected rows).
+    'per_head_equal_bytes' selects k/G per query head (the group path's KV bytes), 'per_head' k per head."""
+    import torch
+    B, Hq, Hkv, d, L, n_sink, n_recent, hh = 4, 32, 8, 128, 16384, 4, 64, 32
+    G = Hq // Hkv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    npg = B * L // 16
+    kp = torch.randn((npg, Hkv, 16, d), generator=gen, device=dev)
+    vp = torch.randn((npg, Hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16)
+    bt = torch.randperm(npg, generator=gen, device=dev).to(torch.int32).reshape(B, L // 16)
+    qf = torch.randn((B, Hq, d), generator=gen, device=dev)
+    # plant: head h of request b gets hh positions (disjoint across heads) whose key in KV head h // G is 4 q_h
+    for b in range(B):
+        pos = torch.randperm(L - n_recent - n_sink - 16, generator=gen, device=dev)[:Hq * hh] + n_sink
+        for h in range(Hq):
+            p = pos[h * hh:(h + 1) * hh]
+            kp[bt[b, p // 16].long(), h // G, p % 16, :] = 0.7 * qf[b, h]
+    kp = kp.to(torch.bfloat16)
+    q = qf.to(torch.bfloat16)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    ws_d = torch.zeros(sfi.workspace_size("dense", k_pool=kp, block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                          max_seq_len=L) + 16, dtype=torch.uint8, device=dev)
+    out_d, lse_d = torch.empty((B, 1, Hq, d), **f32), torch.empty((B, 1, Hq), **f32)
+    Sg, Sh = torch.empty((B, Hkv, L), **f32), torch.empty((B, Hq, L), **f32)
+    dense_g = sfi.bind(sfi.dense_attn_with_stats, q.view(B, 1, Hq, d), kp, vp, bt, lens, max_seq_len=L,
+                       n_sink=n_sink, n_recent=n_recent, out=out_d, lse=lse_d, scores=Sg, workspace=ws_d,
+                       stream=stream)
+    dense_h = sfi.bind(sfi.dense_attn_with_head_stats, q, kp, vp, bt, lens, max_seq_len=L, n_sink=n_sink,
+                       n_recent=n_recent, out=out_d.view(B, Hq, d), lse=lse_d.view(B, Hq), scores=Sh,
+                       workspace=ws_d, stream=stream)
+    dense_g()
+    dense_h()
+    torch.cuda.synchronize()
+    ref = out_d.view(B, Hq, d).clone()
+    res = {"requests": B, "kv_len": L, "q_heads": Hq, "kv_heads": Hkv, "planted_per_query_head": hh,
+           "slow_step_group_us": round(time_loop(lambda i: dense_g(), reps, stream) * 1e6, 1),
+           "slow_step_per_head_us": round(time_loop(lambda i: dense_h(), reps, stream) * 1e6, 1), "budgets": []}
+
+    def err(o):
+        e = (o - ref).norm(dim=-1) / ref.norm(dim=-1)
+        return round(float(e.mean()), 5), round(float(e.max()), 5)
+    for k in (128, 512, 2048):
+        row = {"k_per_kv_head": k}
+        for name, rows, kk, S in (("group", Hkv, k, Sg), ("per_head_equal_bytes", Hq, k // G, Sh),
+                                  ("per_head", Hq, k, Sh)):
+            sel = torch.empty((B, rows, kk), dtype=torch.int32, device=dev)
+            o, l = torch.empty((B, Hq, d), **f32), torch.empty((B, Hq), **f32)
+            unit = rows
+            ws = torch.zeros(sfi.workspace_size("sparse", k_pool=kp, block_table=bt, Hq=Hq, dtype=torch.bfloat16,
+                                                max_seq_len=L, cap=n_sink + kk, n_recent=n_recent) * (unit // Hkv)
+                             + 16, dtype=torch.uint8, device=dev)
+            sel_c = sfi.bind(sfi.select_topk, S, lens, k=kk, n_sink=n_sink, n_recent=n_recent, sel_idx=sel,
+                             stream=stream)
+            fast_c = sfi.bind(sfi.sparse_decode_indexed_attn, q, kp, vp, bt, lens, sel, n_sink=n_sink,
+                              n_recent=n_recent, max_seq_len=L, out=o, lse=l, workspace=ws, stream=stream,
+                              per_head=rows == Hq)
+            sel_c()
+            fast_c()
+            torch.cuda.synchronize()
+            e_mean, e_max = err(o)
+            row[name] = {"k": kk, "rel_err_mean": e_mean, "rel_err_max": e_max,
+                         "select_us": round(time_loop(lambda i: sel_c(), reps, stream) * 1e6, 1),
+                         "fast_us": round(time_loop(lambda i: fast_c(), reps, stream) * 1e6, 1),
+                         "fast_kv_bytes": B * rows * (n_sink + kk + n_recent) * 2 * d * 2}
+        res["budgets"].append(row)
+    log(f"head selection {res}")
+    del kp, vp
     torch.cuda.empty_cache()
     return res
 

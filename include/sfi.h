@@ -264,6 +264,19 @@ SFI_API sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const s
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Slow step with per-query-head logits (t_q = 1): as sfi_dense_attn_with_stats,
+ * but scores [B, Hq, score_stride] holds one masked logit row per query head,
+ * scale * q_h . k_j, instead of the sum over the group (the per-head attention
+ * statistics of the SparseSpec-L abstract, kept per head).  Feeding its rows to
+ * sfi_select_topk with num_kv_heads = Hq selects per query head.  scores must be
+ * non-NULL; the workspace is sfi_dense_attn_workspace_size(shape, kv, 1).
+ */
+SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                          const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                          float* out, float* lse, float* scores, int64_t score_stride,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fast step over an index set read in place (sink + selected + recent, SFI page,
  * Fig. 2; the selected set shared by the layers of a draft step that an intra-draft
  * refresh layer refreshes, ASPIRE abstract).  Every row is read from paged KV through
@@ -276,18 +289,24 @@ SFI_API sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const s
  *
  *   sel_idx  int32 [B, Hkv, k], device, e.g. the output of sfi_select_topk; k >= 0
  *            (sel_idx may be NULL when k is 0).
+ *   per_head 0: one set per KV head, shared by its query heads.  1: one set per
+ *            query head, sel_idx [B, Hq, k] (per-query-head selection, e.g.
+ *            sfi_select_topk over the rows of sfi_dense_attn_with_head_stats); query
+ *            head h reads KV head h / G at its own positions.  The workspace is then
+ *            sized by the same query with num_kv_heads set to num_q_heads.
  *   k_new, v_new  both NULL, or the decoded token's K/V [B, Hkv, d] (16-byte aligned)
  *            stored and attended as in sfi_sparse_decode_append_attn.
  *   workspace  as sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent).
  *   Other arguments as sfi_sparse_decode_attn.  Errors: SFI_ERR_INVALID_ARG for a
- *   NULL sel_idx with k > 0, negative k or an unpaired k_new / v_new; SFI_ERR_UNSUPPORTED when
+ *   NULL sel_idx with k > 0, negative k, per_head not 0 or 1, or an unpaired
+ *   k_new / v_new; SFI_ERR_UNSUPPORTED when
  *   num_pages * 16 exceeds INT32_MAX.
  */
 SFI_API sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
                                           const void* k_new, const void* v_new, const int32_t* seq_lens,
                                           int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
-                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                          void* stream);
+                                          int32_t per_head, float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream);
 
 /*
  * Drafting and verifying requests in one launch (ASPIRE abstract: a unified

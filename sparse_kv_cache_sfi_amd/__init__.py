@@ -77,7 +77,10 @@ _SIGS = {
                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p],
     "sfi_sparse_decode_indexed_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
-                                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+                                       c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
+                                       c_void_p],
+    "sfi_dense_attn_with_head_stats": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                       c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
     "sfi_mixed_attn": [_SHAPE_P, _KV_P, c_void_p, POINTER(c_int32), POINTER(c_int32), c_void_p, c_int32,
                        c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                        c_void_p, c_size_t, c_void_p],
@@ -427,10 +430,12 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
                                n_sink: int, n_recent: int, max_seq_len: int, scale: Optional[float] = None,
                                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                                workspace: Optional[torch.Tensor] = None, stream=None,
-                               k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None):
+                               k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                               per_head: bool = False):
     """Fast step over the positions sel_idx [B, Hkv, k] lists (plus sink and recent), every row
     read in place from paged KV: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq])
-    (sfi_sparse_decode_indexed_attn).  k_new / v_new as in sparse_decode_attn."""
+    (sfi_sparse_decode_indexed_attn).  With per_head, sel_idx is [B, Hq, k], one set per
+    query head.  k_new / v_new as in sparse_decode_attn."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
     _i32(sel_idx, "sel_idx")
@@ -443,24 +448,60 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
                 raise ValueError(f"{n} must be [B, Hkv, d] in the pool dtype")
     B, Hq, d = q.shape
     Hkv = k_pool.shape[1]
-    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, Hkv):
-        raise ValueError("sel_idx must be [B, Hkv, k]")
+    rows = Hq if per_head else Hkv
+    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, rows):
+        raise ValueError(f"sel_idx must be [B, {'Hq' if per_head else 'Hkv'}, k]")
     k = sel_idx.shape[2]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    unit_shape = _shape(B, Hq, rows, d, _dtype_code(q), scale)
     dev = q.device
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = c_size_t(0)
-    _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), n_sink + k, n_recent,
+    _call("sfi_sparse_decode_workspace_size", ctypes.byref(unit_shape), ctypes.byref(kv), n_sink + k, n_recent,
           ctypes.byref(need))
     ws = _workspace(need.value, workspace, dev)
     _call("sfi_sparse_decode_indexed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), _ptr(k_new),
-          _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, out.data_ptr(), _ptr(lse),
-          _ptr(ws), _nbytes(ws), _stream(stream, dev))
+          _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, int(per_head), out.data_ptr(),
+          _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
     return out, lse
+
+
+def dense_attn_with_head_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                               block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
+                               n_sink: int = 0, n_recent: int = 0, scale: Optional[float] = None,
+                               score_stride: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Slow step with one logit row per query head: q [B, Hq, d] -> (out [B, Hq, d] fp32,
+    lse [B, Hq], scores [B, Hq, score_stride]) (sfi_dense_attn_with_head_stats)."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    stride = int(score_stride if score_stride is not None else max_seq_len)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((B, Hq, stride), dtype=torch.float32, device=dev)
+    _dev(scores, "scores")
+    if scores.dtype != torch.float32 or tuple(scores.shape) != (B, Hq, stride):
+        raise ValueError("scores must be float32 [B, Hq, score_stride]")
+    need = c_size_t(0)
+    _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_dense_attn_with_head_stats", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
+          n_sink, n_recent, out.data_ptr(), _ptr(lse), scores.data_ptr(), stride, _ptr(ws), _nbytes(ws),
+          _stream(stream, dev))
+    return out, lse, scores
 
 
 def mixed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,

@@ -4,7 +4,7 @@
 
 namespace sfi {
 
-template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false, bool INDEXED = false>
+template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
   using S = DecodeShape<T, D, G>;
   __shared__ __attribute__((aligned(16))) char smem[INDEXED ? S::SMEM_IDX : S::SMEM];
@@ -15,17 +15,19 @@ template <typename T, int D, int G>
 static hipError_t launch_decode_t(const AttnArgs& a, bool sparse, int B, hipStream_t stream) {
   const dim3 grid(a.n_split, a.Hkv, B), block(256);
   if (sparse && a.sel_k >= 0 && a.k_new)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, true, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, 0, true, true>), grid, block, 0, stream, a);
   else if (sparse && a.sel_k >= 0)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, 0, false, true>), grid, block, 0, stream, a);
   else if (sparse && a.k_new)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, 0, true>), grid, block, 0, stream, a);
   else if (sparse)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true, 0>), grid, block, 0, stream, a);
+  else if (a.scores && a.head_scores)
+    hipLaunchKernelGGL((decode_kernel<T, D, G, false, 2>), grid, block, 0, stream, a);
   else if (a.scores)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, false, 1>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<T, D, G, false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, false, 0>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -81,7 +81,9 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
   return acc;
 }
 
-template <typename T, int D, int G, bool SPARSE, bool SCORES, bool APPEND = false, bool INDEXED = false>
+// SCORES: 0 no logits, 1 the group-summed logits [B, Hkv, stride], 2 one logit row per
+// query head [B, Hq, stride].
+template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, const int g, const int split,
                                             const int q_row0, char* smem) {
   using S = DecodeShape<T, D, G>;
@@ -183,17 +185,21 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     ckb = reinterpret_cast<const T*>(a.ck) + base;
     cvb = reinterpret_cast<const T*>(a.cv) + base;
   }
-  const int64_t page_elems = (int64_t)a.Hkv * kPage * D;
-  const int64_t head_off = (int64_t)g * kPage * D;
+  // Units are KV heads, or with head_div > 1 (per-query-head selection) query heads,
+  // head_div of them per KV head of the pool.
+  const int gp = INDEXED ? g / a.head_div : g;
+  const int pool_heads = INDEXED ? a.Hkv / a.head_div : a.Hkv;
+  const int64_t page_elems = (int64_t)pool_heads * kPage * D;
+  const int64_t head_off = (int64_t)gp * kPage * D;
   const T* knew = nullptr;
   const T* vnew = nullptr;
   if constexpr (APPEND) {
     // The new token (position L - 1) is attended from the arguments; the last split's
     // work-group also stores it into its page (no other work-group reads that row).
-    knew = reinterpret_cast<const T*>(a.k_new) + ((int64_t)b * a.Hkv + g) * D;
-    vnew = reinterpret_cast<const T*>(a.v_new) + ((int64_t)b * a.Hkv + g) * D;
+    knew = reinterpret_cast<const T*>(a.k_new) + ((int64_t)b * pool_heads + gp) * D;
+    vnew = reinterpret_cast<const T*>(a.v_new) + ((int64_t)b * pool_heads + gp) * D;
     constexpr int CH = D * (int)sizeof(T) / 16;
-    if (split == a.n_split - 1 && L > 0 && tid < 2 * CH) {
+    if (split == a.n_split - 1 && g == gp * (INDEXED ? a.head_div : 1) && L > 0 && tid < 2 * CH) {
       const int pg = bt_row[(L - 1) >> 4];
       if (pg >= 0 && pg < a.num_pages) {
         const int64_t off = (int64_t)pg * page_elems + head_off + (int64_t)((L - 1) & 15) * D;
@@ -210,7 +216,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   float* srow = nullptr;
   if constexpr (SCORES) {
     candidate_bounds(L, a.t_q, a.n_sink, a.n_recent, &clo, &chi);
-    srow = a.scores + ((int64_t)b * a.Hkv + g) * a.score_stride;
+    srow = SCORES == 2 ? a.scores + ((int64_t)b * a.Hq + g * G) * a.score_stride
+                       : a.scores + ((int64_t)b * a.Hkv + g) * a.score_stride;
   }
 
   float m[G], l[G], o[G][E];
@@ -305,11 +312,17 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (sub == 0 && in_[u]) {
-          float sc = 0.f;
-#pragma unroll
-          for (int h = 0; h < G; ++h) sc += s[u][h];
           const int j = pos_[u];
-          srow[j] = (ok_[u] && j >= clo && j < chi) ? sc * a.scale : neg_inf();
+          const bool cand = ok_[u] && j >= clo && j < chi;
+          if constexpr (SCORES == 2) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) srow[h * a.score_stride + j] = cand ? s[u][h] * a.scale : neg_inf();
+          } else {
+            float sc = 0.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) sc += s[u][h];
+            srow[j] = cand ? sc * a.scale : neg_inf();
+          }
         }
       }
     }
@@ -395,7 +408,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     const int f0 = max(t1, t0);
     const int64_t f1 = (split == a.n_split - 1) ? a.score_stride
                                                 : min((int64_t)t0 + a.split_tokens, a.score_stride);
-    for (int64_t j = f0 + tid; j < f1; j += NT) srow[j] = neg_inf();
+    for (int h = 0; h < (SCORES == 2 ? G : 1); ++h)
+      for (int64_t j = f0 + tid; j < f1; j += NT) srow[h * a.score_stride + j] = neg_inf();
   }
 
   // Merge the row groups of this wave (lanes that share `sub`).

@@ -68,6 +68,12 @@ struct AttnArgs {
   // compact buffers (sel may be NULL when sel_k is 0).
   const int32_t* sel;
   int32_t sel_k;
+  // Units per KV head of the pool (1; the number of query heads per KV head when an
+  // index-set fast step runs one unit per query head).
+  int32_t head_div;
+  // Slow step: write one logit row per query head ([B, Hq, score_stride]) instead of
+  // the group sums.
+  int32_t head_scores;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves

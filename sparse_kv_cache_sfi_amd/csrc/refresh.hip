@@ -8,7 +8,7 @@ namespace sfi {
 
 // Work-groups [0, rows) are riders (dispatched first, so they start before the
 // attention grid fills the CUs); the rest are the slow step's split-K units.
-template <typename T, int D, int G, bool SCORES>
+template <typename T, int D, int G, int SCORES>
 __global__ __launch_bounds__(256) void dense_refresh_kernel(AttnArgs a, RefreshArgs r) {
   constexpr int SD = DecodeShape<T, D, G>::SMEM, SR = RiderShape::SMEM;
   __shared__ __attribute__((aligned(16))) char smem[SD > SR ? SD : SR];

@@ -156,6 +156,7 @@ sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_
   a.scale = s->scale;
   a.scale_log2 = s->scale * sfi::kLog2e;
   a.sel_k = -1;   // not an index-set call
+  a.head_div = 1;
   return a;
 }
 
@@ -273,10 +274,14 @@ sfi_status sfi_dense_attn_workspace_size(const sfi_shape* shape, const sfi_paged
   return ok();
 }
 
-sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, int32_t t_q,
-                                     const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
-                                     float* lse, float* scores, int64_t score_stride, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, int32_t t_q,
+                      const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out, float* lse,
+                      float* scores, int64_t score_stride, bool head_scores, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
   SFI_TRY(check_ptr16(q, "q"));
@@ -314,6 +319,7 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
   a.lse = lse;
   a.scores = scores;
   a.score_stride = score_stride;
+  a.head_scores = head_scores ? 1 : 0;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -322,6 +328,27 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
   else
     e = sfi::launch_verify(a, shape->head_dim, G, shape->batch, st);
   return hip_status(e, "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, int32_t t_q,
+                                     const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
+                                     float* lse, float* scores, int64_t score_stride, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return dense_call(shape, kv, q, t_q, seq_lens, n_sink, n_recent, out, lse, scores, score_stride, false, workspace,
+                    workspace_bytes, stream);
+}
+
+sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                          const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
+                                          float* lse, float* scores, int64_t score_stride, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (!scores) return fail(SFI_ERR_INVALID_ARG, "scores is NULL");
+  return dense_call(shape, kv, q, 1, seq_lens, n_sink, n_recent, out, lse, scores, score_stride, true, workspace,
+                    workspace_bytes, stream);
 }
 
 sfi_status sfi_dense_attn_with_refresh(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
@@ -467,12 +494,18 @@ namespace {
 
 // The fast step.  Sink and selected rows come from compact buffers, or, when sel_k is
 // >= 0, from paged KV at the positions sel lists (cap is then n_sink + sel_k).
-sfi_status sparse_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, const void* k_new,
+sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const void* q, const void* k_new,
                        const void* v_new, const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
                        const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
-                       const int32_t* sel, int32_t sel_k, float* out, float* lse, void* workspace,
+                       const int32_t* sel, int32_t sel_k, bool per_head, float* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_shape(shape_in));
+  // One unit per query head when each query head has its own selection: the units see
+  // a shape with as many KV heads as query heads, head_div of them per pool head.
+  const int head_div = per_head ? shape_in->num_q_heads / shape_in->num_kv_heads : 1;
+  sfi_shape unit_shape = *shape_in;
+  if (per_head) unit_shape.num_kv_heads = shape_in->num_q_heads;
+  const sfi_shape* shape = &unit_shape;
   SFI_TRY(check_kv(kv));
   SFI_TRY(check_ptr16(q, "q"));
   SFI_TRY(check_ptr16(out, "out"));
@@ -514,6 +547,7 @@ sfi_status sparse_call(const sfi_shape* shape, const sfi_paged_kv* kv, const voi
   a.v_new = v_new;
   a.sel = sel;
   a.sel_k = sel_k;
+  a.head_div = head_div;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
@@ -530,7 +564,7 @@ sfi_status sfi_sparse_decode_attn(const sfi_shape* shape, const sfi_paged_kv* kv
                                   const void* compact_v, int32_t cap, const int32_t* n_compact, float* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_call(shape, kv, q, nullptr, nullptr, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
-                     n_compact, nullptr, -1, out, lse, workspace, workspace_bytes, stream);
+                     n_compact, nullptr, -1, false, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
@@ -541,14 +575,15 @@ sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged
   SFI_TRY(check_ptr16(k_new, "k_new"));
   SFI_TRY(check_ptr16(v_new, "v_new"));
   return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
-                     n_compact, nullptr, -1, out, lse, workspace, workspace_bytes, stream);
+                     n_compact, nullptr, -1, false, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
                                           const void* k_new, const void* v_new, const int32_t* seq_lens,
                                           int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
-                                          float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+                                          int32_t per_head, float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (per_head != 0 && per_head != 1) return fail(SFI_ERR_INVALID_ARG, "per_head must be 0 or 1");
   if (k < 0) return fail(SFI_ERR_INVALID_ARG, "k must be >= 0");
   if (!sel_idx && k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
   if (!k_new != !v_new) return fail(SFI_ERR_INVALID_ARG, "k_new and v_new must both be NULL or both be set");
@@ -557,7 +592,7 @@ sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_page
     SFI_TRY(check_ptr16(v_new, "v_new"));
   }
   return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, nullptr, nullptr, 0, nullptr, sel_idx,
-                     k, out, lse, workspace, workspace_bytes, stream);
+                     k, per_head == 1, out, lse, workspace, workspace_bytes, stream);
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

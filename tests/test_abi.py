@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
               "sfi_mixed_attn", "sfi_dense_attn_with_refresh", "sfi_sparse_decode_append_attn",
-              "sfi_sparse_decode_indexed_attn"):
+              "sfi_sparse_decode_indexed_attn", "sfi_dense_attn_with_head_stats"):
         assert n in names
 
 
@@ -183,10 +183,10 @@ def test_sparse_append_rejects_bad_arguments(lib):
 def test_sparse_indexed_rejects_bad_arguments(lib):
     shape = _shape()
 
-    def call(sel=FAKE, k=64, kn=None, vn=None, q=FAKE, ws_bytes=1 << 40, kv=None, out=FAKE):
+    def call(sel=FAKE, k=64, kn=None, vn=None, q=FAKE, ws_bytes=1 << 40, kv=None, out=FAKE, per_head=0):
         kv = kv or _kv()
         return lib.sfi_sparse_decode_indexed_attn(ctypes.byref(shape), ctypes.byref(kv), q, kn, vn, FAKE, 4, 64, sel,
-                                                  k, out, FAKE, FAKE, ws_bytes, None)
+                                                  k, per_head, out, FAKE, FAKE, ws_bytes, None)
     assert call(sel=0) == 1 and "sel_idx is NULL" in lib.sfi_last_error().decode()
     assert call(k=-1) == 1 and "k must be" in lib.sfi_last_error().decode()
     assert call(kn=FAKE) == 1 and "both" in lib.sfi_last_error().decode()
@@ -195,6 +195,20 @@ def test_sparse_indexed_rejects_bad_arguments(lib):
     assert call(out=0) == 1
     assert call(k=20000, ws_bytes=1) == 3          # several splits: partials needed
     assert call(kv=_kv(num_pages=1 << 27)) == 2 and "slots" in lib.sfi_last_error().decode()
+    assert call(per_head=2) == 1 and "per_head" in lib.sfi_last_error().decode()
+    assert call(per_head=1, k=20000, ws_bytes=1) == 3
+
+
+def test_dense_head_stats_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def call(scores=FAKE, stride=16384, q=FAKE, ws_bytes=1 << 40):
+        return lib.sfi_dense_attn_with_head_stats(ctypes.byref(shape), ctypes.byref(kv), q, FAKE, 4, 64, FAKE, FAKE,
+                                                  scores, stride, FAKE, ws_bytes, None)
+    assert call(scores=0) == 1 and "scores is NULL" in lib.sfi_last_error().decode()
+    assert call(stride=100) == 1 and "score_stride" in lib.sfi_last_error().decode()
+    assert call(q=MISALIGNED) == 1
+    assert call(ws_bytes=1) == 3
 
 
 def test_workspace_queries_match_the_plan(lib):
