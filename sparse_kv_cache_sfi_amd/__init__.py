@@ -128,7 +128,8 @@ def _call(name: str, *args) -> None:
 
 class BoundCall:
     """One library launch with its arguments marshalled once (see bind()).  ``outputs``
-    is what the entry point returned; the object keeps every buffer it allocated alive."""
+    is what the entry point returned; the object keeps every tensor it was given and
+    every buffer it allocated alive, since the launch holds their device addresses."""
 
     def __init__(self, name: str, args: tuple, outputs, keep: list):
         self.name = name
@@ -146,8 +147,9 @@ class BoundCall:
 def bind(op, *args, **kwargs) -> BoundCall:
     """Marshal one entry-point call (e.g. ``bind(sparse_decode_attn, q, ...)``) without making
     it.  Calling the result makes that launch on the same tensors and stream with only the C
-    call's own cost on the host; host-side size queries run once, here.  Tensors passed in
-    must outlive the bound call; buffers the entry point allocates are kept by it."""
+    call's own cost on the host; host-side size queries run once, here.  The bound call
+    holds a reference to every tensor passed in and every buffer the entry point
+    allocates, so none of them is freed while it exists."""
     global _binding
     _binding = {"calls": [], "keep": []}
     try:
@@ -158,7 +160,8 @@ def bind(op, *args, **kwargs) -> BoundCall:
     if len(rec["calls"]) != 1:
         raise ValueError(f"{getattr(op, '__name__', op)} does not make exactly one launch")
     name, cargs = rec["calls"][0]
-    return BoundCall(name, cargs, outputs, rec["keep"])
+    given = [a for a in list(args) + list(kwargs.values()) if isinstance(a, torch.Tensor)]
+    return BoundCall(name, cargs, outputs, rec["keep"] + given)
 
 
 # --------------------------------------------------------------------------- marshalling helpers

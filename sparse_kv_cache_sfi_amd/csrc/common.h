@@ -64,6 +64,32 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The value of x held by lane (lane ^ OFF), for a power of two OFF < 64: DPP
+// quad_perm for 1 and 2, DPP row_ror:8 for 8 (a rotation by 8 inside a 16-lane row
+// is the xor-8 exchange), ds_swizzle in bitmask mode for 4 and 16 (source lane
+// = lane ^ OFF within 32 lanes), ds_bpermute for 32.  Every lane must be active.
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float x) {
+  static_assert(OFF > 0 && OFF < 64 && (OFF & (OFF - 1)) == 0, "power of two below the wave width");
+  if constexpr (OFF == 1) return dpp_mov<0xB1>(x);
+  else if constexpr (OFF == 2) return dpp_mov<0x4E>(x);
+  else if constexpr (OFF == 8) return dpp_mov<0x128>(x);
+  else if constexpr (OFF == 32) return __shfl_xor(x, 32);
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (OFF << 10)));
+}
+
+// x combined by op with the lanes at xor distance FROM, 2 FROM, ..., 32, in that
+// order: every lane ends with op over the lanes that share its bits below FROM.
+template <int FROM, typename Op>
+__device__ __forceinline__ float xor_fold(float x, Op op) {
+  if constexpr (FROM < kWave) {
+    x = op(x, lane_xor<FROM>(x));
+    return xor_fold<FROM * 2>(x, op);
+  } else {
+    return x;
+  }
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Request length as the kernels use it: never beyond what the block table or the

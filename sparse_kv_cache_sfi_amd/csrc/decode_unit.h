@@ -415,20 +415,13 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   // Merge the row groups of this wave (lanes that share `sub`).
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const auto fmax_op = [](float x, float y) { return fmaxf(x, y); };
+    const auto add_op = [](float x, float y) { return x + y; };
+    const float M = xor_fold<LPR>(m[h], fmax_op);
     const float al = (m[h] == neg_inf()) ? 0.f : exp2_fast(m[h] - M);
-    float ls = l[h] * al;
+    const float ls = xor_fold<LPR>(l[h] * al, add_op);
 #pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) ls += __shfl_xor(ls, off);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float x = o[h][e] * al;
-#pragma unroll
-      for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-      o[h][e] = x;
-    }
+    for (int e = 0; e < E; ++e) o[h][e] = xor_fold<LPR>(o[h][e] * al, add_op);
     m[h] = M;
     l[h] = ls;
   }

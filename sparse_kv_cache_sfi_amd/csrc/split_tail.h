@@ -2,6 +2,8 @@
 // (request, KV head) unit.  Shared by the decode and the verification kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,14 +38,20 @@ constexpr int kCoherentLoad = 16;
 
 // Wave-wide reductions (all 64 lanes receive the result).
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  x = fmaxf(x, lane_xor<1>(x));
+  x = fmaxf(x, lane_xor<2>(x));
+  x = fmaxf(x, lane_xor<4>(x));
+  x = fmaxf(x, lane_xor<8>(x));
+  x = fmaxf(x, lane_xor<16>(x));
+  return fmaxf(x, lane_xor<32>(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-  return x;
+  x += lane_xor<1>(x);
+  x += lane_xor<2>(x);
+  x += lane_xor<4>(x);
+  x += lane_xor<8>(x);
+  x += lane_xor<16>(x);
+  return x + lane_xor<32>(x);
 }
 
 // A unit (b, g) owns R = t_q * G output rows: row r = (t, h) with t = r / G,
@@ -170,12 +178,22 @@ struct SplitTail {
         for (int j = 0; j < PRE; ++j)
           if (p + P * (j0 + j) < ns) add(wr[p + P * (j0 + j)], v[j]);
       }
-      for (int off = 1; off < P; off <<= 1) {
-        acc.x += __shfl_xor(acc.x, off);
-        acc.y += __shfl_xor(acc.y, off);
-        acc.z += __shfl_xor(acc.z, off);
-        acc.w += __shfl_xor(acc.w, off);
-      }
+      // xor tree over the P lanes of the group (P is uniform over the work-group)
+      auto fold = [&](auto off_tag) {
+        constexpr int OFF = decltype(off_tag)::value;
+        if (OFF < P) {
+          acc.x += lane_xor<OFF>(acc.x);
+          acc.y += lane_xor<OFF>(acc.y);
+          acc.z += lane_xor<OFF>(acc.z);
+          acc.w += lane_xor<OFF>(acc.w);
+        }
+      };
+      fold(std::integral_constant<int, 1>{});
+      fold(std::integral_constant<int, 2>{});
+      fold(std::integral_constant<int, 4>{});
+      fold(std::integral_constant<int, 8>{});
+      fold(std::integral_constant<int, 16>{});
+      fold(std::integral_constant<int, 32>{});
       if (p == 0) {
         const int64_t orow = row(a, q_row0, g, G, r);
         const int e4 = grp % D4;

@@ -126,6 +126,27 @@ def test_bound_calls_repeat_the_direct_calls(gpu_lib):
     assert torch.equal(o1, o3) and torch.equal(l1, l3) and torch.equal(s1, s3)
 
 
+def test_bound_calls_keep_the_tensors_they_were_given(gpu_lib):
+    """A bound call holds its tensors: temporaries passed to bind() are not freed and reused."""
+    c = make_case(113, name="keep", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[2500, 900], n_sink=4,
+                  n_recent=64, k_sel=128)
+    dc = DevCase(c)
+    rng = np.random.default_rng(3)
+    sel = dev_array(np.stack([_random_selection(rng, c, int(c.seq_lens[b]), 128) for b in range(2)]))
+    ck, cv, nc = gpu_lib.pack_compact(dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=4, cap=132, max_seq_len=dc.max_seq_len)
+    kw = dict(n_sink=4, n_recent=64, max_seq_len=dc.max_seq_len)
+    o1, l1 = gpu_lib.sparse_decode_attn(dc.q[:, 0].contiguous(), dc.k, dc.v, dc.bt, dc.lens, ck, cv, nc, **kw)
+    call = gpu_lib.bind(gpu_lib.sparse_decode_attn, dc.q[:, 0].contiguous(), dc.k, dc.v, dc.bt, dc.lens, ck.clone(),
+                        cv.clone(), nc.clone(), **kw)
+    torch.cuda.synchronize()
+    churn = [torch.full_like(ck, float("nan")) for _ in range(4)] + [torch.full_like(dc.q, float("nan"))]
+    call()
+    torch.cuda.synchronize()
+    o2, l2 = call.outputs
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    del churn
+
+
 def test_dense_is_invariant_to_physical_page_order(gpu_lib):
     c = make_case(111, name="i", B=1, Hq=8, Hkv=4, d=128, dtype="bf16", seq_lens=[1800], n_sink=4,
                   n_recent=32, k_sel=64, spare_pages=7)
