@@ -385,6 +385,18 @@ def test_append_token_stores_one_row_and_a_dominant_new_key_returns_its_value():
         np.testing.assert_allclose(out[h], v_new[h // 2], rtol=0, atol=1e-12)
 
 
+def test_append_token_behind_an_invalid_page_or_at_length_zero_stores_nothing():
+    c = make_case(42, name="ap", B=1, Hq=4, Hkv=2, d=64, dtype="f32", seq_lens=[100], capacity=[112], n_sink=4,
+                  n_recent=16, k_sel=8)
+    bt = c.kv.block_table[0].copy()
+    bt[6] = -1                                   # the page of position 100
+    kn = np.ones((2, 64), np.float32)
+    for row, L in ((bt, 101), (c.kv.block_table[0], 0)):
+        k2, v2 = O.append_token(c.kv.k, c.kv.v, row, L, kn, kn)
+        np.testing.assert_array_equal(k2, c.kv.k)
+        np.testing.assert_array_equal(v2, c.kv.v)
+
+
 # --------------------------------------------------------------------------- refresh schedule
 
 def _drift(seed=31, q_gain=1.0, hh=12):
