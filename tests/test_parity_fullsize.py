@@ -1,0 +1,128 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations the benchmark
+times (bound calls, shared workspaces, the refresh driver).
+
+* The 16K decode layer (1 request, 16 query / 8 KV heads, d 128, 12.5 % retention):
+  one whole step (slow step with logits -> Selector -> pack -> fast step) on the
+  benchmark's first replica, every KV head checked against the oracle.
+* The batched decode (16 requests, 32 query / 8 KV heads, lengths in [16K, 32K],
+  selected 1024, recent 256): one slow and one fast step of RefreshSchedule; the
+  Selector and pack checked on every row, attention outputs and logits on sampled
+  requests.
+
+Tolerances as everywhere: out 2e-3, lse 1e-3, logits within the fp32 forward-error
+bound, Selector and pack bit-exact (selection taken from the GPU's own logits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sfi_synth import qwen06b_decode_case, qwen8b_batched_case
+from _gpu import DEV, LSE_TOL, OUT_TOL, DevCase, assert_close, dev_array, host_bits, score_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_logits(c, kv, b, q_vals, S, L, groups):
+    lo, hi = O.candidate_range(L, 1, c.n_sink, c.n_recent)
+    assert np.all(np.isneginf(S[:, :lo])) and np.all(np.isneginf(S[:, hi:]))
+    ref = O.group_scores(q_vals[None], c.kv.k, c.kv.block_table[b], L, c.scale, c.Hkv, c.n_sink, c.n_recent,
+                         S.shape[-1], kv_dtype=c.dtype, groups=groups)
+    for g in groups:
+        rows = O.paged_rows(kv, c.kv.block_table[b], g, np.arange(lo, hi))
+        bound = score_bound(q_vals[g * c.G:(g + 1) * c.G], rows, c.scale)
+        assert_close(S[g, lo:hi], ref[g, lo:hi], bound, f"logits b={b} g={g}")
+
+
+def test_16k_layer_step_at_full_size(gpu_lib):
+    c = qwen06b_decode_case(1000)            # the benchmark's first replica
+    dc = DevCase(c)
+    L, k, B = int(c.seq_lens[0]), c.k_sel, 1
+    cap = c.n_sink + k
+    q1 = dc.q[:, 0].contiguous()
+    out = torch.empty((B, 1, c.Hq, c.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, c.Hq), dtype=torch.float32, device=DEV)
+    sc = torch.empty((B, c.Hkv, L), dtype=torch.float32, device=DEV)
+    sel = torch.empty((B, c.Hkv, k), dtype=torch.int32, device=DEV)
+    ck = torch.empty((B, c.Hkv, cap, c.d), dtype=torch.bfloat16, device=DEV)
+    cv = torch.empty_like(ck)
+    nc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    fo = torch.empty((B, c.Hq, c.d), dtype=torch.float32, device=DEV)
+    fl = torch.empty((B, c.Hq), dtype=torch.float32, device=DEV)
+    kw = dict(n_sink=c.n_sink, n_recent=c.n_recent)
+    calls = [
+        gpu_lib.bind(gpu_lib.dense_attn_with_stats, dc.q, dc.k, dc.v, dc.bt, dc.lens, max_seq_len=L, out=out, lse=lse,
+                     scores=sc, **kw),
+        gpu_lib.bind(gpu_lib.select_topk, sc, dc.lens, k=k, sel_idx=sel, **kw),
+        gpu_lib.bind(gpu_lib.pack_compact, dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=c.n_sink, cap=cap, max_seq_len=L,
+                     compact_k=ck, compact_v=cv, n_compact=nc),
+        gpu_lib.bind(gpu_lib.sparse_decode_attn, q1, dc.k, dc.v, dc.bt, dc.lens, ck, cv, nc, max_seq_len=L, out=fo,
+                     lse=fl, **kw),
+    ]
+    for call in calls:
+        call()
+    torch.cuda.synchronize()
+    qv = c.q_values()[0, 0]
+    ro, rl = O.dense_attention(qv[None], c.kv.k, c.kv.v, c.kv.block_table[0], L, c.scale, c.Hkv, kv_dtype="bf16")
+    assert_close(out.cpu().numpy()[0, 0], ro[0], OUT_TOL, "dense out")
+    assert_close(lse.cpu().numpy()[0, 0], rl[0], LSE_TOL, "dense lse")
+    S = sc.cpu().numpy()[0]
+    _check_logits(c, c.kv.k_values(), 0, qv, S, L, range(c.Hkv))
+    lo, hi = O.candidate_range(L, 1, c.n_sink, c.n_recent)
+    got_sel = sel.cpu().numpy()[0]
+    ref_sel = np.stack([O.select_topk(S[g].astype(np.float64), lo, hi, k) for g in range(c.Hkv)])
+    assert np.array_equal(got_sel, ref_sel)
+    rck, rcv, rnc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[0], L, c.n_sink, ref_sel, cap)
+    assert int(nc.cpu()[0]) == rnc == cap
+    assert np.array_equal(host_bits(ck)[0], rck) and np.array_equal(host_bits(cv)[0], rcv)
+    so, sl = O.sparse_decode(qv, rck, rcv, rnc, c.kv.k, c.kv.v, c.kv.block_table[0], L, c.n_sink, c.n_recent,
+                             c.scale, kv_dtype="bf16")
+    assert_close(fo.cpu().numpy()[0], so, OUT_TOL, "fast out")
+    assert_close(fl.cpu().numpy()[0], sl, LSE_TOL, "fast lse")
+    # the planted heavy hitters are found
+    for g in range(c.Hkv):
+        assert set(c.planted[(0, g)].tolist()) <= set(got_sel[g].tolist()), g
+
+
+def test_batched_16k_32k_decode_at_full_size(gpu_lib):
+    from sparse_kv_cache_sfi_amd.schedule import RefreshSchedule
+    c = qwen8b_batched_case(3)
+    dc = DevCase(c)
+    B, k = c.B, c.k_sel
+    q1 = dc.q[:, 0].contiguous()
+    sched = RefreshSchedule(dc.k, dc.v, dc.bt, q1, dc.lens, max_seq_len=dc.max_seq_len, n_sink=c.n_sink,
+                            n_recent=c.n_recent, k=k, interval=2)
+    assert sched.step()                              # slow step: dense + logits -> Selector -> pack
+    torch.cuda.synchronize()
+    out_s, lse_s = sched.out.cpu().numpy(), sched.lse.cpu().numpy()
+    S = sched.scores.cpu().numpy()
+    sel = sched.sel.cpu().numpy()
+    ckb, cvb, ncb = host_bits(sched.compact_k), host_bits(sched.compact_v), sched.n_compact.cpu().numpy()
+    assert not sched.step()                          # fast step over the packed state
+    torch.cuda.synchronize()
+    out_f, lse_f = sched.out.cpu().numpy(), sched.lse.cpu().numpy()
+    qv = c.q_values()[:, 0]
+    cap = c.n_sink + k
+    for b in range(B):                               # Selector and pack: every row
+        L = int(c.seq_lens[b])
+        lo, hi = O.candidate_range(L, 1, c.n_sink, c.n_recent)
+        ref_sel = np.stack([O.select_topk(S[b, g].astype(np.float64), lo, hi, k) for g in range(c.Hkv)])
+        assert np.array_equal(sel[b], ref_sel), b
+        for g in range(c.Hkv):
+            assert set(c.planted[(b, g)].tolist()) <= set(sel[b, g].tolist()), (b, g)
+        rck, rcv, rnc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], L, c.n_sink, ref_sel, cap)
+        assert ncb[b] == rnc
+        assert np.array_equal(ckb[b], rck) and np.array_equal(cvb[b], rcv), b
+    kv = c.kv.k_values()
+    for b in (0, int(np.argmax(c.seq_lens)), B - 1):  # attention and logits: sampled requests, all heads
+        L = int(c.seq_lens[b])
+        ro, rl = O.dense_attention(qv[b][None], c.kv.k, c.kv.v, c.kv.block_table[b], L, c.scale, c.Hkv,
+                                   kv_dtype="bf16")
+        assert_close(out_s[b], ro[0], OUT_TOL, f"slow out b={b}")
+        assert_close(lse_s[b], rl[0], LSE_TOL, f"slow lse b={b}")
+        _check_logits(c, kv, b, qv[b], S[b], L, range(c.Hkv))
+        rck, rcv, rnc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], L, c.n_sink, sel[b], cap)
+        so, sl = O.sparse_decode(qv[b], rck, rcv, rnc, c.kv.k, c.kv.v, c.kv.block_table[b], L, c.n_sink,
+                                 c.n_recent, c.scale, kv_dtype="bf16")
+        assert_close(out_f[b], so, OUT_TOL, f"fast out b={b}")
+        assert_close(lse_f[b], sl, LSE_TOL, f"fast lse b={b}")
