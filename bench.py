@@ -126,6 +126,9 @@ def main():
                     help="run only the 128K draft/verify mix (for counter collection) and print its figures")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated legs to run alone, printing their figures: append_fast, draft_refresh, "
+                         "head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -140,6 +143,20 @@ def main():
     dev = torch.device("cuda:0")
     if args.specmix_only:
         print(json.dumps({"specmix_128k": specmix(sfi, dev)}), flush=True)
+        return
+    if args.only:
+        legs = {"append_fast": lambda: append_fast(sfi, dev, torch.cuda.current_stream(dev)),
+                "draft_refresh": lambda: draft_refresh_c3(sfi, dev),
+                "head_selection": lambda: head_selection(sfi, dev),
+                "refresh_schedule": lambda: refresh_schedule_c3(sfi, dev),
+                "refresh_64k_overlap": lambda: refresh_overlap(sfi, dev),
+                "specmix_128k": lambda: specmix(sfi, dev)}
+        names = [n for n in args.only.split(",") if n]
+        unknown = [n for n in names if n not in legs]
+        if unknown:
+            print(f"unknown legs {unknown}; known: {sorted(legs)}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({n: legs[n]() for n in names}), flush=True)
         return
     L, B, Hq, Hkv, d = 16384, 1, 16, 8, 128
     n_sink, n_recent = 4, 64
