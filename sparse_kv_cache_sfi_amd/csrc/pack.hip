@@ -13,7 +13,9 @@
 
 namespace sfi {
 
-constexpr int kPackRowsPerBlock = 64;
+// Rows per work-group: 16 while that keeps the grid within kPackSmallGrid work-groups
+// (small batches: more, shorter work-groups cut the launch's latency), else 32.
+constexpr int kPackSmallGrid = 4096;
 
 struct PackArgs {
   const void* k_pool;
@@ -30,7 +32,7 @@ struct PackArgs {
   int32_t* n_compact;
 };
 
-template <int ROW_BYTES>
+template <int ROW_BYTES, int RPB>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
   constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
   constexpr int RPP = 256 / CPR;       // rows per pass of the work-group
@@ -47,8 +49,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
   char* ckp = reinterpret_cast<char*>(p.ck);
   char* cvp = reinterpret_cast<char*>(p.cv);
 
-  for (int rr = threadIdx.x / CPR; rr < kPackRowsPerBlock; rr += RPP) {
-    const int i = blockIdx.x * kPackRowsPerBlock + rr;
+  for (int rr = threadIdx.x / CPR; rr < RPB; rr += RPP) {
+    const int i = blockIdx.x * RPB + rr;
     if (i >= ns + p.k || i >= p.cap) continue;
     const int pos = i < ns ? i : srow[i - ns];
     if (pos < 0) continue;
@@ -85,13 +87,18 @@ hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, con
                        int cap, int32_t* n_compact, hipStream_t stream) {
   PackArgs p{k_pool, v_pool, block_table, max_pages, num_pages, max_seq_len, Hkv, seq_lens,
              n_sink, sel, k, ck, cv, cap, n_compact};
-  const int rows = n_sink + k;
-  const dim3 grid((rows + kPackRowsPerBlock - 1) / kPackRowsPerBlock, Hkv, B), block(256);
+  const int64_t rows = (int64_t)n_sink + k;
+  const bool small = (int64_t)B * Hkv * ((rows + 15) / 16) <= kPackSmallGrid;
+  const int rpb = small ? 16 : 32;
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb), Hkv, B), block(256);
   const int row_bytes = d * (dtype == 1 ? 2 : 4);
-  switch (row_bytes) {
-    case 128: hipLaunchKernelGGL((pack_kernel<128>), grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((pack_kernel<256>), grid, block, 0, stream, p); break;
-    case 512: hipLaunchKernelGGL((pack_kernel<512>), grid, block, 0, stream, p); break;
+  switch (row_bytes * (small ? 1 : -1)) {
+    case 128: hipLaunchKernelGGL((pack_kernel<128, 16>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((pack_kernel<256, 16>), grid, block, 0, stream, p); break;
+    case 512: hipLaunchKernelGGL((pack_kernel<512, 16>), grid, block, 0, stream, p); break;
+    case -128: hipLaunchKernelGGL((pack_kernel<128, 32>), grid, block, 0, stream, p); break;
+    case -256: hipLaunchKernelGGL((pack_kernel<256, 32>), grid, block, 0, stream, p); break;
+    case -512: hipLaunchKernelGGL((pack_kernel<512, 32>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
