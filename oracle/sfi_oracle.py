@@ -182,21 +182,30 @@ def pack_compact(k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.nda
     """Compact buffer of one request (SFI page, Fig. 3B: sink and selected tokens packed
     into a contiguous buffer).
 
-    Row i of KV head g is the stored row at position ([0, min(n_sink, L)) followed by
-    the non-negative entries of sel[g])[i]; the copy is bitwise.  sel: [Hkv, k].
-    Returns ck, cv of shape [Hkv, cap, d] (rows past n_compact are zero) and n_compact.
+    With ns = min(n_sink, L) and k_eff = the number of entries of sel[0] before its first
+    negative one, row i < ns + k_eff of KV head g is the stored row at position i
+    (i < ns) or sel[g][i - ns]; the copy is bitwise.  A position outside [0, L) or behind
+    an invalid block-table entry gives a zero row (reading: the pages pack only selected
+    positions, which lie in [0, L) on valid pages; anything else packs as zeros).
+    sel: [Hkv, k].  Returns ck, cv of shape [Hkv, cap, d] (rows past n_compact are zero)
+    and n_compact.
     """
     Hkv = k_pool.shape[1]
     d = k_pool.shape[3]
+    num_pages = k_pool.shape[0]
+    sel = np.asarray(sel)
     ns_eff = min(n_sink, L)
-    k_eff = int(np.count_nonzero(np.asarray(sel)[0] >= 0)) if Hkv > 0 else 0
+    neg = np.flatnonzero(sel[0] < 0) if Hkv > 0 else np.zeros(0, int)
+    k_eff = int(neg[0]) if len(neg) else sel.shape[1]
     n_c = ns_eff + k_eff
     ck = np.zeros((Hkv, cap, d), dtype=k_pool.dtype)
     cv = np.zeros((Hkv, cap, d), dtype=v_pool.dtype)
     for g in range(Hkv):
         pos = np.concatenate([np.arange(ns_eff), np.asarray(sel[g][:k_eff], dtype=np.int64)])
-        ck[g, :n_c] = paged_rows(k_pool, block_table_row, g, pos, page_size)
-        cv[g, :n_c] = paged_rows(v_pool, block_table_row, g, pos, page_size)
+        for i, p in enumerate(pos):
+            if 0 <= p < L and _valid_page(block_table_row, int(p), num_pages, page_size):
+                ck[g, i] = paged_rows(k_pool, block_table_row, g, [p], page_size)[0]
+                cv[g, i] = paged_rows(v_pool, block_table_row, g, [p], page_size)[0]
     return ck, cv, n_c
 
 

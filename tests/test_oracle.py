@@ -362,6 +362,24 @@ def test_mixed_dispatches_per_request():
     assert np.array_equal(res[1][0], o1) and res[1][2].shape == (2, 256)
 
 
+def test_pack_writes_zero_rows_past_the_end_and_behind_invalid_pages():
+    c = make_case(43, name="pz", B=1, Hq=4, Hkv=2, d=32, dtype="f32", seq_lens=[200], capacity=[240], n_sink=4,
+                  n_recent=16, k_sel=6)
+    bt = c.kv.block_table[0].copy()
+    bt[3] = -1                                     # positions 48..63
+    sel = np.array([[10, 50, 205, 100, -1, 7], [11, 12, 13, 14, 15, 16]], np.int32)
+    ck, cv, n_c = O.pack_compact(c.kv.k, c.kv.v, bt, 200, 4, sel, 12)
+    assert n_c == 4 + 4                            # head 0's entries before its first negative one
+    Kl, Vl = _logical(c.kv.k, bt, 240, 0), _logical(c.kv.v, bt, 240, 0)
+    np.testing.assert_array_equal(ck[0, :5], Kl[[0, 1, 2, 3, 10]])
+    np.testing.assert_array_equal(cv[0, :5], Vl[[0, 1, 2, 3, 10]])
+    assert not ck[0, 5].any() and not cv[0, 5].any()      # 50: behind the invalid page
+    assert not ck[0, 6].any() and not cv[0, 6].any()      # 205: past L = 200
+    np.testing.assert_array_equal(ck[0, 7], Kl[100])
+    assert not ck[:, 8:].any()                           # rows past n_compact stay zero
+    np.testing.assert_array_equal(ck[1, 4:8], _logical(c.kv.k, bt, 240, 1)[[11, 12, 13, 14]])
+
+
 # --------------------------------------------------------------------------- KV append
 
 def test_append_token_stores_one_row_and_a_dominant_new_key_returns_its_value():
