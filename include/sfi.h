@@ -296,16 +296,24 @@ SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const 
  *            sized by the same query with num_kv_heads set to num_q_heads.
  *   k_new, v_new  both NULL, or the decoded token's K/V [B, Hkv, d] (16-byte aligned)
  *            stored and attended as in sfi_sparse_decode_append_attn.
+ *   compact_k, compact_v, cap, n_compact  all NULL (cap ignored), or a compact buffer
+ *            [B, units, cap, d] (units = Hkv, or Hq with per_head; 16-byte aligned,
+ *            cap >= n_sink + k) and n_compact [B]: the launch also writes them exactly as
+ *            sfi_pack_compact would for sel_idx (SFI page, Fig. 3B), from the rows it
+ *            reads anyway, so the first fast step after a refresh packs the state the
+ *            following fast steps read.
  *   workspace  as sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent).
  *   Other arguments as sfi_sparse_decode_attn.  Errors: SFI_ERR_INVALID_ARG for a
- *   NULL sel_idx with k > 0, negative k, per_head not 0 or 1, or an unpaired
- *   k_new / v_new; SFI_ERR_UNSUPPORTED when
+ *   NULL sel_idx with k > 0, negative k, per_head not 0 or 1, an unpaired
+ *   k_new / v_new, or a partial or misaligned compact buffer or cap < n_sink + k;
+ *   SFI_ERR_UNSUPPORTED when
  *   num_pages * 16 exceeds INT32_MAX.
  */
 SFI_API sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
                                           const void* k_new, const void* v_new, const int32_t* seq_lens,
                                           int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
-                                          int32_t per_head, float* out, float* lse, void* workspace,
+                                          int32_t per_head, void* compact_k, void* compact_v, int32_t cap,
+                                          int32_t* n_compact, float* out, float* lse, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
 /*

@@ -77,8 +77,8 @@ _SIGS = {
                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p],
     "sfi_sparse_decode_indexed_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
-                                       c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
-                                       c_void_p],
+                                       c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_dense_attn_with_head_stats": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                        c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
     "sfi_mixed_attn": [_SHAPE_P, _KV_P, c_void_p, POINTER(c_int32), POINTER(c_int32), c_void_p, c_int32,
@@ -207,6 +207,29 @@ def _kv(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor, m
                       k_pool.shape[2], k_pool.shape[0], int(max_seq_len))
 
 
+def _check_pool(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor, B: int, d: int) -> int:
+    """The pools' layout against the call's batch and head size; returns the pools' KV heads.
+    The library takes every size from the descriptors it is given, so a tensor that disagrees
+    with the pools would make it address memory outside them."""
+    if k_pool.dim() != 4 or tuple(v_pool.shape) != tuple(k_pool.shape) or k_pool.shape[2] != PAGE_SIZE:
+        raise ValueError("k_pool and v_pool must both be [num_pages, Hkv, 16, d]")
+    if v_pool.dtype != k_pool.dtype:
+        raise TypeError("k_pool and v_pool must share a dtype")
+    if k_pool.shape[3] != d:
+        raise ValueError(f"head size {d} does not match the pools' {k_pool.shape[3]}")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages]")
+    return k_pool.shape[1]
+
+
+def _f32_out(t: Optional[torch.Tensor], shape: tuple, name: str) -> None:
+    if t is None:
+        return
+    _dev(t, name)
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be float32 {tuple(shape)}")
+
+
 def _i32(t: torch.Tensor, name: str) -> None:
     _dev(t, name)
     if t.dtype != torch.int32:
@@ -266,11 +289,17 @@ def dense_attn_with_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     [B, Hkv, score_stride] or None)."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, t_q, Hq, d]")
     B, t_q, Hq, d = q.shape
-    Hkv = k_pool.shape[1]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
+    if q.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens must be [B]")
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     dev = q.device
+    _f32_out(out, (B, t_q, Hq, d), "out")
+    _f32_out(lse, (B, t_q, Hq), "lse")
     if out is None:
         out = torch.empty((B, t_q, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
@@ -278,6 +307,8 @@ def dense_attn_with_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     if with_scores and scores is None:
         stride = int(score_stride if score_stride is not None else max_seq_len)
         scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
+    if scores is not None:
+        _f32_out(scores, (B, Hkv, scores.shape[-1]), "scores")
     stride = scores.shape[-1] if scores is not None else 0
     need = c_size_t(0)
     _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), t_q, ctypes.byref(need))
@@ -307,12 +338,21 @@ def dense_attn_with_refresh(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
     _dev(r_scores, "r_scores")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, 1, Hq, d]")
     B, t_q, Hq, d = q.shape
     if t_q != 1:
         raise ValueError("the refresh launch takes one query token per request")
-    Hkv = k_pool.shape[1]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
     rkv = _kv(r_k_pool, r_v_pool, r_block_table, r_max_seq_len)
+    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
+    if _check_pool(r_k_pool, r_v_pool, r_block_table, B, d) != Hkv:
+        raise ValueError("both layers' pools must hold the same KV heads")
+    if q.dtype != k_pool.dtype or r_k_pool.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q and both layers' pools must share a dtype; seq_lens must be [B]")
+    _f32_out(r_scores, (B, Hkv, r_scores.shape[-1]), "r_scores")
+    _f32_out(out, (B, 1, Hq, d), "out")
+    _f32_out(lse, (B, 1, Hq), "lse")
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     dev = q.device
     if out is None:
@@ -325,6 +365,11 @@ def dense_attn_with_refresh(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
     stride = scores.shape[-1] if scores is not None else 0
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    _i32(sel_idx, "sel_idx")
+    if tuple(sel_idx.shape) != (B, Hkv, k):
+        raise ValueError(f"sel_idx must be [B, Hkv, k] = {(B, Hkv, k)}")
+    if scores is not None:
+        _f32_out(scores, (B, Hkv, scores.shape[-1]), "scores")
     if pack:
         if compact_k is None:
             compact_k = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
@@ -332,6 +377,11 @@ def dense_attn_with_refresh(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
             compact_v = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
         if n_compact is None:
             n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
+        for tt, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+            _dev(tt, n)
+            if tt.dtype != r_k_pool.dtype or tuple(tt.shape) != (B, Hkv, cap, d):
+                raise ValueError(f"{n} must be [B, Hkv, cap, d] in the pool dtype")
+        _i32(n_compact, "n_compact")
     else:
         compact_k = compact_v = n_compact = None
     ref = SfiRefresh(rkv, r_scores.data_ptr(), r_scores.shape[-1], r_n_sink, r_n_recent, k, sel_idx.data_ptr(),
@@ -365,9 +415,13 @@ def pack_compact(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.
     """Gather-pack: -> (compact_k, compact_v [B, Hkv, cap, d], n_compact [B] int32)."""
     _i32(sel_idx, "sel_idx")
     _i32(seq_lens, "seq_lens")
+    if sel_idx.dim() != 3:
+        raise ValueError("sel_idx must be [B, Hkv, k]")
     B, Hkv, k = sel_idx.shape
     d = k_pool.shape[3]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    if _check_pool(k_pool, v_pool, block_table, B, d) != Hkv:
+        raise ValueError(f"sel_idx has {Hkv} rows per request; the pools hold {k_pool.shape[1]} KV heads")
     shape = _shape(B, Hkv, Hkv, d, _dtype_code(k_pool), None)
     dev = k_pool.device
     if compact_k is None:
@@ -376,6 +430,13 @@ def pack_compact(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.
         compact_v = torch.empty((B, Hkv, cap, d), dtype=k_pool.dtype, device=dev)
     if n_compact is None:
         n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
+    for t, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+        _dev(t, n)
+        if t.dtype != k_pool.dtype or tuple(t.shape) != (B, Hkv, cap, d):
+            raise ValueError(f"{n} must be [B, Hkv, cap, d] = {(B, Hkv, cap, d)} in the pool dtype")
+    _i32(n_compact, "n_compact")
+    if tuple(seq_lens.shape) != (B,) or tuple(n_compact.shape) != (B,):
+        raise ValueError("seq_lens and n_compact must be [B]")
     _call("sfi_pack_compact", ctypes.byref(shape), ctypes.byref(kv), seq_lens.data_ptr(), n_sink,
           sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
           _stream(stream, dev))
@@ -403,11 +464,22 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
     _dev(compact_v, "compact_v")
     _i32(seq_lens, "seq_lens")
     _i32(n_compact, "n_compact")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
     B, Hq, d = q.shape
     Hkv, cap = compact_k.shape[1], compact_k.shape[2]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    if _check_pool(k_pool, v_pool, block_table, B, d) != Hkv:
+        raise ValueError(f"compact_k has {Hkv} KV heads; the pools hold {k_pool.shape[1]}")
+    for t, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+        if t.dtype != k_pool.dtype or tuple(t.shape) != (B, Hkv, cap, d):
+            raise ValueError(f"{n} must be [B, Hkv, cap, d] in the pool dtype")
+    if q.dtype != k_pool.dtype or tuple(n_compact.shape) != (B,) or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens and n_compact must be [B]")
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     dev = q.device
+    _f32_out(out, (B, Hq, d), "out")
+    _f32_out(lse, (B, Hq), "lse")
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
@@ -434,11 +506,13 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
                                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                                workspace: Optional[torch.Tensor] = None, stream=None,
                                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
-                               per_head: bool = False):
+                               per_head: bool = False, compact_k: Optional[torch.Tensor] = None,
+                               compact_v: Optional[torch.Tensor] = None, n_compact: Optional[torch.Tensor] = None):
     """Fast step over the positions sel_idx [B, Hkv, k] lists (plus sink and recent), every row
     read in place from paged KV: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq])
     (sfi_sparse_decode_indexed_attn).  With per_head, sel_idx is [B, Hq, k], one set per
-    query head.  k_new / v_new as in sparse_decode_attn."""
+    query head.  k_new / v_new as in sparse_decode_attn.  With compact_k / compact_v
+    [B, units, cap, d] and n_compact [B], the launch also packs them as pack_compact would."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
     _i32(sel_idx, "sel_idx")
@@ -449,16 +523,35 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
             _dev(t, n)
             if t.dtype != k_pool.dtype or tuple(t.shape) != (q.shape[0], k_pool.shape[1], q.shape[2]):
                 raise ValueError(f"{n} must be [B, Hkv, d] in the pool dtype")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
     B, Hq, d = q.shape
-    Hkv = k_pool.shape[1]
+    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
+    if q.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens must be [B]")
     rows = Hq if per_head else Hkv
     if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, rows):
         raise ValueError(f"sel_idx must be [B, {'Hq' if per_head else 'Hkv'}, k]")
     k = sel_idx.shape[2]
+    packing = (compact_k, compact_v, n_compact)
+    if any(t is not None for t in packing) and not all(t is not None for t in packing):
+        raise ValueError("compact_k, compact_v and n_compact go together")
+    cap = 0
+    if compact_k is not None:
+        for t, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+            _dev(t, n)
+            if t.dtype != k_pool.dtype or t.dim() != 4 or tuple(t.shape[:2]) != (B, rows) or t.shape[3] != d:
+                raise ValueError(f"{n} must be [B, units, cap, d] in the pool dtype")
+        if compact_v.shape != compact_k.shape:
+            raise ValueError("compact_v must match compact_k")
+        _i32(n_compact, "n_compact")
+        cap = compact_k.shape[2]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     unit_shape = _shape(B, Hq, rows, d, _dtype_code(q), scale)
     dev = q.device
+    _f32_out(out, (B, Hq, d), "out")
+    _f32_out(lse, (B, Hq), "lse")
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
@@ -468,8 +561,9 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
           ctypes.byref(need))
     ws = _workspace(need.value, workspace, dev)
     _call("sfi_sparse_decode_indexed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), _ptr(k_new),
-          _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, int(per_head), out.data_ptr(),
-          _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream, dev))
+          _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, int(per_head),
+          _ptr(compact_k), _ptr(compact_v), cap, _ptr(n_compact), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
+          _stream(stream, dev))
     return out, lse
 
 
@@ -483,11 +577,17 @@ def dense_attn_with_head_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
     lse [B, Hq], scores [B, Hq, score_stride]) (sfi_dense_attn_with_head_stats)."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
     B, Hq, d = q.shape
-    Hkv = k_pool.shape[1]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
+    if q.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens must be [B]")
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     dev = q.device
+    _f32_out(out, (B, Hq, d), "out")
+    _f32_out(lse, (B, Hq), "lse")
     stride = int(score_stride if score_stride is not None else max_seq_len)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
@@ -517,12 +617,27 @@ def mixed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, bloc
     -> (out [R, Hq, d], lse [R, Hq], scores [B, Hkv, stride] or None)."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
+    _i32(n_compact, "n_compact")
+    if q.dim() != 3:
+        raise ValueError("q must be [R, Hq, d]")
     R, Hq, d = q.shape
     B = len(modes)
+    if len(t_q) != B or sum(int(x) for x in t_q) != R:
+        raise ValueError("t_q must have one entry per request and sum to q's rows")
     Hkv, cap = compact_k.shape[1], compact_k.shape[2]
     kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    if _check_pool(k_pool, v_pool, block_table, B, d) != Hkv:
+        raise ValueError(f"compact_k has {Hkv} KV heads; the pools hold {k_pool.shape[1]}")
+    for tt, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+        _dev(tt, n)
+        if tt.dtype != k_pool.dtype or tuple(tt.shape) != (B, Hkv, cap, d):
+            raise ValueError(f"{n} must be [B, Hkv, cap, d] in the pool dtype")
+    if q.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,) or tuple(n_compact.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens and n_compact must be [B]")
     shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
     dev = q.device
+    _f32_out(out, (R, Hq, d), "out")
+    _f32_out(lse, (R, Hq), "lse")
     m = (c_int32 * B)(*[int(x) for x in modes])
     t = (c_int32 * B)(*[int(x) for x in t_q])
     if out is None:
@@ -532,6 +647,8 @@ def mixed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, bloc
     if with_scores and scores is None:
         stride = int(score_stride if score_stride is not None else max_seq_len)
         scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
+    if scores is not None:
+        _f32_out(scores, (B, Hkv, scores.shape[-1]), "scores")
     stride = scores.shape[-1] if scores is not None else 0
     need = c_size_t(0)
     _call("sfi_mixed_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), m, t, cap, n_recent,

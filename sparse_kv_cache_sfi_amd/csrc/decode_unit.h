@@ -165,13 +165,25 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * NT;
       if (i < cnt) {
-        int sl = -1;
+        // -1: padding (no row); -2: a position past the end or behind an invalid page
+        // (a masked row, packed as zeros)
+        int sl = pos[j] < 0 ? -1 : -2;
         if (pos[j] >= 0 && pos[j] < L) {
           const int e = bt_row[pos[j] >> 4];
           if (e >= 0 && e < a.num_pages) sl = e * kPage + (pos[j] & 15);
         }
         slot_s[i] = sl;
       }
+    }
+    if (a.pack_n && split == 0 && g == 0 && w == 0) {
+      // n_compact of the packed buffer: ns + the entries of unit 0's selection before
+      // its first negative one (as the gather-pack counts them).
+      const int32_t* sel0 = a.sel + (int64_t)b * a.Hkv * a.sel_k;
+      float first = (float)a.sel_k;
+      for (int i = lane; i < a.sel_k; i += kWave)
+        if (sel0[i] < 0) first = fminf(first, (float)i);
+      first = xor_fold<1>(first, [](float x, float y) { return fminf(x, y); });
+      if (lane == 0) a.pack_n[b] = ns + (int)first;
     }
   }
   __syncthreads();
@@ -297,6 +309,21 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       int vi, pg;
       bool compact;
       locate(it, u, vi, pos_[u], in_[u], compact, pg, ok_[u]);
+      if constexpr (INDEXED) {
+        // Pack while attending: the row just loaded goes to its compact slot vi
+        // (zeros for a masked position, nothing for padding).
+        if (a.pack_k && in_[u] && compact && pos_[u] != -1) {
+          const int64_t dst = (((int64_t)b * a.Hkv + g) * a.pack_cap + vi) * D;
+          T* dk = reinterpret_cast<T*>(a.pack_k) + dst;
+          T* dv = reinterpret_cast<T*>(a.pack_v) + dst;
+          const bool real = pos_[u] >= 0;
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            *reinterpret_cast<u32x4*>(dk + (c * LPR + sub) * EPC) = real ? B.k[u][c] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(dv + (c * LPR + sub) * EPC) = real ? B.v[u][c] : u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
     }
     float s[U][G];
 #pragma unroll

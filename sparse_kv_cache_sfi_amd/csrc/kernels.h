@@ -74,6 +74,13 @@ struct AttnArgs {
   // Slow step: write one logit row per query head ([B, Hq, score_stride]) instead of
   // the group sums.
   int32_t head_scores;
+  // Index-set fast step that also packs (nullable): the sink and selected rows it
+  // reads are written to pack_k / pack_v [B, units, pack_cap, d] exactly as the
+  // gather-pack would, and pack_n[b] as its n_compact.
+  void* pack_k;
+  void* pack_v;
+  int32_t* pack_n;
+  int32_t pack_cap;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves

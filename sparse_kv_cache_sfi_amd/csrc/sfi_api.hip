@@ -498,7 +498,8 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
                        const void* v_new, const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
                        const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
                        const int32_t* sel, int32_t sel_k, bool per_head, float* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, void* pack_k = nullptr, void* pack_v = nullptr,
+                       int32_t pack_cap = 0, int32_t* pack_n = nullptr) {
   SFI_TRY(check_shape(shape_in));
   // One unit per query head when each query head has its own selection: the units see
   // a shape with as many KV heads as query heads, head_div of them per pool head.
@@ -548,6 +549,10 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
   a.sel = sel;
   a.sel_k = sel_k;
   a.head_div = head_div;
+  a.pack_k = pack_k;
+  a.pack_v = pack_v;
+  a.pack_n = pack_n;
+  a.pack_cap = pack_cap;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
@@ -581,9 +586,17 @@ sfi_status sfi_sparse_decode_append_attn(const sfi_shape* shape, const sfi_paged
 sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
                                           const void* k_new, const void* v_new, const int32_t* seq_lens,
                                           int32_t n_sink, int32_t n_recent, const int32_t* sel_idx, int32_t k,
-                                          int32_t per_head, float* out, float* lse, void* workspace,
+                                          int32_t per_head, void* compact_k, void* compact_v, int32_t cap,
+                                          int32_t* n_compact, float* out, float* lse, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   if (per_head != 0 && per_head != 1) return fail(SFI_ERR_INVALID_ARG, "per_head must be 0 or 1");
+  if (compact_k || compact_v || n_compact) {
+    SFI_TRY(check_ptr16(compact_k, "compact_k"));
+    SFI_TRY(check_ptr16(compact_v, "compact_v"));
+    if (!n_compact) return fail(SFI_ERR_INVALID_ARG, "n_compact is NULL (compact_k, compact_v and n_compact go together)");
+    if ((int64_t)cap < (int64_t)n_sink + k)
+      return fail(SFI_ERR_INVALID_ARG, "cap (%d) must be >= n_sink + k (%lld)", cap, (long long)n_sink + k);
+  }
   if (k < 0) return fail(SFI_ERR_INVALID_ARG, "k must be >= 0");
   if (!sel_idx && k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
   if (!k_new != !v_new) return fail(SFI_ERR_INVALID_ARG, "k_new and v_new must both be NULL or both be set");
@@ -592,7 +605,8 @@ sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_page
     SFI_TRY(check_ptr16(v_new, "v_new"));
   }
   return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, nullptr, nullptr, 0, nullptr, sel_idx,
-                     k, per_head == 1, out, lse, workspace, workspace_bytes, stream);
+                     k, per_head == 1, out, lse, workspace, workspace_bytes, stream, compact_k, compact_v, cap,
+                     n_compact);
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

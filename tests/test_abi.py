@@ -183,10 +183,12 @@ def test_sparse_append_rejects_bad_arguments(lib):
 def test_sparse_indexed_rejects_bad_arguments(lib):
     shape = _shape()
 
-    def call(sel=FAKE, k=64, kn=None, vn=None, q=FAKE, ws_bytes=1 << 40, kv=None, out=FAKE, per_head=0):
+    def call(sel=FAKE, k=64, kn=None, vn=None, q=FAKE, ws_bytes=1 << 40, kv=None, out=FAKE, per_head=0, ck=None,
+             cap=0, nc=None):
         kv = kv or _kv()
         return lib.sfi_sparse_decode_indexed_attn(ctypes.byref(shape), ctypes.byref(kv), q, kn, vn, FAKE, 4, 64, sel,
-                                                  k, per_head, out, FAKE, FAKE, ws_bytes, None)
+                                                  k, per_head, ck, FAKE if ck else None, cap, nc, out, FAKE, FAKE,
+                                                  ws_bytes, None)
     assert call(sel=0) == 1 and "sel_idx is NULL" in lib.sfi_last_error().decode()
     assert call(k=-1) == 1 and "k must be" in lib.sfi_last_error().decode()
     assert call(kn=FAKE) == 1 and "both" in lib.sfi_last_error().decode()
@@ -197,6 +199,10 @@ def test_sparse_indexed_rejects_bad_arguments(lib):
     assert call(kv=_kv(num_pages=1 << 27)) == 2 and "slots" in lib.sfi_last_error().decode()
     assert call(per_head=2) == 1 and "per_head" in lib.sfi_last_error().decode()
     assert call(per_head=1, k=20000, ws_bytes=1) == 3
+    assert call(ck=FAKE, cap=68) == 1 and "go together" in lib.sfi_last_error().decode()
+    assert call(ck=FAKE, cap=67, nc=FAKE) == 1 and "cap" in lib.sfi_last_error().decode()
+    assert call(ck=MISALIGNED, cap=68, nc=FAKE) == 1 and "aligned" in lib.sfi_last_error().decode()
+    assert call(ck=FAKE, cap=20004, nc=FAKE, k=20000, ws_bytes=1) == 3
 
 
 def test_dense_head_stats_rejects_bad_arguments(lib):

@@ -199,3 +199,130 @@ def test_draft_refresh_driver_matches_the_oracle_loop(gpu_lib, refresh_layer):
             for layer, (ro, rl) in enumerate(layer_res):
                 assert_close(outs[t][layer, b], ro, OUT_TOL, f"out t={t} layer={layer} b={b}")
                 assert_close(lses[t][layer, b], rl, LSE_TOL, f"lse t={t} layer={layer} b={b}")
+
+
+# --------------------------------------------------------------------------- packing while attending
+
+def _sentinel_like(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).fill_(0x3f3f)
+    return t
+
+
+PACK_CASES = [
+    ("bf16_g2_ragged_padded", lambda: make_case(311, name="pk_a", B=3, Hq=16, Hkv=8, d=128, dtype="bf16",
+                                                 seq_lens=[300, 5000, 2047], n_sink=4, n_recent=64, k_sel=600),
+     600, 37, False),
+    ("f32_g2", lambda: make_case(312, name="pk_b", B=2, Hq=4, Hkv=2, d=128, dtype="f32", seq_lens=[900, 1200],
+                                  n_sink=4, n_recent=32, k_sel=200), 200, 0, False),
+    ("bf16_g4_per_head", lambda: make_case(313, name="pk_c", B=2, Hq=16, Hkv=4, d=128, dtype="bf16",
+                                            seq_lens=[2500, 900], n_sink=4, n_recent=64, k_sel=128), 128, 0, True),
+]
+
+
+@pytest.mark.parametrize("name,mk,k,pad,per_head", PACK_CASES, ids=[n[0] for n in PACK_CASES])
+def test_indexed_fast_step_packs_exactly_like_pack_compact(gpu_lib, name, mk, k, pad, per_head):
+    c = mk()
+    dc = DevCase(c)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    units = c.Hq if per_head else c.Hkv
+    L = c.seq_lens.astype(np.int32)
+    sels = []
+    for b in range(c.B):
+        s_ = np.concatenate([_selection(rng, c, int(L[b]), k, pad) for _ in range(units // c.Hkv)])
+        sels.append(s_)
+    sel = np.stack(sels).astype(np.int32)
+    if not per_head:
+        sel[0, 0, 5] = int(L[0]) + 3            # past the end: a zero row
+        sel[min(1, c.B - 1), 1, 7] = -1         # padding in the middle: no row
+    sel_d = dev_array(sel)
+    cap = c.n_sink + k + 2
+    kdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    kw = dict(n_sink=c.n_sink, n_recent=c.n_recent, max_seq_len=dc.max_seq_len, scale=c.scale, per_head=per_head)
+    q1 = dc.q[:, 0].contiguous()
+    ck1, cv1 = _sentinel_like((c.B, units, cap, c.d), kdt), _sentinel_like((c.B, units, cap, c.d), kdt)
+    nc1 = torch.full((c.B,), -5, dtype=torch.int32, device=DEV)
+    o1, l1 = gpu_lib.sparse_decode_indexed_attn(q1, dc.k, dc.v, dc.bt, dc.lens, sel_d, compact_k=ck1,
+                                                compact_v=cv1, n_compact=nc1, **kw)
+    o0, l0 = gpu_lib.sparse_decode_indexed_attn(q1, dc.k, dc.v, dc.bt, dc.lens, sel_d, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    ibits = torch.int16 if kdt == torch.bfloat16 else torch.int32
+    if per_head:
+        # the gather-pack has no per-query-head form: the reference packs each query head's set from its
+        # KV head's rows on the host (pools with every KV head repeated for its G query heads)
+        kr, vr = np.repeat(c.kv.k, c.G, axis=1), np.repeat(c.kv.v, c.G, axis=1)
+        got_k, got_v, got_n = host_bits(ck1), host_bits(cv1), nc1.cpu().numpy()
+        for b in range(c.B):
+            rck, rcv, rnc = O.pack_compact(kr, vr, c.kv.block_table[b], int(L[b]), c.n_sink, sel[b], cap)
+            assert got_n[b] == rnc, b
+            assert np.array_equal(got_k[b, :, :rnc], rck[:, :rnc]) and np.array_equal(got_v[b, :, :rnc], rcv[:, :rnc])
+        return
+    ck2, cv2 = _sentinel_like((c.B, units, cap, c.d), kdt), _sentinel_like((c.B, units, cap, c.d), kdt)
+    nc2 = torch.full((c.B,), -5, dtype=torch.int32, device=DEV)
+    gpu_lib.pack_compact(dc.k, dc.v, dc.bt, dc.lens, sel_d, n_sink=c.n_sink, cap=cap, max_seq_len=dc.max_seq_len,
+                         compact_k=ck2, compact_v=cv2, n_compact=nc2)
+    torch.cuda.synchronize()
+    assert torch.equal(nc1, nc2)
+    assert torch.equal(ck1.view(ibits), ck2.view(ibits))
+    assert torch.equal(cv1.view(ibits), cv2.view(ibits))
+    # and the packed buffer serves the compact fast step like any other
+    if pad == 0:
+        o2, l2 = gpu_lib.sparse_decode_attn(q1, dc.k, dc.v, dc.bt, dc.lens, ck1, cv1, nc1, n_sink=c.n_sink,
+                                            n_recent=c.n_recent, max_seq_len=dc.max_seq_len, scale=c.scale)
+        torch.cuda.synchronize()
+        qv = c.q_values()[:, 0]
+        for b in range(c.B):
+            rck, rcv, rnc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], int(L[b]), c.n_sink, sel[b], cap)
+            ro, rl = O.sparse_decode(qv[b], rck, rcv, rnc, c.kv.k, c.kv.v, c.kv.block_table[b], int(L[b]),
+                                     c.n_sink, c.n_recent, c.scale, kv_dtype=c.dtype)
+            assert_close(o2.cpu().numpy()[b], ro, OUT_TOL, f"compact after fused pack b={b}")
+
+
+def test_indexed_pack_with_invalid_pages_and_append(gpu_lib):
+    c = make_case(314, name="pk_d", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", seq_lens=[700, 1300],
+                  capacity=[710, 1310], n_sink=4, n_recent=32, k_sel=64)
+    dc = DevCase(c)
+    bt = c.kv.block_table.copy()
+    bt[0, 20] = -1
+    bt[1, 5] = c.kv.num_pages + 9
+    bt_d = dev_array(bt)
+    rng = np.random.default_rng(15)
+    sel = np.stack([_selection(rng, c, int(c.seq_lens[b]), 64) for b in range(2)]).astype(np.int32)
+    sel[0, 1, 3] = 325                              # on the invalid page: a zero row
+    sel_d = dev_array(sel)
+    L = (c.seq_lens + 1).astype(np.int32)
+    lens = dc.lens_tensor(L)
+    x = rng.standard_normal((2, 2, 2, 128)).astype(np.float32)
+    kn, vn = dev_array(bf16_bits(x[0])), dev_array(bf16_bits(x[1]))
+    ck1, cv1 = _sentinel_like((2, 2, 68, 128), torch.bfloat16), _sentinel_like((2, 2, 68, 128), torch.bfloat16)
+    nc1 = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    kw = dict(n_sink=4, n_recent=32, max_seq_len=dc.max_seq_len, scale=c.scale)
+    o1, l1 = gpu_lib.sparse_decode_indexed_attn(dc.q[:, 0].contiguous(), dc.k, dc.v, bt_d, lens, sel_d, k_new=kn,
+                                                v_new=vn, compact_k=ck1, compact_v=cv1, n_compact=nc1, **kw)
+    ck2, cv2 = _sentinel_like((2, 2, 68, 128), torch.bfloat16), _sentinel_like((2, 2, 68, 128), torch.bfloat16)
+    nc2 = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    gpu_lib.pack_compact(dc.k, dc.v, bt_d, lens, sel_d, n_sink=4, cap=68, max_seq_len=dc.max_seq_len,
+                         compact_k=ck2, compact_v=cv2, n_compact=nc2)
+    torch.cuda.synchronize()
+    assert torch.equal(nc1, nc2)
+    assert torch.equal(ck1.view(torch.int16), ck2.view(torch.int16))
+    assert torch.equal(cv1.view(torch.int16), cv2.view(torch.int16))
+
+
+def test_binding_rejects_selections_and_buffers_that_disagree_with_the_pools(gpu_lib):
+    """Sizes the library takes from its descriptors must agree with the pools; the binding refuses a
+    mismatch before anything is launched (a per-query-head selection is not a gather-pack input)."""
+    c = make_case(315, name="pk_e", B=2, Hq=16, Hkv=4, d=128, dtype="bf16", seq_lens=[600, 900], n_sink=4,
+                  n_recent=32, k_sel=16)
+    dc = DevCase(c)
+    per_head_sel = torch.zeros((2, 16, 16), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="KV heads"):
+        gpu_lib.pack_compact(dc.k, dc.v, dc.bt, dc.lens, per_head_sel, n_sink=4, cap=20, max_seq_len=dc.max_seq_len)
+    wrong = torch.zeros((2, 16, 20, 128), dtype=torch.bfloat16, device=DEV)
+    nc = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="KV heads"):
+        gpu_lib.sparse_decode_attn(dc.q[:, 0].contiguous(), dc.k, dc.v, dc.bt, dc.lens, wrong, wrong, nc, n_sink=4,
+                                   n_recent=32, max_seq_len=dc.max_seq_len)
+    with pytest.raises(ValueError, match="block_table"):
+        gpu_lib.dense_attn_with_stats(dc.q[:1], dc.k, dc.v, dc.bt, dc.lens[:1], max_seq_len=dc.max_seq_len)
