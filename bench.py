@@ -285,6 +285,8 @@ def main():
     }
 
     result["riders_16k"] = riders_16k(sfi, layers, main_s, k_sel, cap, n_sink, n_recent, max_len, ws_dense)
+    result["fused_pack_step"] = fused_pack_steps(sfi, layers, dev, args.steps, k_sel, cap, n_sink, n_recent, max_len,
+                                                 ws_dense, ws_sparse)
     result["hip_graph"] = graph_steps(sfi, layers, dev, args.steps, step_bytes, k_sel, cap, n_sink, n_recent,
                                       max_len, ws_dense, ws_sparse)
 
@@ -933,6 +935,45 @@ def riders_16k(sfi, layers, stream, k_sel, cap, n_sink, n_recent, max_len, ws_de
            "hidden_fraction": round(max(0.0, min(1.0, (t_ser - t_fus) / t_sel)), 3),
            "matches_separate_calls": same}
     log(f"riders 16K {res}")
+    return res
+
+
+def fused_pack_steps(sfi, layers, dev, steps, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
+    """The same step with the pack fused into the fast step: slow step -> Selector -> one launch that
+    attends over sink + selected + recent read in place and writes the compact buffer as it goes
+    (sfi_sparse_decode_indexed_attn with a compact buffer).  Outputs, selection and compact buffer must
+    equal the four-launch step's bit for bit."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    R = len(layers)
+    B, Hq, d = layers[0]["q1"].shape
+    Hkv = layers[0]["k"].shape[1]
+    calls = []
+    for ly in layers:
+        fz = {"ck": torch.empty_like(ly["ck"]), "cv": torch.empty_like(ly["cv"]), "nc": torch.empty_like(ly["nc"]),
+              "out": torch.empty_like(ly["fout"]), "lse": torch.empty_like(ly["flse"])}
+        ly["fused"] = fz
+        calls.append((ly["dense"], ly["select"],
+                      sfi.bind(sfi.sparse_decode_indexed_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"],
+                               ly["sel"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=fz["out"],
+                               lse=fz["lse"], workspace=ws_sparse, stream=stream, compact_k=fz["ck"],
+                               compact_v=fz["cv"], n_compact=fz["nc"])))
+
+    def step(i):
+        for c in calls[i % R]:
+            c()
+    for i in range(R):
+        step(i)
+        layers[i]["pack"]()
+        layers[i]["fast"]()
+    torch.cuda.synchronize()
+    same = all(torch.equal(ly["fused"]["out"], ly["fout"]) and torch.equal(ly["fused"]["lse"], ly["flse"])
+               and torch.equal(ly["fused"]["nc"], ly["nc"])
+               and torch.equal(ly["fused"]["ck"].view(torch.int16), ly["ck"].view(torch.int16))
+               and torch.equal(ly["fused"]["cv"].view(torch.int16), ly["cv"].view(torch.int16)) for ly in layers)
+    t = time_loop(step, steps, stream)
+    res = {"ms_per_step": round(t * 1e3, 5), "launches_per_step": 3, "matches_four_launch_step": bool(same)}
+    log(f"fused-pack step {res}")
     return res
 
 
