@@ -200,12 +200,16 @@ def pack_compact(k_pool: np.ndarray, v_pool: np.ndarray, block_table_row: np.nda
     n_c = ns_eff + k_eff
     ck = np.zeros((Hkv, cap, d), dtype=k_pool.dtype)
     cv = np.zeros((Hkv, cap, d), dtype=v_pool.dtype)
+    bt = np.asarray(block_table_row, dtype=np.int64)
     for g in range(Hkv):
         pos = np.concatenate([np.arange(ns_eff), np.asarray(sel[g][:k_eff], dtype=np.int64)])
-        for i, p in enumerate(pos):
-            if 0 <= p < L and _valid_page(block_table_row, int(p), num_pages, page_size):
-                ck[g, i] = paged_rows(k_pool, block_table_row, g, [p], page_size)[0]
-                cv[g, i] = paged_rows(v_pool, block_table_row, g, [p], page_size)[0]
+        inside = (pos >= 0) & (pos < L)
+        page = np.full(len(pos), -1, dtype=np.int64)
+        page[inside] = bt[pos[inside] // page_size]
+        ok = inside & (page >= 0) & (page < num_pages)
+        rows = np.flatnonzero(ok)
+        ck[g, rows] = paged_rows(k_pool, bt, g, pos[ok], page_size)
+        cv[g, rows] = paged_rows(v_pool, bt, g, pos[ok], page_size)
     return ck, cv, n_c
 
 
