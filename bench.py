@@ -285,6 +285,24 @@ def main():
     }
 
     result["riders_16k"] = riders_16k(sfi, layers, main_s, k_sel, cap, n_sink, n_recent, max_len, ws_dense)
+    # every kernel of the step back to back over the replicas (HIP events on its stream)
+    kern = {}
+    for name in ("select", "pack", "fast"):
+        for i in range(R):
+            layers[i][name]()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record(main_s)
+        for i in range(n_b2b):
+            layers[i % R][name]()
+        k1.record(main_s)
+        torch.cuda.synchronize()
+        kern[name + "_us"] = round(k0.elapsed_time(k1) * 1e3 / n_b2b, 2)
+    kern["dense_us"] = round(dense_s * 1e6, 2)
+    kern["select_GBps"] = round(B * Hkv * (L - n_sink - n_recent) * 4 / kern["select_us"] / 1e3, 1)
+    kern["pack_GBps"] = round(pack_bytes / kern["pack_us"] / 1e3, 1)
+    kern["fast_GBps"] = round(fast_kv / kern["fast_us"] / 1e3, 1)
+    result["step_kernels"] = kern
+    log(f"step kernels {kern}")
     result["fused_pack_step"] = fused_pack_steps(sfi, layers, dev, args.steps, k_sel, cap, n_sink, n_recent, max_len,
                                                  ws_dense, ws_sparse)
     result["hip_graph"] = graph_steps(sfi, layers, dev, args.steps, step_bytes, k_sel, cap, n_sink, n_recent,
