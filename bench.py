@@ -197,32 +197,46 @@ def main():
                                scores=ly["scores"], workspace=ws_dense, stream=main_s)
         ly["select"] = sfi.bind(sfi.select_topk, ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink,
                                 n_recent=n_recent, sel_idx=ly["sel"], stream=aux_s)
+        # The step's slow step leaves its split-K combine to the pack launch (same outputs, bit for
+        # bit, as the plain slow step and pack).
+        ly["dense_d"] = sfi.bind(sfi.dense_attn_with_stats_deferred, ly["q"], ly["k"], ly["v"], ly["bt"],
+                                 ly["lens"], max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, out=ly["out"],
+                                 lse=ly["lse"], scores=ly["scores"], workspace=ws_dense, stream=main_s)
         ly["pack"] = sfi.bind(sfi.pack_compact, ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink,
                               cap=cap, max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"],
                               n_compact=ly["nc"], stream=aux_s)
+        ly["pack_m"] = sfi.bind(sfi.pack_compact_merge, ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"],
+                                n_sink=n_sink, cap=cap, max_seq_len=max_len, out=ly["out"], lse=ly["lse"],
+                                workspace=ws_dense, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
+                                stream=main_s)
         ly["fast"] = sfi.bind(sfi.sparse_decode_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"],
                               ly["cv"], ly["nc"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
                               out=ly["fout"], lse=ly["flse"], workspace=ws_sparse, stream=main_s)
     dense_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
+                for _ in range(R)]
     sync_ev = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(args.steps + args.warmup)]
 
     def step(i, record=None):
         ly = layers[i % R]
+        aux = aux_s is not main_s
         if record is not None:
             dense_ev[record][0].record(main_s)
-        ly["dense"]()
+        # On one stream the pack launch finishes the slow step; with the maintenance on a second
+        # stream the slow step merges its own splits.
+        (ly["dense"] if aux else ly["dense_d"])()
         if record is not None:
             dense_ev[record][1].record(main_s)
-        if aux_s is not main_s:
+        if aux:
             ready, packed = sync_ev[i]
             ready.record(main_s)
             aux_s.wait_event(ready)
-        ly["select"]()
-        ly["pack"]()
-        if aux_s is not main_s:
+            ly["select"]()
+            ly["pack"]()
             packed.record(aux_s)
             main_s.wait_event(packed)
+        else:
+            ly["select"]()
+            ly["pack_m"]()
         ly["fast"]()
 
     log(f"warmup {args.warmup} steps")
@@ -234,24 +248,32 @@ def main():
     torch.cuda.synchronize()
     t0e.record(main_s)
     for i in range(args.steps):
-        step(args.warmup + i, record=i)
+        step(args.warmup + i)
     t1e.record(main_s)
     torch.cuda.synchronize()
     step_s = t0e.elapsed_time(t1e) * 1e-3 / args.steps
+    # The slow-step launch inside the step, between events recorded around it (outside the timed
+    # steps: each event adds a stream command of its own).
+    for i in range(R):
+        step(i, record=i)
+    torch.cuda.synchronize()
     in_step_dense_s = float(np.mean([a.elapsed_time(b) for a, b in dense_ev])) * 1e-3
     # The slow-step kernel's own duration: the same bound launches back to back over the replicas
     # (events on its stream).  Inside the step its event pair also spans the dispatch gap after the
     # previous kernel, which rocprofv3's kernel durations do not count.
     n_b2b = 20 * R
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(R):
-        layers[i]["dense"]()
-    b0.record(main_s)
-    for i in range(n_b2b):
-        layers[i % R]["dense"]()
-    b1.record(main_s)
-    torch.cuda.synchronize()
-    dense_s = b0.elapsed_time(b1) * 1e-3 / n_b2b
+
+    def b2b(name):
+        for i in range(R):
+            layers[i][name]()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(main_s)
+        for i in range(n_b2b):
+            layers[i % R][name]()
+        b1.record(main_s)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) * 1e-3 / n_b2b
+    dense_s = b2b("dense_d")
 
     esize = 2
     n_c = cap
@@ -262,7 +284,8 @@ def main():
     value = step_bytes / step_s / 1e9
     dense_alg = dense_kv + B * Hkv * L * 4            # K/V read + scores written
     traffic, traffic_src = profiled_traffic()
-    roof = {"kernel": "decode_kernel<bf16, d128, G2, dense + group logits> (slow step)", "bound": "hbm",
+    roof = {"kernel": "decode_kernel<bf16, d128, G2, dense + group logits> (slow step; its split-K combine "
+                      "runs in the pack launch)", "bound": "hbm",
             "achieved": dense_alg / dense_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
             "traffic_source": traffic_src, "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6,
@@ -277,17 +300,19 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: B=1, Hq=16, Hkv=8, d=128, page 16, "
                                "sink 4, recent 64, selected 1980 (12.5% retention); step = slow step "
-                               "(dense + logits) + Selector + pack + fast step"
+                               "(dense + logits) + Selector + pack (which also combines the slow step's splits) "
+                               "+ fast step"
                                + (" (Selector and pack on a second stream)" if args.aux_stream else ""),
                    "global_batch": B, "seq_len": L, "replicas": R, "step_kv_bytes": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roof,
     }
 
+    result["separate_combine_step"] = separate_combine_step(layers, main_s, args.steps, step_bytes, b2b)
     result["riders_16k"] = riders_16k(sfi, layers, main_s, k_sel, cap, n_sink, n_recent, max_len, ws_dense)
     # every kernel of the step back to back over the replicas (HIP events on its stream)
     kern = {}
-    for name in ("select", "pack", "fast"):
+    for name in ("select", "pack_m", "fast"):
         for i in range(R):
             layers[i][name]()
         k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -298,6 +323,7 @@ def main():
         torch.cuda.synchronize()
         kern[name + "_us"] = round(k0.elapsed_time(k1) * 1e3 / n_b2b, 2)
     kern["dense_us"] = round(dense_s * 1e6, 2)
+    kern["pack_us"] = kern.pop("pack_m_us")
     kern["select_GBps"] = round(B * Hkv * (L - n_sink - n_recent) * 4 / kern["select_us"] / 1e3, 1)
     kern["pack_GBps"] = round(pack_bytes / kern["pack_us"] / 1e3, 1)
     kern["fast_GBps"] = round(fast_kv / kern["fast_us"] / 1e3, 1)
@@ -956,6 +982,37 @@ def riders_16k(sfi, layers, stream, k_sel, cap, n_sink, n_recent, max_len, ws_de
     return res
 
 
+def separate_combine_step(layers, stream, steps, step_bytes, b2b):
+    """The step with the slow step's own split-K combine (sfi_dense_attn_with_stats, sfi_select_topk,
+    sfi_pack_compact, fast step): its time, its slow-step and pack kernels back to back, and whether the
+    step's outputs (slow-step output and lse, logits, selection, compact buffer, fast-step output) equal
+    those of the step whose pack launch finishes the slow step, bit for bit."""
+    import torch
+    R = len(layers)
+    names = ("out", "lse", "scores", "sel", "ck", "cv", "nc", "fout", "flse")
+    deferred, plain = ("dense_d", "select", "pack_m", "fast"), ("dense", "select", "pack", "fast")
+
+    def run(ly, calls):
+        for c in calls:
+            ly[c]()
+    same = True
+    for ly in layers:
+        run(ly, deferred)
+        torch.cuda.synchronize()
+        ref = {n: ly[n].clone() for n in names}
+        for n in names:
+            ly[n].zero_()
+        run(ly, plain)
+        torch.cuda.synchronize()
+        same &= all(torch.equal(ref[n].view(torch.uint8), ly[n].view(torch.uint8)) for n in names)
+    t = time_loop(lambda i: run(layers[i % R], plain), steps, stream)
+    res = {"ms_per_step": round(t * 1e3, 5), "value": round(step_bytes / t / 1e9, 2),
+           "dense_us": round(b2b("dense") * 1e6, 2), "pack_us": round(b2b("pack") * 1e6, 2),
+           "outputs_match_combine_in_pack": bool(same)}
+    log(f"separate-combine step {res}")
+    return res
+
+
 def fused_pack_steps(sfi, layers, dev, steps, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
     """The same step with the pack fused into the fast step: slow step -> Selector -> one launch that
     attends over sink + selected + recent read in place and writes the compact buffer as it goes
@@ -1004,12 +1061,13 @@ def graph_steps(sfi, layers, dev, steps, step_bytes, k_sel, cap, n_sink, n_recen
     side = torch.cuda.Stream(device=dev)
 
     def run(ly):
-        sfi.dense_attn_with_stats(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
-                                  n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
-                                  scores=ly["scores"], workspace=ws_dense)
+        sfi.dense_attn_with_stats_deferred(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
+                                           n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
+                                           scores=ly["scores"], workspace=ws_dense)
         sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"])
-        sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
-                         max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"])
+        sfi.pack_compact_merge(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
+                               max_seq_len=max_len, out=ly["out"], lse=ly["lse"], workspace=ws_dense,
+                               compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"])
         sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"], ly["cv"], ly["nc"],
                                n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=ly["fout"],
                                lse=ly["flse"], workspace=ws_sparse)

@@ -493,7 +493,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       }
     }
   }
-  if (a.n_split > 1)
+  if (a.n_split > 1 && !a.defer_merge)
     SplitTail<D>::run(a, b, g, q_row0, G, G, kMaxSplits, reinterpret_cast<int*>(wml + WAVES * G * 2),
                       wml + WAVES * G * 2 + 4);
 }

@@ -81,6 +81,9 @@ struct AttnArgs {
   void* pack_v;
   int32_t* pack_n;
   int32_t pack_cap;
+  // Leave the split partials for a later launch to merge (no arrival ticket, out and
+  // lse are not written when there is more than one split).
+  int32_t defer_merge;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves
@@ -128,10 +131,12 @@ hipError_t launch_mixed(const AttnArgs& a, const MixedPlan& plan, int d, int G, 
 hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, const int32_t* seq_lens,
                          int t_q, int n_sink, int n_recent, int k, int32_t* sel,
                          hipStream_t stream);
+// merge (nullable): a slow step's split partials for the launch to combine into
+// out / lse as well (head dim d), one extra work-group per (request, KV head).
 hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_pages, int num_pages, int max_seq_len,
                        const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck,
-                       void* cv, int cap, int32_t* n_compact, hipStream_t stream);
+                       void* cv, int cap, int32_t* n_compact, hipStream_t stream, const AttnArgs* merge = nullptr);
 hipError_t launch_dense_refresh(const AttnArgs& a, const RefreshArgs& r, int dtype, int d, int G, int B,
                                 hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

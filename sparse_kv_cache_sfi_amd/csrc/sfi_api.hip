@@ -281,7 +281,7 @@ namespace {
 sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q, int32_t t_q,
                       const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out, float* lse,
                       float* scores, int64_t score_stride, bool head_scores, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, bool defer_merge = false) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
   SFI_TRY(check_ptr16(q, "q"));
@@ -320,6 +320,7 @@ sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void
   a.scores = scores;
   a.score_stride = score_stride;
   a.head_scores = head_scores ? 1 : 0;
+  a.defer_merge = defer_merge ? 1 : 0;
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -328,6 +329,25 @@ sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void
   else
     e = sfi::launch_verify(a, shape->head_dim, G, shape->batch, st);
   return hip_status(e, "attention launch");
+}
+
+sfi_status pack_call(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens, int32_t n_sink,
+                     const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v, int32_t cap,
+                     int32_t* n_compact, void* stream, const sfi::AttnArgs* merge = nullptr) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (!seq_lens || !sel_idx || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens, sel_idx and n_compact must be non-NULL");
+  SFI_TRY(check_ptr16(compact_k, "compact_k"));
+  SFI_TRY(check_ptr16(compact_v, "compact_v"));
+  if (k < 1) return fail(SFI_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (n_sink < 0) return fail(SFI_ERR_INVALID_ARG, "n_sink must be >= 0");
+  if ((int64_t)cap < (int64_t)n_sink + k)
+    return fail(SFI_ERR_INVALID_ARG, "cap (%d) must be >= n_sink + k (%lld)", cap, (long long)n_sink + k);
+  const hipError_t e = sfi::launch_pack(shape->dtype, shape->head_dim, shape->batch, shape->num_kv_heads, kv->k, kv->v,
+                                        kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len, seq_lens,
+                                        n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact,
+                                        static_cast<hipStream_t>(stream), merge);
+  return hip_status(e, "pack launch");
 }
 
 }  // namespace
@@ -340,6 +360,15 @@ sfi_status sfi_dense_attn_with_stats(const sfi_shape* shape, const sfi_paged_kv*
                                      size_t workspace_bytes, void* stream) {
   return dense_call(shape, kv, q, t_q, seq_lens, n_sink, n_recent, out, lse, scores, score_stride, false, workspace,
                     workspace_bytes, stream);
+}
+
+sfi_status sfi_dense_attn_with_stats_deferred(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                              const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
+                                              float* lse, float* scores, int64_t score_stride, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  if (!scores) return fail(SFI_ERR_INVALID_ARG, "scores is NULL (the Selector that finishes the call reads them)");
+  return dense_call(shape, kv, q, 1, seq_lens, n_sink, n_recent, out, lse, scores, score_stride, false, workspace,
+                    workspace_bytes, stream, true);
 }
 
 sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
@@ -458,23 +487,35 @@ sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_he
   return hip_status(e, "select launch");
 }
 
+
 sfi_status sfi_pack_compact(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens, int32_t n_sink,
                             const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v, int32_t cap,
                             int32_t* n_compact, void* stream) {
+  return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream);
+}
+
+sfi_status sfi_pack_compact_merge(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens,
+                                  int32_t n_sink, const int32_t* sel_idx, int32_t k, void* compact_k,
+                                  void* compact_v, int32_t cap, int32_t* n_compact, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
-  if (!seq_lens || !sel_idx || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens, sel_idx and n_compact must be non-NULL");
-  SFI_TRY(check_ptr16(compact_k, "compact_k"));
-  SFI_TRY(check_ptr16(compact_v, "compact_v"));
-  if (k < 1) return fail(SFI_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
-  if (n_sink < 0) return fail(SFI_ERR_INVALID_ARG, "n_sink must be >= 0");
-  if ((int64_t)cap < (int64_t)n_sink + k)
-    return fail(SFI_ERR_INVALID_ARG, "cap (%d) must be >= n_sink + k (%lld)", cap, (long long)n_sink + k);
-  const hipError_t e = sfi::launch_pack(shape->dtype, shape->head_dim, shape->batch, shape->num_kv_heads, kv->k, kv->v,
-                                        kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len, seq_lens,
-                                        n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact,
-                                        static_cast<hipStream_t>(stream));
-  return hip_status(e, "pack launch");
+  SFI_TRY(check_ptr16(out, "out"));
+  // The partials are laid out as the deferred slow step of the same shape left them.
+  const Split sp = plan_dense(shape, kv, 1);
+  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
+  SFI_TRY(check_unit_span(shape, 1, sp.n));
+  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
+  if (sp.n <= 1)   // the slow step wrote out and lse itself
+    return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream);
+  sfi::AttnArgs m = base_args(shape, kv, seq_lens);
+  m.n_split = sp.n;
+  m.split_tokens = sp.tokens;
+  m.t_q = 1;
+  m.out = out;
+  m.lse = lse;
+  set_partials(m, workspace, rows, shape->head_dim);
+  return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream, &m);
 }
 
 sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, int32_t cap,

@@ -67,6 +67,58 @@ struct SplitTail {
     return (int64_t)(q_row0 + r / G) * a.Hq + g * G + r % G;
   }
 
+  // Per-row max M and weighted sum L over the splits (one wave per row); each m_s
+  // in w_s is replaced by its weight 2^(m_s - M) (0 for an empty split).
+  __device__ static void row_stats(int R, int ns, int ns_max, float* w_s, const float* l_s, float* M_r, float* L_r) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    for (int r = w; r < R; r += NT / kWave) {
+      float M = neg_inf();
+      for (int s = lane; s < ns; s += kWave) M = fmaxf(M, w_s[r * ns_max + s]);
+      M = wave_max(M);
+      float L = 0.f;
+      for (int s = lane; s < ns; s += kWave) {
+        const float m = w_s[r * ns_max + s];
+        const float wt = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
+        w_s[r * ns_max + s] = wt;
+        L = fmaf(wt, l_s[r * ns_max + s], L);
+      }
+      L = wave_sum(L);
+      if (lane == 0) {
+        M_r[r] = M;
+        L_r[r] = L;
+      }
+    }
+  }
+
+  // Sums the P lane partials of one float4 output group by a fixed xor tree (P is
+  // uniform over the wave, whose lanes must all be active) and writes the group's
+  // outputs, and the row's lse, from lane p = 0.
+  __device__ static void fold_store(const AttnArgs& a, int q_row0, int g, int G, int r, int e4, int P, int p,
+                                    float4 acc, const float* M_r, const float* L_r) {
+    auto fold = [&](auto off_tag) {
+      constexpr int OFF = decltype(off_tag)::value;
+      if (OFF < P) {
+        acc.x += lane_xor<OFF>(acc.x);
+        acc.y += lane_xor<OFF>(acc.y);
+        acc.z += lane_xor<OFF>(acc.z);
+        acc.w += lane_xor<OFF>(acc.w);
+      }
+    };
+    fold(std::integral_constant<int, 1>{});
+    fold(std::integral_constant<int, 2>{});
+    fold(std::integral_constant<int, 4>{});
+    fold(std::integral_constant<int, 8>{});
+    fold(std::integral_constant<int, 16>{});
+    fold(std::integral_constant<int, 32>{});
+    if (p == 0) {
+      const int64_t orow = row(a, q_row0, g, G, r);
+      const float ls = L_r[r];
+      *reinterpret_cast<float4*>(a.out + orow * D + e4 * 4) =
+          ls > 0.f ? make_float4(acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e4 == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M_r[r] + log2f(ls)) * kLn2 : neg_inf();
+    }
+  }
+
   // Called by every work-group of the unit after it has stored its partials.
   // The last one to arrive merges the n_split partials of each row (M = max m_s;
   // out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s; lse = (M + log2 of that sum) *
@@ -82,28 +134,40 @@ struct SplitTail {
   // does not depend on which work-group merges.  tail: LDS of bytes(R, ns_max).
   __device__ static void run(const AttnArgs& a, int b, int g, int q_row0, int G, int R, int ns_max, int* flag,
                              float* tail) {
-    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    constexpr int WAVES = NT / kWave;
-    constexpr int D4 = D / 4;
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
       const int ticket = __hip_atomic_fetch_add(&a.counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
       *flag = (ticket == a.n_split - 1) ? 1 : 0;
     }
     __syncthreads();
     if (*flag == 0) return;
+    merge(a, g, q_row0, G, R, ns_max, tail);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // The merge itself: every thread of the work-group takes part (it has barriers).
+  // Also run by a later launch on the partials an earlier one left (the Selector
+  // launch that finishes a slow step), where the device-coherent loads cost nothing
+  // extra.
+  __device__ static void merge(const AttnArgs& a, int g, int q_row0, int G, int R, int ns_max, float* tail) {
+    const int tid = threadIdx.x;
+    constexpr int D4 = D / 4;
     const int ns = a.n_split;
     float* w_s = tail;                // [R][ns_max]: m, then the weight 2^(m - M)
     float* l_s = tail + R * ns_max;   // [R][ns_max]
     float* M_r = tail + 2 * R * ns_max;
     float* L_r = M_r + R;
 
-    // Lanes per float4 group: a power of two, at most a wave, filling the work-group.
+    // Lanes per float4 group: a power of two, at most a wave, filling 256 threads.  P
+    // fixes the summation order, so it does not depend on the work-group's width: a
+    // wider work-group (the Selector launch) leaves its extra threads idle and adds in
+    // exactly the order of the slow step's own merge.
     const int n_grp = R * D4;
     int P = 1;
-    while (P < kWave && 2 * P * n_grp <= NT) P *= 2;
+    while (P < kWave && 2 * P * n_grp <= 256) P *= 2;
     const int grp0 = tid / P, p = tid % P;
     // The unit's partial rows as one buffer resource (its base is uniform over the
     // work-group); loads outside it return zero.
@@ -132,23 +196,7 @@ struct SplitTail {
       l_s[r * ns_max + s] = ml.y;
     }
     __syncthreads();
-    for (int r = w; r < R; r += WAVES) {
-      float M = neg_inf();
-      for (int s = lane; s < ns; s += kWave) M = fmaxf(M, w_s[r * ns_max + s]);
-      M = wave_max(M);
-      float L = 0.f;
-      for (int s = lane; s < ns; s += kWave) {
-        const float m = w_s[r * ns_max + s];
-        const float wt = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
-        w_s[r * ns_max + s] = wt;
-        L = fmaf(wt, l_s[r * ns_max + s], L);
-      }
-      L = wave_sum(L);
-      if (lane == 0) {
-        M_r[r] = M;
-        L_r[r] = L;
-      }
-    }
+    row_stats(R, ns, ns_max, w_s, l_s, M_r, L_r);
     __syncthreads();
     for (int grp = grp0; grp < n_grp; grp += NT / P) {
       const int r = grp / D4;
@@ -178,32 +226,8 @@ struct SplitTail {
         for (int j = 0; j < PRE; ++j)
           if (p + P * (j0 + j) < ns) add(wr[p + P * (j0 + j)], v[j]);
       }
-      // xor tree over the P lanes of the group (P is uniform over the work-group)
-      auto fold = [&](auto off_tag) {
-        constexpr int OFF = decltype(off_tag)::value;
-        if (OFF < P) {
-          acc.x += lane_xor<OFF>(acc.x);
-          acc.y += lane_xor<OFF>(acc.y);
-          acc.z += lane_xor<OFF>(acc.z);
-          acc.w += lane_xor<OFF>(acc.w);
-        }
-      };
-      fold(std::integral_constant<int, 1>{});
-      fold(std::integral_constant<int, 2>{});
-      fold(std::integral_constant<int, 4>{});
-      fold(std::integral_constant<int, 8>{});
-      fold(std::integral_constant<int, 16>{});
-      fold(std::integral_constant<int, 32>{});
-      if (p == 0) {
-        const int64_t orow = row(a, q_row0, g, G, r);
-        const int e4 = grp % D4;
-        const float ls = L_r[r];
-        *reinterpret_cast<float4*>(a.out + orow * D + e4 * 4) =
-            ls > 0.f ? make_float4(acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls) : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e4 == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M_r[r] + log2f(ls)) * kLn2 : neg_inf();
-      }
+      fold_store(a, q_row0, g, G, r, grp % D4, P, p, acc, M_r, L_r);
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 };
 

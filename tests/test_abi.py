@@ -255,3 +255,26 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         sfi.select_topk(torch.zeros((1, 1, 8)), torch.zeros(1, dtype=torch.int32), k=2, n_sink=0, n_recent=0)
+
+
+def test_deferred_slow_step_and_selector_merge_reject_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+
+    def dense(scores=FAKE, q=FAKE, ws_bytes=1 << 40):
+        return lib.sfi_dense_attn_with_stats_deferred(ctypes.byref(shape), ctypes.byref(kv), q, FAKE, 4, 64, FAKE,
+                                                      FAKE, scores, 16384, FAKE, ws_bytes, None)
+
+    assert dense(scores=0) == 1 and "scores is NULL" in lib.sfi_last_error().decode()
+    assert dense(q=MISALIGNED) == 1
+    assert dense(ws_bytes=10) == 3
+
+    def merge(shape_=shape, sel=FAKE, out=FAKE, cap=200, k=100, ws_bytes=1 << 40):
+        return lib.sfi_pack_compact_merge(ctypes.byref(shape_), ctypes.byref(kv), FAKE, 4, sel, k, FAKE, FAKE, cap,
+                                          FAKE, out, FAKE, FAKE, ws_bytes, None)
+
+    assert merge(sel=0) == 1
+    assert merge(out=0) == 1
+    assert merge(cap=50) == 1 and "cap" in lib.sfi_last_error().decode()
+    assert merge(k=0) == 1 and "k must be" in lib.sfi_last_error().decode()
+    assert merge(ws_bytes=10) == 3
+    assert merge(shape_=_shape(d=96)) == 2

@@ -1,0 +1,129 @@
+"""GPU parity of the slow step whose split-K combine runs in the pack launch.
+
+sfi_dense_attn_with_stats_deferred leaves the slow step's split partials in the
+workspace; after the Selector, sfi_pack_compact_merge packs and merges them into
+out and lse.  The three calls must give out, lse, scores, sel_idx and the compact
+buffer bit-identical to sfi_dense_attn_with_stats, sfi_select_topk and
+sfi_pack_compact (which the other parity files check against the oracle); the
+16K layer is also checked against the fp64 oracle directly.  Cases cover one and
+many splits, query groups of 1, 2, 4 and 8, fp32 and bf16, d 64 and 128, requests
+with fewer candidates than k, and long rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sfi_synth import make_case, qwen06b_decode_case, tiny_case
+from _gpu import DEV, LSE_TOL, OUT_TOL, DevCase, assert_close
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("out", "lse", "scores", "sel_idx", "compact_k", "compact_v", "n_compact")
+
+
+def _bits(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy()
+    a = t.numpy()
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _zero_compact(dc, cap):
+    """Compact buffers zeroed first: rows past n_compact are never written, so the two runs compare whole."""
+    B, Hkv, d = int(dc.bt.shape[0]), int(dc.k.shape[1]), int(dc.k.shape[3])
+    return (torch.zeros((B, Hkv, cap, d), dtype=dc.k.dtype, device=DEV),
+            torch.zeros((B, Hkv, cap, d), dtype=dc.k.dtype, device=DEV))
+
+
+def _pair(sfi, dc, n_sink, n_recent, k, workspace=None):
+    out, lse, sc, ws = sfi.dense_attn_with_stats_deferred(dc.q, dc.k, dc.v, dc.bt, dc.lens,
+                                                          max_seq_len=dc.max_seq_len, n_sink=n_sink,
+                                                          n_recent=n_recent, workspace=workspace)
+    sel = sfi.select_topk(sc, dc.lens, k=k, n_sink=n_sink, n_recent=n_recent)
+    ck, cv = _zero_compact(dc, n_sink + k)
+    ck, cv, nc = sfi.pack_compact_merge(dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=n_sink, cap=n_sink + k,
+                                        max_seq_len=dc.max_seq_len, out=out, lse=lse, workspace=ws,
+                                        compact_k=ck, compact_v=cv)
+    return out, lse, sc, sel, ck, cv, nc
+
+
+def _separate(sfi, dc, n_sink, n_recent, k):
+    out, lse, sc = sfi.dense_attn_with_stats(dc.q, dc.k, dc.v, dc.bt, dc.lens, max_seq_len=dc.max_seq_len,
+                                             n_sink=n_sink, n_recent=n_recent)
+    sel = sfi.select_topk(sc, dc.lens, k=k, n_sink=n_sink, n_recent=n_recent)
+    ck, cv = _zero_compact(dc, n_sink + k)
+    ck, cv, nc = sfi.pack_compact(dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=n_sink, cap=n_sink + k,
+                                  max_seq_len=dc.max_seq_len, compact_k=ck, compact_v=cv)
+    return out, lse, sc, sel, ck, cv, nc
+
+
+def _check_identical(sfi, c, k, n_splits_min=1):
+    dc = DevCase(c)
+    d = c.q.shape[-1]
+    _, ns = sfi.plan_splits(0, B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=d, bf16=(c.dtype == "bf16"),
+                            max_pages=int(dc.bt.shape[1]), num_pages=int(dc.k.shape[0]), max_seq_len=dc.max_seq_len)
+    assert ns >= n_splits_min, ns
+    ref = _separate(sfi, dc, c.n_sink, c.n_recent, k)
+    got = _pair(sfi, dc, c.n_sink, c.n_recent, k)
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, got, ref):
+        assert np.array_equal(_bits(x), _bits(y)), f"{c.name}: {name} differs from the separate calls (splits {ns})"
+    return dc, got
+
+
+@pytest.mark.parametrize("name,mk,k,min_splits", [
+    ("tiny_fp32_d64_g4", lambda: tiny_case(3), 64, 2),
+    ("ragged_bf16_g4", lambda: make_case(611, name="ragged", B=3, Hq=16, Hkv=4, d=128, dtype="bf16",
+                                         seq_lens=[5000, 333, 9000], n_sink=4, n_recent=64, k_sel=300,
+                                         hh_per_head=10), 300, 2),
+    ("g1_d64_bf16", lambda: make_case(612, name="g1", B=2, Hq=4, Hkv=4, d=64, dtype="bf16", seq_lens=[3000, 100],
+                                      n_sink=4, n_recent=64, k_sel=200), 200, 2),
+    ("g8_bf16", lambda: make_case(613, name="g8", B=2, Hq=64, Hkv=8, d=128, dtype="bf16", seq_lens=[6000, 2500],
+                                  n_sink=4, n_recent=64, k_sel=512, hh_per_head=20), 512, 2),
+    ("one_split_fp32", lambda: make_case(614, name="one_split", B=32, Hq=16, Hkv=8, d=64, dtype="f32",
+                                         seq_lens=[300 + 7 * i for i in range(32)], n_sink=4, n_recent=32,
+                                         k_sel=100), 100, 1),
+])
+def test_deferred_pair_equals_separate_calls(gpu_lib, name, mk, k, min_splits):
+    _check_identical(gpu_lib, mk(), k, min_splits)
+
+
+def test_deferred_pair_rows_beyond_the_register_selector(gpu_lib):
+    """Rows of more than 65536 candidates (the streaming Selector variant) with the merge."""
+    c = make_case(615, name="long", B=1, Hq=8, Hkv=2, d=128, dtype="bf16", seq_lens=[70000], n_sink=4,
+                  n_recent=64, k_sel=2048)
+    _check_identical(gpu_lib, c, 2048, 2)
+
+
+def test_deferred_pair_16k_layer_matches_oracle(gpu_lib):
+    c = qwen06b_decode_case(1000, L=16384, B=1, frac=(1, 8))
+    dc, (out, lse, sc, sel, _, _, _) = _check_identical(gpu_lib, c, c.k_sel, 2)
+    L = int(c.seq_lens[0])
+    ref_o, ref_l = O.dense_attention(c.q_values()[0], c.kv.k, c.kv.v, c.kv.block_table[0], L, c.scale, c.Hkv,
+                                     kv_dtype=c.dtype)
+    assert_close(out.cpu().numpy()[0], ref_o, OUT_TOL, "16K out")
+    assert_close(lse.cpu().numpy()[0], ref_l, LSE_TOL, "16K lse")
+    lo, hi = O.candidate_range(L, 1, c.n_sink, c.n_recent)
+    scn, seln = sc.cpu().numpy(), sel.cpu().numpy()
+    for g in (0, 5):
+        assert np.array_equal(seln[0, g], O.select_topk(scn[0, g], lo, hi, c.k_sel)), f"selection g={g}"
+
+
+def test_deferred_pair_after_other_calls_on_one_workspace(gpu_lib):
+    """A ticket-merged slow step on the same workspace before the deferred calls changes nothing."""
+    sfi = gpu_lib
+    c = make_case(616, name="shared", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[4096, 3001], n_sink=4,
+                  n_recent=64, k_sel=256)
+    dc = DevCase(c)
+    ref = _separate(sfi, dc, 4, 64, 256)
+    ws = torch.zeros(sfi.workspace_size("dense", k_pool=dc.k, block_table=dc.bt, Hq=16, dtype=torch.bfloat16,
+                                        max_seq_len=dc.max_seq_len), dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        sfi.dense_attn_with_stats(dc.q, dc.k, dc.v, dc.bt, dc.lens, max_seq_len=dc.max_seq_len, n_sink=4,
+                                  n_recent=64, workspace=ws)
+        got = _pair(sfi, dc, 4, 64, 256, workspace=ws)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, got, ref):
+            assert np.array_equal(_bits(x), _bits(y)), name
