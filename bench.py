@@ -44,7 +44,7 @@ METRIC = "sparse decode-attn effective KV GB/s (% HBM peak) + speedup vs dense a
 DECODE_SOURCES = ["sparse_kv_cache_sfi_amd/csrc/decode_unit.h", "sparse_kv_cache_sfi_amd/csrc/split_tail.h",
                   "sparse_kv_cache_sfi_amd/csrc/decode.hip", "sparse_kv_cache_sfi_amd/csrc/common.h"]
 TRAFFIC_PROFILE = "profiles/decode_layer_16k_b1_hbm_bytes.txt"
-DENSE_KERNEL = "decode_kernel<unsigned short, 128, 2, false, 1, false, false>"
+DENSE_KERNEL = "decode_kernel<unsigned short, 128, 2, false, 1, false, false, true>"
 
 
 def decode_source_hash():

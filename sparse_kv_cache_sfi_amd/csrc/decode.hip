@@ -4,11 +4,13 @@
 
 namespace sfi {
 
-template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false>
+template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false,
+          bool DEFER = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
   using S = DecodeShape<T, D, G>;
   __shared__ __attribute__((aligned(16))) char smem[INDEXED ? S::SMEM_IDX : S::SMEM];
-  decode_unit<T, D, G, SPARSE, SCORES, APPEND, INDEXED>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z, smem);
+  decode_unit<T, D, G, SPARSE, SCORES, APPEND, INDEXED, DEFER>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z,
+                                                               smem);
 }
 
 template <typename T, int D, int G>
@@ -24,6 +26,8 @@ static hipError_t launch_decode_t(const AttnArgs& a, bool sparse, int B, hipStre
     hipLaunchKernelGGL((decode_kernel<T, D, G, true, 0>), grid, block, 0, stream, a);
   else if (a.scores && a.head_scores)
     hipLaunchKernelGGL((decode_kernel<T, D, G, false, 2>), grid, block, 0, stream, a);
+  else if (a.scores && a.defer_merge)
+    hipLaunchKernelGGL((decode_kernel<T, D, G, false, 1, false, false, true>), grid, block, 0, stream, a);
   else if (a.scores)
     hipLaunchKernelGGL((decode_kernel<T, D, G, false, 1>), grid, block, 0, stream, a);
   else

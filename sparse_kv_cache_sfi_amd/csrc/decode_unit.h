@@ -82,8 +82,10 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& q, const u32x4& k
 }
 
 // SCORES: 0 no logits, 1 the group-summed logits [B, Hkv, stride], 2 one logit row per
-// query head [B, Hq, stride].
-template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false>
+// query head [B, Hq, stride].  DEFER: leave the split partials for a later launch to
+// merge (the slow step whose combine runs in the pack launch).
+template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false, bool INDEXED = false,
+          bool DEFER = false>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, const int g, const int split,
                                             const int q_row0, char* smem) {
   using S = DecodeShape<T, D, G>;
@@ -493,7 +495,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       }
     }
   }
-  if (a.n_split > 1 && !a.defer_merge)
+  if (a.n_split > 1 && !DEFER)
     SplitTail<D>::run(a, b, g, q_row0, G, G, kMaxSplits, reinterpret_cast<int*>(wml + WAVES * G * 2),
                       wml + WAVES * G * 2 + 4);
 }

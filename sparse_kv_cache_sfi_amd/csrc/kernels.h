@@ -82,7 +82,7 @@ struct AttnArgs {
   int32_t* pack_n;
   int32_t pack_cap;
   // Leave the split partials for a later launch to merge (no arrival ticket, out and
-  // lse are not written when there is more than one split).
+  // lse are not written when there is more than one split); selects the kernel variant.
   int32_t defer_merge;
 };
 
