@@ -209,6 +209,13 @@ def main():
                                 n_sink=n_sink, cap=cap, max_seq_len=max_len, out=ly["out"], lse=ly["lse"],
                                 workspace=ws_dense, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
                                 stream=main_s)
+        # The rest of the step in one launch: the fast step over the selection read in place, with the
+        # pack and the slow step's combine as work-groups of their own.
+        ly["finish"] = sfi.bind(sfi.sparse_decode_indexed_attn_merge, ly["q1"], ly["k"], ly["v"], ly["bt"],
+                                ly["lens"], ly["sel"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
+                                slow_out=ly["out"], slow_lse=ly["lse"], slow_workspace=ws_dense,
+                                compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"], out=ly["fout"],
+                                lse=ly["flse"], workspace=ws_sparse, stream=main_s)
         ly["fast"] = sfi.bind(sfi.sparse_decode_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"],
                               ly["cv"], ly["nc"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
                               out=ly["fout"], lse=ly["flse"], workspace=ws_sparse, stream=main_s)
@@ -221,8 +228,8 @@ def main():
         aux = aux_s is not main_s
         if record is not None:
             dense_ev[record][0].record(main_s)
-        # On one stream the pack launch finishes the slow step; with the maintenance on a second
-        # stream the slow step merges its own splits.
+        # On one stream the last launch (fast step + pack) finishes the slow step; with the maintenance
+        # on a second stream the slow step merges its own splits.
         (ly["dense"] if aux else ly["dense_d"])()
         if record is not None:
             dense_ev[record][1].record(main_s)
@@ -234,10 +241,10 @@ def main():
             ly["pack"]()
             packed.record(aux_s)
             main_s.wait_event(packed)
+            ly["fast"]()
         else:
             ly["select"]()
-            ly["pack_m"]()
-        ly["fast"]()
+            ly["finish"]()
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -285,7 +292,7 @@ def main():
     dense_alg = dense_kv + B * Hkv * L * 4            # K/V read + scores written
     traffic, traffic_src = profiled_traffic()
     roof = {"kernel": "decode_kernel<bf16, d128, G2, dense + group logits> (slow step; its split-K combine "
-                      "runs in the pack launch)", "bound": "hbm",
+                      "runs in the step's last launch)", "bound": "hbm",
             "achieved": dense_alg / dense_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
             "traffic_source": traffic_src, "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6,
@@ -300,8 +307,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: B=1, Hq=16, Hkv=8, d=128, page 16, "
                                "sink 4, recent 64, selected 1980 (12.5% retention); step = slow step "
-                               "(dense + logits) + Selector + pack (which also combines the slow step's splits) "
-                               "+ fast step"
+                               "(dense + logits) + Selector + one launch of fast step over the selection read in "
+                               "place, pack, and the slow step's split combine"
                                + (" (Selector and pack on a second stream)" if args.aux_stream else ""),
                    "global_batch": B, "seq_len": L, "replicas": R, "step_kv_bytes": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -312,7 +319,7 @@ def main():
     result["riders_16k"] = riders_16k(sfi, layers, main_s, k_sel, cap, n_sink, n_recent, max_len, ws_dense)
     # every kernel of the step back to back over the replicas (HIP events on its stream)
     kern = {}
-    for name in ("select", "pack_m", "fast"):
+    for name in ("select", "finish", "pack", "fast"):
         for i in range(R):
             layers[i][name]()
         k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -323,7 +330,7 @@ def main():
         torch.cuda.synchronize()
         kern[name + "_us"] = round(k0.elapsed_time(k1) * 1e3 / n_b2b, 2)
     kern["dense_us"] = round(dense_s * 1e6, 2)
-    kern["pack_us"] = kern.pop("pack_m_us")
+    kern["finish_GBps"] = round((pack_bytes + fast_kv) / kern["finish_us"] / 1e3, 1)
     kern["select_GBps"] = round(B * Hkv * (L - n_sink - n_recent) * 4 / kern["select_us"] / 1e3, 1)
     kern["pack_GBps"] = round(pack_bytes / kern["pack_us"] / 1e3, 1)
     kern["fast_GBps"] = round(fast_kv / kern["fast_us"] / 1e3, 1)
@@ -983,41 +990,47 @@ def riders_16k(sfi, layers, stream, k_sel, cap, n_sink, n_recent, max_len, ws_de
 
 
 def separate_combine_step(layers, stream, steps, step_bytes, b2b):
-    """The step with the slow step's own split-K combine (sfi_dense_attn_with_stats, sfi_select_topk,
-    sfi_pack_compact, fast step): its time, its slow-step and pack kernels back to back, and whether the
-    step's outputs (slow-step output and lse, logits, selection, compact buffer, fast-step output) equal
-    those of the step whose pack launch finishes the slow step, bit for bit."""
+    """The step as four launches: with the slow step's own split-K combine (sfi_dense_attn_with_stats,
+    sfi_select_topk, sfi_pack_compact, fast step over the compact buffer), and with the combine in the pack
+    launch (sfi_pack_compact_merge).  Their times, the slow-step and pack kernels back to back, and whether
+    every output of the step (slow-step output and lse, logits, selection, compact buffer, fast-step output
+    and lse) equals that of the three-launch step, bit for bit."""
     import torch
     R = len(layers)
     names = ("out", "lse", "scores", "sel", "ck", "cv", "nc", "fout", "flse")
-    deferred, plain = ("dense_d", "select", "pack_m", "fast"), ("dense", "select", "pack", "fast")
+    main = ("dense_d", "select", "finish")
+    plain = ("dense", "select", "pack", "fast")
+    pack_combine = ("dense_d", "select", "pack_m", "fast")
 
     def run(ly, calls):
         for c in calls:
             ly[c]()
-    same = True
+    same = {"plain": True, "pack_combine": True}
     for ly in layers:
-        run(ly, deferred)
+        run(ly, main)
         torch.cuda.synchronize()
         ref = {n: ly[n].clone() for n in names}
-        for n in names:
-            ly[n].zero_()
-        run(ly, plain)
-        torch.cuda.synchronize()
-        same &= all(torch.equal(ref[n].view(torch.uint8), ly[n].view(torch.uint8)) for n in names)
-    t = time_loop(lambda i: run(layers[i % R], plain), steps, stream)
-    res = {"ms_per_step": round(t * 1e3, 5), "value": round(step_bytes / t / 1e9, 2),
-           "dense_us": round(b2b("dense") * 1e6, 2), "pack_us": round(b2b("pack") * 1e6, 2),
-           "outputs_match_combine_in_pack": bool(same)}
-    log(f"separate-combine step {res}")
+        for key, calls in (("plain", plain), ("pack_combine", pack_combine)):
+            for n in names:
+                ly[n].zero_()
+            run(ly, calls)
+            torch.cuda.synchronize()
+            same[key] &= all(torch.equal(ref[n].view(torch.uint8), ly[n].view(torch.uint8)) for n in names)
+    t_plain = time_loop(lambda i: run(layers[i % R], plain), steps, stream)
+    t_pc = time_loop(lambda i: run(layers[i % R], pack_combine), steps, stream)
+    res = {"plain_ms_per_step": round(t_plain * 1e3, 5), "plain_value": round(step_bytes / t_plain / 1e9, 2),
+           "pack_combine_ms_per_step": round(t_pc * 1e3, 5),
+           "dense_us": round(b2b("dense") * 1e6, 2), "pack_combine_us": round(b2b("pack_m") * 1e6, 2),
+           "outputs_match_three_launch_step": same}
+    log(f"four-launch steps {res}")
     return res
 
 
 def fused_pack_steps(sfi, layers, dev, steps, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
-    """The same step with the pack fused into the fast step: slow step -> Selector -> one launch that
-    attends over sink + selected + recent read in place and writes the compact buffer as it goes
+    """The three-launch step with the slow step's own combine: slow step -> Selector -> one launch of the
+    fast step over sink + selected + recent read in place, whose pack work-groups write the compact buffer
     (sfi_sparse_decode_indexed_attn with a compact buffer).  Outputs, selection and compact buffer must
-    equal the four-launch step's bit for bit."""
+    equal the headline step's bit for bit."""
     import torch
     stream = torch.cuda.current_stream(dev)
     R = len(layers)
@@ -1054,7 +1067,7 @@ def fused_pack_steps(sfi, layers, dev, steps, k_sel, cap, n_sink, n_recent, max_
 
 def graph_steps(sfi, layers, dev, steps, step_bytes, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
     """The same step captured once per replica in a HIP graph and replayed: the GPU time of the
-    step without host launch cost or launch gaps between its four kernels.  The first replay's
+    step without host launch cost or launch gaps between its kernels.  The first replay's
     fast-step output is checked against the eager step's."""
     import torch
     R = len(layers)
@@ -1065,12 +1078,11 @@ def graph_steps(sfi, layers, dev, steps, step_bytes, k_sel, cap, n_sink, n_recen
                                            n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
                                            scores=ly["scores"], workspace=ws_dense)
         sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"])
-        sfi.pack_compact_merge(ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink, cap=cap,
-                               max_seq_len=max_len, out=ly["out"], lse=ly["lse"], workspace=ws_dense,
-                               compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"])
-        sfi.sparse_decode_attn(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"], ly["cv"], ly["nc"],
-                               n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=ly["fout"],
-                               lse=ly["flse"], workspace=ws_sparse)
+        sfi.sparse_decode_indexed_attn_merge(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"],
+                                             n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
+                                             slow_out=ly["out"], slow_lse=ly["lse"], slow_workspace=ws_dense,
+                                             compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
+                                             out=ly["fout"], lse=ly["flse"], workspace=ws_sparse)
 
     torch.cuda.synchronize()
     eager = layers[0]["fout"].clone()

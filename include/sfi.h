@@ -350,6 +350,31 @@ SFI_API sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const 
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * The rest of a slow step in one launch: the index-set fast step (as
+ * sfi_sparse_decode_indexed_attn with no appended token and one selection per
+ * KV head) that also packs compact_k / compact_v / n_compact (as
+ * sfi_pack_compact) and merges the split partials that
+ * sfi_dense_attn_with_stats_deferred left in slow_workspace into slow_out and
+ * slow_lse (SFI page, Fig. 2 and Fig. 3B: the slow step's selection is packed
+ * while the next attention runs; here all three run as work-groups of one
+ * launch, the attention reading the selected rows in place).  Every output is
+ * bit-identical to the plain calls.  The shape, kv and seq_lens are the slow
+ * step's; workspace (for this call's own split partials, of
+ * sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent) bytes) and
+ * slow_workspace must not overlap.  Errors as the calls it replaces; nothing is
+ * launched on any error.
+ */
+SFI_API sfi_status sfi_sparse_decode_indexed_attn_merge(const sfi_shape* shape, const sfi_paged_kv* kv,
+                                                const void* q, const int32_t* seq_lens,
+                                                int32_t n_sink, int32_t n_recent,
+                                                const int32_t* sel_idx, int32_t k, void* compact_k,
+                                                void* compact_v, int32_t cap, int32_t* n_compact,
+                                                float* out, float* lse, void* workspace,
+                                                size_t workspace_bytes, float* slow_out,
+                                                float* slow_lse, void* slow_workspace,
+                                                size_t slow_workspace_bytes, void* stream);
+
+/*
  * Drafting and verifying requests in one launch (ASPIRE abstract: a unified
  * mixed forward lets drafting and verifying requests share one batched
  * pass; SparseSpec-L abstract: drafts attend over a sparse, recallable KV

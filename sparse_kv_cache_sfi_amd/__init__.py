@@ -25,6 +25,7 @@ import torch
 __all__ = [
     "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats", "dense_attn_with_refresh",
     "select_topk", "pack_compact", "dense_attn_with_stats_deferred", "pack_compact_merge",
+    "sparse_decode_indexed_attn_merge",
     "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
 ]
@@ -70,6 +71,9 @@ _SIGS = {
     "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, POINTER(c_size_t)],
     "sfi_dense_attn_with_stats_deferred": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                            c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
+    "sfi_sparse_decode_indexed_attn_merge": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                             c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_pack_compact_merge": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_pack_compact": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
@@ -650,6 +654,64 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
           _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, int(per_head),
           _ptr(compact_k), _ptr(compact_v), cap, _ptr(n_compact), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
           _stream(stream, dev))
+    return out, lse
+
+
+def sparse_decode_indexed_attn_merge(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                     block_table: torch.Tensor, seq_lens: torch.Tensor, sel_idx: torch.Tensor, *,
+                                     n_sink: int, n_recent: int, max_seq_len: int, slow_out: torch.Tensor,
+                                     slow_lse: Optional[torch.Tensor], slow_workspace: Optional[torch.Tensor],
+                                     compact_k: torch.Tensor, compact_v: torch.Tensor, n_compact: torch.Tensor,
+                                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                     stream=None):
+    """The rest of a slow step in one launch (sfi_sparse_decode_indexed_attn_merge): the fast step over
+    sel_idx [B, Hkv, k] read in place, q [B, Hq, d] -> (out [B, Hq, d], lse [B, Hq]), which also packs
+    compact_k / compact_v [B, Hkv, cap, d] and n_compact [B], and merges the split partials that
+    dense_attn_with_stats_deferred left in slow_workspace into slow_out [B, 1, Hq, d] and slow_lse."""
+    _dev(q, "q")
+    _i32(seq_lens, "seq_lens")
+    _i32(sel_idx, "sel_idx")
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
+    if q.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("q must share the pool dtype; seq_lens must be [B]")
+    if sel_idx.dim() != 3 or tuple(sel_idx.shape[:2]) != (B, Hkv):
+        raise ValueError("sel_idx must be [B, Hkv, k]")
+    k = sel_idx.shape[2]
+    for t, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
+        _dev(t, n)
+        if t.dtype != k_pool.dtype or t.dim() != 4 or tuple(t.shape[:2]) != (B, Hkv) or t.shape[3] != d:
+            raise ValueError(f"{n} must be [B, Hkv, cap, d] in the pool dtype")
+    if compact_v.shape != compact_k.shape:
+        raise ValueError("compact_v must match compact_k")
+    _i32(n_compact, "n_compact")
+    if tuple(n_compact.shape) != (B,):
+        raise ValueError("n_compact must be [B]")
+    cap = compact_k.shape[2]
+    _f32_out(slow_out, (B, 1, Hq, d), "slow_out")
+    _f32_out(slow_lse, (B, 1, Hq), "slow_lse")
+    if slow_workspace is not None:
+        _dev(slow_workspace, "slow_workspace")
+    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
+    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
+    dev = q.device
+    _f32_out(out, (B, Hq, d), "out")
+    _f32_out(lse, (B, Hq), "lse")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = c_size_t(0)
+    _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), n_sink + k, n_recent,
+          ctypes.byref(need))
+    ws = _workspace(need.value, workspace, dev)
+    _call("sfi_sparse_decode_indexed_attn_merge", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
+          seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(),
+          cap, n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws), slow_out.data_ptr(),
+          _ptr(slow_lse), _ptr(slow_workspace), _nbytes(slow_workspace), _stream(stream, dev))
     return out, lse
 
 

@@ -17,36 +17,16 @@
 // own merge code, while the other work-groups copy rows.
 #include "common.h"
 #include "kernels.h"
+#include "pack_unit.h"
 #include "split_tail.h"
 
 namespace sfi {
-
-// Rows per work-group: 16 while that keeps the grid within kPackSmallGrid work-groups
-// (small batches: more, shorter work-groups cut the launch's latency), else 32.
-constexpr int kPackSmallGrid = 4096;
-
-struct PackArgs {
-  const void* k_pool;
-  const void* v_pool;
-  const int32_t* block_table;
-  int32_t max_pages, num_pages, max_seq_len, Hkv;
-  const int32_t* seq_lens;
-  int32_t n_sink;
-  const int32_t* sel;
-  int32_t k;
-  void* ck;
-  void* cv;
-  int32_t cap;
-  int32_t* n_compact;
-};
 
 // Query heads per KV head, at most (the merge's LDS is sized for it).
 constexpr int kPackMergeRows = 8;
 
 template <int ROW_BYTES, int RPB, int MD>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs p, AttnArgs m) {
-  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;       // rows per pass of the work-group
   const int b = blockIdx.z, g = blockIdx.y;
   if constexpr (MD > 0) {
     if (blockIdx.x == 0) {
@@ -56,49 +36,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p, AttnArgs m) {
       return;
     }
   }
-  const int bx = blockIdx.x - (MD > 0 ? 1 : 0);   // this work-group's block of rows
-  const int L = clamp_len(p.seq_lens[b], p.max_seq_len, p.max_pages);
-  const int ns = min(p.n_sink, L);
-  const int32_t* srow = p.sel + ((int64_t)b * p.Hkv + g) * p.k;
-  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-  const int chunk = threadIdx.x % CPR;
-  const int64_t dst_head = ((int64_t)b * p.Hkv + g) * p.cap;
-  const int64_t page_bytes = (int64_t)p.Hkv * kPage * ROW_BYTES;
-  const char* kp = reinterpret_cast<const char*>(p.k_pool);
-  const char* vp = reinterpret_cast<const char*>(p.v_pool);
-  char* ckp = reinterpret_cast<char*>(p.ck);
-  char* cvp = reinterpret_cast<char*>(p.cv);
-
-  for (int rr = threadIdx.x / CPR; rr < RPB; rr += RPP) {
-    const int i = bx * RPB + rr;
-    if (i >= ns + p.k || i >= p.cap) continue;
-    const int pos = i < ns ? i : srow[i - ns];
-    if (pos < 0) continue;
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (pos < L) {
-      const int pg = bt[pos >> 4];
-      if (pg >= 0 && pg < p.num_pages) {
-        const int64_t off = (int64_t)pg * page_bytes + ((int64_t)g * kPage + (pos & 15)) * ROW_BYTES + chunk * 16;
-        kx = *reinterpret_cast<const u32x4*>(kp + off);
-        vx = *reinterpret_cast<const u32x4*>(vp + off);
-      }
-    }
-    const int64_t dst = (dst_head + i) * ROW_BYTES + chunk * 16;
-    *reinterpret_cast<u32x4*>(ckp + dst) = kx;
-    *reinterpret_cast<u32x4*>(cvp + dst) = vx;
-  }
-
-  if (bx == 0 && g == 0) {
-    // n_compact[b] = ns + (entries of head 0's selection before its first negative one).
-    __shared__ int first_neg;
-    if (threadIdx.x == 0) first_neg = p.k;
-    __syncthreads();
-    const int32_t* s0 = p.sel + (int64_t)b * p.Hkv * p.k;
-    for (int i = threadIdx.x; i < p.k; i += 256)
-      if (s0[i] < 0) atomicMin(&first_neg, i);
-    __syncthreads();
-    if (threadIdx.x == 0) p.n_compact[b] = ns + first_neg;
-  }
+  pack_block<ROW_BYTES, RPB>(p, blockIdx.x - (MD > 0 ? 1 : 0), g, b);
 }
 
 hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,

@@ -12,6 +12,7 @@
 #include "sfi.h"
 #include "common.h"
 #include "kernels.h"
+#include "pack_unit.h"
 
 namespace {
 
@@ -540,7 +541,7 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
                        const void* compact_k, const void* compact_v, int32_t cap, const int32_t* n_compact,
                        const int32_t* sel, int32_t sel_k, bool per_head, float* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream, void* pack_k = nullptr, void* pack_v = nullptr,
-                       int32_t pack_cap = 0, int32_t* pack_n = nullptr) {
+                       int32_t pack_cap = 0, int32_t* pack_n = nullptr, const sfi::AttnArgs* merge = nullptr) {
   SFI_TRY(check_shape(shape_in));
   // One unit per query head when each query head has its own selection: the units see
   // a shape with as many KV heads as query heads, head_div of them per pool head.
@@ -597,6 +598,17 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (pack_k && head_div == 1 && !k_new) {
+    // The pack (and a deferred slow step's merge) as work-groups of their own in the
+    // attention's launch; the attention reads the selected rows in place.
+    a.pack_k = a.pack_v = nullptr;
+    a.pack_n = nullptr;
+    const sfi::PackArgs p{kv->k, kv->v, kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len,
+                          shape->num_kv_heads, seq_lens, n_sink, sel, sel_k, pack_k, pack_v, pack_cap, pack_n};
+    const hipError_t e = sfi::launch_fast_pack(a, p, merge, shape->dtype, shape->head_dim, G, shape->batch, st);
+    return hip_status(e, "sparse decode + pack launch");
+  }
+  if (merge) return fail(SFI_ERR_INVALID_ARG, "a deferred combine rides only with packing and no appended token");
   hipError_t e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, true, shape->batch, st);
   return hip_status(e, "sparse decode launch");
 }
@@ -648,6 +660,46 @@ sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const sfi_page
   return sparse_call(shape, kv, q, k_new, v_new, seq_lens, n_sink, n_recent, nullptr, nullptr, 0, nullptr, sel_idx,
                      k, per_head == 1, out, lse, workspace, workspace_bytes, stream, compact_k, compact_v, cap,
                      n_compact);
+}
+
+sfi_status sfi_sparse_decode_indexed_attn_merge(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                                const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                                const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v,
+                                                int32_t cap, int32_t* n_compact, float* out, float* lse,
+                                                void* workspace, size_t workspace_bytes, float* slow_out,
+                                                float* slow_lse, void* slow_workspace, size_t slow_workspace_bytes,
+                                                void* stream) {
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  SFI_TRY(check_ptr16(compact_k, "compact_k"));
+  SFI_TRY(check_ptr16(compact_v, "compact_v"));
+  SFI_TRY(check_ptr16(slow_out, "slow_out"));
+  if (!n_compact) return fail(SFI_ERR_INVALID_ARG, "n_compact is NULL");
+  if (k < 0) return fail(SFI_ERR_INVALID_ARG, "k must be >= 0");
+  if (!sel_idx && k > 0) return fail(SFI_ERR_INVALID_ARG, "sel_idx is NULL");
+  if ((int64_t)cap < (int64_t)n_sink + k)
+    return fail(SFI_ERR_INVALID_ARG, "cap (%d) must be >= n_sink + k (%lld)", cap, (long long)n_sink + k);
+  // The deferred slow step's partials, laid out as sfi_dense_attn_with_stats_deferred left them.
+  const Split sp = plan_dense(shape, kv, 1);
+  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
+  SFI_TRY(check_unit_span(shape, 1, sp.n));
+  SFI_TRY(check_workspace(slow_workspace, slow_workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
+  if (sp.n > 1 && workspace && workspace_bytes > 0) {
+    const char* a0 = static_cast<const char*>(workspace);
+    const char* b0 = static_cast<const char*>(slow_workspace);
+    if (a0 < b0 + slow_workspace_bytes && b0 < a0 + workspace_bytes)
+      return fail(SFI_ERR_INVALID_ARG, "workspace and slow_workspace must not overlap (both are in use in one launch)");
+  }
+  sfi::AttnArgs m = base_args(shape, kv, seq_lens);
+  m.n_split = sp.n;
+  m.split_tokens = sp.tokens;
+  m.t_q = 1;
+  m.out = slow_out;
+  m.lse = slow_lse;
+  set_partials(m, slow_workspace, rows, shape->head_dim);
+  return sparse_call(shape, kv, q, nullptr, nullptr, seq_lens, n_sink, n_recent, nullptr, nullptr, 0, nullptr, sel_idx,
+                     k, false, out, lse, workspace, workspace_bytes, stream, compact_k, compact_v, cap, n_compact,
+                     sp.n > 1 ? &m : nullptr);
 }
 
 sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* modes,

@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 from sfi_synth import make_case, qwen06b_decode_case, tiny_case
-from _gpu import DEV, LSE_TOL, OUT_TOL, DevCase, assert_close
+from _gpu import DEV, LSE_TOL, OUT_TOL, DevCase, assert_close, dev_array
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,76 @@ def test_deferred_pair_after_other_calls_on_one_workspace(gpu_lib):
         torch.cuda.synchronize()
         for name, x, y in zip(NAMES, got, ref):
             assert np.array_equal(_bits(x), _bits(y)), name
+
+
+def _three_launch(sfi, dc, q1, n_sink, n_recent, k):
+    """Deferred slow step, Selector, then one launch with the fast step over the index set, the pack and
+    the slow step's combine."""
+    out, lse, sc, ws = sfi.dense_attn_with_stats_deferred(dc.q, dc.k, dc.v, dc.bt, dc.lens,
+                                                          max_seq_len=dc.max_seq_len, n_sink=n_sink,
+                                                          n_recent=n_recent)
+    sel = sfi.select_topk(sc, dc.lens, k=k, n_sink=n_sink, n_recent=n_recent)
+    ck, cv = _zero_compact(dc, n_sink + k)
+    nc = torch.empty((dc.q.shape[0],), dtype=torch.int32, device=DEV)
+    fo, fl = sfi.sparse_decode_indexed_attn_merge(q1, dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=n_sink,
+                                                  n_recent=n_recent, max_seq_len=dc.max_seq_len, slow_out=out,
+                                                  slow_lse=lse, slow_workspace=ws, compact_k=ck, compact_v=cv,
+                                                  n_compact=nc)
+    return out, lse, sc, sel, ck, cv, nc, fo, fl
+
+
+@pytest.mark.parametrize("name,mk,k", [
+    ("tiny_fp32_d64_g4", lambda: tiny_case(3), 64),
+    ("ragged_bf16_g4", lambda: make_case(621, name="ragged", B=3, Hq=16, Hkv=4, d=128, dtype="bf16",
+                                         seq_lens=[5000, 333, 9000], n_sink=4, n_recent=64, k_sel=300,
+                                         hh_per_head=10), 300),
+    ("g8_bf16", lambda: make_case(623, name="g8", B=2, Hq=64, Hkv=8, d=128, dtype="bf16", seq_lens=[6000, 2500],
+                                  n_sink=4, n_recent=64, k_sel=512, hh_per_head=20), 512),
+    ("one_split_fp32", lambda: make_case(624, name="one_split", B=32, Hq=16, Hkv=8, d=64, dtype="f32",
+                                         seq_lens=[300 + 7 * i for i in range(32)], n_sink=4, n_recent=32,
+                                         k_sel=100), 100),
+    ("no_sink_g1", lambda: make_case(625, name="no_sink", B=2, Hq=4, Hkv=4, d=64, dtype="bf16",
+                                     seq_lens=[3000, 90], n_sink=0, n_recent=64, k_sel=200), 200),
+    ("layer_16k", lambda: qwen06b_decode_case(1000, L=16384, B=1, frac=(1, 8)), None),
+])
+def test_three_launch_step_equals_separate_calls(gpu_lib, name, mk, k):
+    """Slow step + Selector + one launch (index-set fast step, pack, combine) against the plain slow step,
+    Selector, pack and fast step over the compact buffer: all nine outputs bit for bit."""
+    sfi = gpu_lib
+    c = mk()
+    k = c.k_sel if k is None else k
+    dc = DevCase(c)
+    q1 = dev_array(np.ascontiguousarray(c.q[:, -1]))
+    ref = list(_separate(sfi, dc, c.n_sink, c.n_recent, k))
+    ref += list(sfi.sparse_decode_attn(q1, dc.k, dc.v, dc.bt, dc.lens, ref[4], ref[5], ref[6], n_sink=c.n_sink,
+                                       n_recent=c.n_recent, max_seq_len=dc.max_seq_len))
+    got = _three_launch(sfi, dc, q1, c.n_sink, c.n_recent, k)
+    torch.cuda.synchronize()
+    for nm, x, y in zip(NAMES, got, ref):
+        assert np.array_equal(_bits(x), _bits(y)), f"{name}: {nm} differs from the separate calls"
+    # The fast step over the index set walks all k entries of a selection row (padding as masked rows),
+    # the one over the compact buffer only the filled ones: with padding their split boundaries fall on
+    # other tokens, so the sums round in another order.  Bit for bit when every row is full.
+    full = bool((ref[3].cpu().numpy() >= 0).all())
+    for nm, x, y in zip(("fast_out", "fast_lse"), got[7:], ref[7:]):
+        if full:
+            assert np.array_equal(_bits(x), _bits(y)), f"{name}: {nm} differs from the separate calls"
+        else:
+            assert_close(x.cpu().numpy(), y.cpu().numpy(), 1e-5, f"{name}: {nm}")
+
+
+def test_three_launch_step_rejects_shared_workspaces(gpu_lib):
+    sfi = gpu_lib
+    c = make_case(626, name="ws", B=1, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[4096], n_sink=4, n_recent=64,
+                  k_sel=256)
+    dc = DevCase(c)
+    out, lse, sc, ws = sfi.dense_attn_with_stats_deferred(dc.q, dc.k, dc.v, dc.bt, dc.lens,
+                                                          max_seq_len=dc.max_seq_len, n_sink=4, n_recent=64)
+    sel = sfi.select_topk(sc, dc.lens, k=256, n_sink=4, n_recent=64)
+    ck, cv = _zero_compact(dc, 260)
+    nc = torch.empty((1,), dtype=torch.int32, device=DEV)
+    with pytest.raises(sfi.SfiError, match="overlap"):
+        sfi.sparse_decode_indexed_attn_merge(dev_array(np.ascontiguousarray(c.q[:, -1])), dc.k, dc.v, dc.bt, dc.lens,
+                                             sel, n_sink=4, n_recent=64, max_seq_len=dc.max_seq_len, slow_out=out,
+                                             slow_lse=lse, slow_workspace=ws, compact_k=ck, compact_v=cv,
+                                             n_compact=nc, workspace=ws)
