@@ -278,3 +278,25 @@ def test_deferred_slow_step_and_selector_merge_reject_bad_arguments(lib):
     assert merge(k=0) == 1 and "k must be" in lib.sfi_last_error().decode()
     assert merge(ws_bytes=10) == 3
     assert merge(shape_=_shape(d=96)) == 2
+
+
+def test_indexed_fast_step_with_pack_and_combine_rejects_bad_arguments(lib):
+    shape, kv = _shape(), _kv()
+    WS = 0x100000
+
+    def call(sel=FAKE, k=100, ck=FAKE, cap=200, nc=FAKE, slow_out=FAKE, ws=FAKE, ws_bytes=1 << 20, slow_ws=WS,
+             slow_bytes=1 << 40, shape_=shape):
+        return lib.sfi_sparse_decode_indexed_attn_merge(ctypes.byref(shape_), ctypes.byref(kv), FAKE, FAKE, 4, 64,
+                                                        sel, k, ck, FAKE, cap, nc, FAKE, FAKE, ws, ws_bytes, slow_out,
+                                                        FAKE, slow_ws, slow_bytes, None)
+
+    assert call(ck=0) == 1
+    assert call(ck=MISALIGNED) == 1
+    assert call(nc=0) == 1 and "n_compact" in lib.sfi_last_error().decode()
+    assert call(slow_out=0) == 1
+    assert call(sel=0) == 1 and "sel_idx" in lib.sfi_last_error().decode()
+    assert call(k=-1) == 1
+    assert call(cap=50) == 1 and "cap" in lib.sfi_last_error().decode()
+    assert call(slow_bytes=10) == 3
+    assert call(ws=WS + 64) == 1 and "overlap" in lib.sfi_last_error().decode()
+    assert call(shape_=_shape(d=96)) == 2
