@@ -39,13 +39,20 @@ struct VerifyShape {
   static constexpr int KS = D / 16;                         // QK^T k-steps of 16 dims
   static constexpr int DB = D / 32;                         // 32-dim blocks of O^T
   static constexpr int ROW_BYTES = D * 2;                   // bf16 row
-  static constexpr int LDS_ROW = ROW_BYTES + 16;            // padded LDS row stride
+  static constexpr int LDS_ROW = ROW_BYTES + 16;            // padded LDS row stride of the query rows
+  // K and V tile rows: at d 128 unpadded, their 16-byte chunks XOR-swizzled (tile_off);
+  // at d 64 padded like the query rows.
+  static constexpr bool SWZ = D == 128;
+  static constexpr int TILE_ROW = SWZ ? ROW_BYTES : LDS_ROW;
   static constexpr int TILE = kVerifyTile;                  // 32 tokens
   static constexpr int WAVES = 4;
   static constexpr int CPR = ROW_BYTES / 16;                // 16-byte chunks per row
   static constexpr int LOADS = TILE * CPR / kWave;          // loads per lane per tile per tensor
-  static constexpr int WAVE_LDS = 2 * TILE * LDS_ROW;       // K and V tiles of one wave
-  static constexpr int MERGE = WAVES * (32 * D + 64) * 4;   // per-wave O, m, l for the merge
+  static constexpr int WAVE_LDS = 2 * TILE * TILE_ROW;      // K and V tiles of one wave
+  // Per-wave O rows of the merge, one float longer than d: the 32 rows a write
+  // instruction touches then start on different banks.
+  static constexpr int MO_ROW = D + 1;
+  static constexpr int MERGE = WAVES * (32 * MO_ROW + 64) * 4;   // per-wave O, m, l for the merge
   static constexpr int TILES_LDS = WAVES * WAVE_LDS > MERGE ? WAVES * WAVE_LDS : MERGE;
   static constexpr int TAIL = SplitTail<D>::bytes(32, kMaxVerifySplits);
   static constexpr int BIG = TILES_LDS > TAIL ? TILES_LDS : TAIL;
@@ -63,6 +70,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// Byte offset of byte `byte` of tile row r.  Swizzled rows (d 128, 256 bytes) keep
+// logical 16-byte chunk c at chunk c ^ (4 (r mod 4) + (r / 4) mod 4): sixteen
+// consecutive rows read at one chunk (the K operand, 16 bytes per lane) and four
+// consecutive rows read over four consecutive chunks (a half-wave of transposed V
+// reads, 8 bytes per lane) each cover sixteen distinct chunks of a 256-byte span.
+template <bool SWZ>
+__device__ __forceinline__ int tile_off(int r, int byte, int row_bytes) {
+  if constexpr (SWZ) return r * row_bytes + (((byte >> 4) ^ (4 * (r & 3) + ((r >> 2) & 3))) << 4) + (byte & 15);
+  return r * row_bytes + byte;
+}
+
 template <int D, bool SCORES>
 __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, const int g, const int split,
                                             const int q_row0, const int G, char* smem) {
@@ -77,7 +95,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
   int* flag = bt_s + kBtSlots;
   char* big = smem + S::BIG_OFF;
   char* kt = big + w * S::WAVE_LDS;   // this wave's K tile, then its V tile
-  char* vt = kt + TILE * LDS_ROW;
+  char* vt = kt + TILE * S::TILE_ROW;
 
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
   const int t0 = split * a.split_tokens;
@@ -145,8 +163,8 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int rr = (i * kWave + lane) / CPR, ch = (i * kWave + lane) % CPR;
-      *reinterpret_cast<u32x4*>(kt + rr * LDS_ROW + ch * 16) = kr[i];
-      *reinterpret_cast<u32x4*>(vt + rr * LDS_ROW + ch * 16) = vr[i];
+      *reinterpret_cast<u32x4*>(kt + tile_off<S::SWZ>(rr, ch * 16, S::TILE_ROW)) = kr[i];
+      *reinterpret_cast<u32x4*>(vt + tile_off<S::SWZ>(rr, ch * 16, S::TILE_ROW)) = vr[i];
     }
   };
 
@@ -183,7 +201,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       // B operand: lane holds query row n, dims [16 s + 8 hb, +8).
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + n * LDS_ROW + (16 * s + 8 * hb) * 2);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + tile_off<S::SWZ>(n, (16 * s + 8 * hb) * 2, S::TILE_ROW));
       const u32x4 qb = *reinterpret_cast<const u32x4*>(q_s + n * LDS_ROW + (16 * s + 8 * hb) * 2);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qb),
                                                       sacc, 0, 0, 0);
@@ -264,14 +282,15 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
     // 4 j + i / 4 points at, for j = 0..3), so group lane s points at token
     // 16 s + 8 h + 4 hb + s / 4, dims 32 db + 16 (group & 1) + 4 (s % 4) + 0..3.
     const int tgrp = lane >> 4, tl = lane & 15;
-    const char* vbase = vt + (4 * hb + (tl >> 2)) * LDS_ROW + (16 * (tgrp & 1) + 4 * (tl & 3)) * 2;
+    const int vrow = 4 * hb + (tl >> 2), vbyte = (16 * (tgrp & 1) + 4 * (tl & 3)) * 2;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const char* p0 = vbase + 16 * s * LDS_ROW + 64 * db;
+        const char* p0 = vt + tile_off<S::SWZ>(vrow + 16 * s, vbyte + 64 * db, S::TILE_ROW);
+        const char* p1 = vt + tile_off<S::SWZ>(vrow + 16 * s + 8, vbyte + 64 * db, S::TILE_ROW);
         const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0));
-        const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 8 * LDS_ROW));
+        const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p1));
         const bf16x8 vA = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, phi[s]), oacc[db], 0, 0, 0);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vA, __builtin_bit_cast(bf16x8, plo[s]), oacc[db], 0, 0, 0);
@@ -284,15 +303,16 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
   __syncthreads();   // every wave is done with its tiles before the merge reuses the area
 
   // Merge the waves through LDS (the tile area is free now).
-  float* mo = reinterpret_cast<float*>(big);                // [WAVES][32][D]
-  float* mml = mo + WAVES * 32 * D;                         // [WAVES][32][2]
+  constexpr int MO_ROW = S::MO_ROW;
+  float* mo = reinterpret_cast<float*>(big);                // [WAVES][32][MO_ROW]
+  float* mml = mo + WAVES * 32 * MO_ROW;                    // [WAVES][32][2]
   l_run += __shfl_xor(l_run, 32);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int dim = 32 * db + 8 * (i / 4) + 4 * hb + (i % 4);
-      mo[(w * 32 + n) * D + dim] = oacc[db][i];
+      mo[(w * 32 + n) * MO_ROW + dim] = oacc[db][i];
     }
   if (hb == 0) {
     mml[(w * 32 + n) * 2] = m_run;
@@ -310,7 +330,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
       const float mw = mml[(x * 32 + r) * 2];
       const float al = (mw == neg_inf()) ? 0.f : exp2_fast(mw - M);
       ls = fmaf(al, mml[(x * 32 + r) * 2 + 1], ls);
-      os = fmaf(al, mo[(x * 32 + r) * D + e], os);
+      os = fmaf(al, mo[(x * 32 + r) * MO_ROW + e], os);
     }
     const int64_t orow = SplitTail<D>::row(a, q_row0, g, G, r);
     if (a.n_split == 1) {
