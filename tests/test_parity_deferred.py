@@ -158,6 +158,9 @@ def _three_launch(sfi, dc, q1, n_sink, n_recent, k):
     ("no_sink_g1", lambda: make_case(625, name="no_sink", B=2, Hq=4, Hkv=4, d=64, dtype="bf16",
                                      seq_lens=[3000, 90], n_sink=0, n_recent=64, k_sel=200), 200),
     ("layer_16k", lambda: qwen06b_decode_case(1000, L=16384, B=1, frac=(1, 8)), None),
+    ("batch16_g4", lambda: make_case(627, name="b16", B=16, Hq=32, Hkv=8, d=128, dtype="bf16",
+                                     seq_lens=[2000 + 131 * i for i in range(16)], n_sink=4, n_recent=256,
+                                     k_sel=384, hh_per_head=16), None),
 ])
 def test_three_launch_step_equals_separate_calls(gpu_lib, name, mk, k):
     """Slow step + Selector + one launch (index-set fast step, pack, combine) against the plain slow step,
