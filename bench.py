@@ -131,7 +131,7 @@ def main():
                          "head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
