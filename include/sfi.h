@@ -317,8 +317,10 @@ SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const 
  * attended positions are, in order: [0, min(n_sink, L_b)), every entry of
  * sel_idx[b, g, 0:k] that lies in [0, L_b) (negative entries are padding), then
  * [max(n_sink, L_b - n_recent), L_b).  A position behind an invalid block-table
- * entry is skipped.  With the entries of sel_idx valid, the result equals
- * sfi_pack_compact followed by sfi_sparse_decode_attn bit for bit.
+ * entry is skipped.  With every entry of sel_idx a valid position (no padding), the
+ * result equals sfi_pack_compact followed by sfi_sparse_decode_attn with cap =
+ * n_sink + k bit for bit; with padding the two split the work at other tokens and
+ * agree to rounding.
  *
  *   sel_idx  int32 [B, Hkv, k], device, e.g. the output of sfi_select_topk; k >= 0
  *            (sel_idx may be NULL when k is 0).
@@ -332,9 +334,11 @@ SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const 
  *   compact_k, compact_v, cap, n_compact  all NULL (cap ignored), or a compact buffer
  *            [B, units, cap, d] (units = Hkv, or Hq with per_head; 16-byte aligned,
  *            cap >= n_sink + k) and n_compact [B]: the launch also writes them exactly as
- *            sfi_pack_compact would for sel_idx (SFI page, Fig. 3B), from the rows it
- *            reads anyway, so the first fast step after a refresh packs the state the
- *            following fast steps read.
+ *            sfi_pack_compact would for sel_idx (SFI page, Fig. 3B), so the first fast
+ *            step after a refresh packs the state the following fast steps read.  With
+ *            one set per KV head and no appended token, work-groups of their own in the
+ *            same launch copy the rows; otherwise the attention work-groups write the
+ *            rows they read.
  *   workspace  as sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent).
  *   Other arguments as sfi_sparse_decode_attn.  Errors: SFI_ERR_INVALID_ARG for a
  *   NULL sel_idx with k > 0, negative k, per_head not 0 or 1, an unpaired
@@ -357,12 +361,19 @@ SFI_API sfi_status sfi_sparse_decode_indexed_attn(const sfi_shape* shape, const 
  * sfi_dense_attn_with_stats_deferred left in slow_workspace into slow_out and
  * slow_lse (SFI page, Fig. 2 and Fig. 3B: the slow step's selection is packed
  * while the next attention runs; here all three run as work-groups of one
- * launch, the attention reading the selected rows in place).  Every output is
- * bit-identical to the plain calls.  The shape, kv and seq_lens are the slow
- * step's; workspace (for this call's own split partials, of
+ * launch, the attention reading the selected rows in place).  The compact
+ * buffer, n_compact, slow_out and slow_lse are bit-identical to the plain calls;
+ * out and lse are as sfi_sparse_decode_indexed_attn gives them.  The shape, kv and
+ * seq_lens are the slow step's; workspace (for this call's own split partials, of
  * sfi_sparse_decode_workspace_size(shape, kv, n_sink + k, n_recent) bytes) and
  * slow_workspace must not overlap.  Errors as the calls it replaces; nothing is
  * launched on any error.
+ *
+ *   q         [B, Hq, d] (pool dtype); out [B, Hq, d] float32, lse [B, Hq] float32 or NULL
+ *   sel_idx   int32 [B, Hkv, k]; compact_k, compact_v [B, Hkv, cap, d] (16-byte aligned,
+ *             cap >= n_sink + k); n_compact int32 [B]
+ *   slow_out  [B, 1, Hq, d] float32 and slow_lse [B, 1, Hq] float32 or NULL, as passed to
+ *             sfi_dense_attn_with_stats_deferred; slow_workspace its workspace
  */
 SFI_API sfi_status sfi_sparse_decode_indexed_attn_merge(const sfi_shape* shape, const sfi_paged_kv* kv,
                                                 const void* q, const int32_t* seq_lens,
