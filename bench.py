@@ -400,6 +400,22 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
         dense(i)
     t_dense = time_loop(dense, n_rep, stream)
     dense_kv = kv_bytes_dense(B, Hkv, L, d)
+    # The slow step itself (dense + logits), with its own split-K combine and deferred as the step
+    # runs it (the combine then rides in the step's last launch); algorithmic bytes are K/V + logits.
+    scs = [torch.empty((B, Hkv, max_len), dtype=torch.float32, device=dev) for _ in range(R)]
+    slow_bytes = dense_kv + B * Hkv * L * 4
+    slow = {}
+    for name, op in (("slow_step", sfi.dense_attn_with_stats), ("slow_step_deferred", sfi.dense_attn_with_stats_deferred)):
+        calls = [sfi.bind(op, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len, n_sink=n_sink,
+                          n_recent=n_recent, out=outs[r], lse=lses[r], scores=scs[r], workspace=ws_dense,
+                          stream=stream) for r, ly in enumerate(layers)]
+        for i in range(R):
+            calls[i]()
+        t_s = time_loop(lambda i: calls[i % R](), n_rep, stream)
+        slow[name] = {"us": round(t_s * 1e6, 2), "GBps": round(slow_bytes / t_s / 1e9, 1),
+                      "pct_peak": round(100 * slow_bytes / t_s / 1e9 / HBM_PEAK_GBS, 1)}
+        del calls
+    del scs
     rows = []
     rng = __import__("numpy").random.default_rng(9)
     for frac in RETENTIONS:
@@ -440,8 +456,9 @@ def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense
                      "dense_us": round(t_dense * 1e6, 2), "dense_GBps": round(dense_kv / t_dense / 1e9, 1),
                      "speedup": round(t_dense / t, 3), "speedup_x_r": round(t_dense / t * r, 3)})
         del comp, fast_calls
-    log(f"sweep L={L} B={B} " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows))
-    return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows}
+    log(f"sweep L={L} B={B} " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows)
+        + f"; slow step {slow['slow_step']['pct_peak']}% of peak, deferred {slow['slow_step_deferred']['pct_peak']}%")
+    return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows, **slow}
 
 
 def gpu_layers(R, L, B, Hq, Hkv, d, dev, seed):
