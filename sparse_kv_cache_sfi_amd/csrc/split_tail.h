@@ -149,9 +149,9 @@ struct SplitTail {
   }
 
   // The merge itself: every thread of the work-group takes part (it has barriers).
-  // Also run by a later launch on the partials an earlier one left (the Selector
-  // launch that finishes a slow step), where the device-coherent loads cost nothing
-  // extra.
+  // Also run by a later launch on the partials an earlier one left (the pack or the
+  // fast-step launch that finishes a deferred slow step), where the device-coherent
+  // loads cost nothing extra.
   __device__ static void merge(const AttnArgs& a, int g, int q_row0, int G, int R, int ns_max, float* tail) {
     const int tid = threadIdx.x;
     constexpr int D4 = D / 4;
@@ -162,9 +162,9 @@ struct SplitTail {
     float* L_r = M_r + R;
 
     // Lanes per float4 group: a power of two, at most a wave, filling 256 threads.  P
-    // fixes the summation order, so it does not depend on the work-group's width: a
-    // wider work-group (the Selector launch) leaves its extra threads idle and adds in
-    // exactly the order of the slow step's own merge.
+    // fixes the summation order, so it is set by that width rather than NT: a wider
+    // work-group would leave its extra threads idle and add in exactly the order of
+    // the slow step's own merge.
     const int n_grp = R * D4;
     int P = 1;
     while (P < kWave && 2 * P * n_grp <= 256) P *= 2;
