@@ -8,7 +8,7 @@ template <typename T, int D, int G, bool SPARSE, int SCORES, bool APPEND = false
           bool DEFER = false>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
   using S = DecodeShape<T, D, G>;
-  __shared__ __attribute__((aligned(16))) char smem[INDEXED ? S::SMEM_IDX : S::SMEM];
+  __shared__ __attribute__((aligned(16))) char smem[(INDEXED || SCORES == 1) ? S::SMEM_IDX : S::SMEM];
   decode_unit<T, D, G, SPARSE, SCORES, APPEND, INDEXED, DEFER>(a, blockIdx.z, blockIdx.y, blockIdx.x, blockIdx.z,
                                                                smem);
 }

@@ -54,10 +54,12 @@ struct DecodeShape {
   static constexpr int TAIL = SplitTail<D>::bytes(G, kMaxSplits);
   static constexpr int SMEM = kBtSlots * 4 + WAVES * G * D * 4 + WAVES * G * 2 * 4 + 16 + TAIL;
   // The index-set fast step also stages its split's sink and selected rows as page
-  // slots (page * 16 + row, or -1), one int per token.
+  // slots (page * 16 + row, or -1), one int per token; the slow step keeps its split's
+  // group-summed logits there until the loop ends.
   static constexpr int IDX_OFF = (SMEM + 15) / 16 * 16;
   static constexpr int SMEM_IDX = IDX_OFF + kMaxSplitTokens * 4;
   static_assert(C >= 1, "row too short for the lane mapping");
+  static_assert(2 * U * ROWS <= kWave, "a wave's logits of an iteration pair fit its lanes");
 };
 
 template <typename T>
@@ -234,6 +236,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
                        : a.scores + ((int64_t)b * a.Hkv + g) * a.score_stride;
   }
 
+  float sbuf = 0.f;   // logits of the current iteration pair (SCORES == 1)
+  float* sc_s = reinterpret_cast<float*>(smem + S::IDX_OFF);
   float m[G], l[G], o[G][E];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -251,7 +255,10 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   // Where slot u of iteration `it` comes from: its position p, whether it lies in
   // this split (in) and whether it is backed by a compact row or a valid page (ok).
   auto locate = [&](int it, int u, int& vi, int& p, bool& in, bool& compact, int& pg, bool& ok) {
-    vi = t0 + it * TILE + (w * U + u) * ROWS + r;
+    // Iterations go in pairs; in pair it / 2 wave w takes the 2 U ROWS consecutive rows
+    // starting at w * 2 U ROWS of the pair's 2 TILE rows, so a wave's logits of both
+    // iterations are contiguous.
+    vi = t0 + (it >> 1) * (2 * TILE) + w * (2 * U * ROWS) + (it & 1) * (U * ROWS) + u * ROWS + r;
     in = vi < t1;
     compact = SPARSE && vi < n_c;
     if constexpr (INDEXED) {
@@ -337,22 +344,43 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
         for (int c = 0; c < C; ++c) acc = dot_chunk<T>(q[h][c], B.k[u][c], acc);
         s[u][h] = group_sum<LPR>(acc);
       }
-    if constexpr (SCORES) {
+    if constexpr (SCORES == 2) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (sub == 0 && in_[u]) {
           const int j = pos_[u];
           const bool cand = ok_[u] && j >= clo && j < chi;
-          if constexpr (SCORES == 2) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) srow[h * a.score_stride + j] = cand ? s[u][h] * a.scale : neg_inf();
-          } else {
-            float sc = 0.f;
-#pragma unroll
-            for (int h = 0; h < G; ++h) sc += s[u][h];
-            srow[j] = cand ? sc * a.scale : neg_inf();
-          }
+          for (int h = 0; h < G; ++h) srow[h * a.score_stride + j] = cand ? s[u][h] * a.scale : neg_inf();
         }
+      }
+    } else if constexpr (SCORES == 1) {
+      // Group-summed logits, gathered so that lane (it mod 2) WR + u ROWS + r holds row (u, r)
+      // of this iteration (every lane of a row group holds its sum; lane r LPR is the
+      // source); after the second iteration of a pair the wave's 2 WR consecutive positions
+      // go to the split's LDS copy, which is written out in one burst after the loop
+      // (writes spread through the K/V stream cost several times their bytes).
+      constexpr int WR = U * ROWS;
+      float val[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float sc = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc += s[u][h];
+        const int j = pos_[u];
+        val[u] = (ok_[u] && j >= clo && j < chi) ? sc * a.scale : neg_inf();
+      }
+      const int jj = lane % WR, uu = jj / ROWS, rr = jj % ROWS;
+      float mine = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float t = __shfl(val[u], rr * LPR);
+        mine = (u == uu) ? t : mine;
+      }
+      if (lane / WR == (it & 1)) sbuf = mine;
+      if ((it & 1) && lane < 2 * WR) {
+        const int pos = t0 + (it >> 1) * (2 * TILE) + w * (2 * WR) + lane;
+        if (pos < t1) sc_s[pos - t0] = sbuf;
       }
     }
     bool need = false;
@@ -468,6 +496,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   }
   __syncthreads();
+  if constexpr (SCORES == 1)
+    for (int j = tid; j < t1 - t0; j += NT) srow[t0 + j] = sc_s[j];
 
   // Merge the waves and write the split's result.
   for (int idx = tid; idx < G * D; idx += NT) {

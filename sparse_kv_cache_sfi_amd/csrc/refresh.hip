@@ -10,7 +10,8 @@ namespace sfi {
 // attention grid fills the CUs); the rest are the slow step's split-K units.
 template <typename T, int D, int G, int SCORES>
 __global__ __launch_bounds__(256) void dense_refresh_kernel(AttnArgs a, RefreshArgs r) {
-  constexpr int SD = DecodeShape<T, D, G>::SMEM, SR = RiderShape::SMEM;
+  constexpr int SD = SCORES == 1 ? DecodeShape<T, D, G>::SMEM_IDX : DecodeShape<T, D, G>::SMEM;
+  constexpr int SR = RiderShape::SMEM;
   __shared__ __attribute__((aligned(16))) char smem[SD > SR ? SD : SR];
   int bid = blockIdx.x;
   if (bid < r.rows) {
