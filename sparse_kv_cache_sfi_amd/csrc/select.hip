@@ -10,7 +10,8 @@
 // order-preserving uint32 keys (-0.0 folded onto +0.0, so the key order is the
 // IEEE order).  Radix passes, most significant digit first, narrow the key T of
 // the k_eff-th largest element, each pass an LDS histogram of the keys that
-// still match the digits found so far (integer counts: order-independent).  A
+// still match the digits found so far (integer counts: order-independent); the
+// narrowing stops once the chosen bin holds exactly the keys still wanted.  A
 // final ordered pass takes every key > T and the lowest-positioned keys == T,
 // writing positions in ascending order through block-wide exclusive scans, so
 // the output is identical on every run.  Rows of up to 65536 candidates keep
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   __shared__ uint32_t hist[kSelWaves][256];
   __shared__ int scan_sh[kSelWaves + 1];
   __shared__ int scan_sh2[kSelWaves + 1];   // the collection's second scan (no barrier between the two)
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   const int row = blockIdx.x;
   const int b = row / Hkv;
   const int tid = threadIdx.x, w = tid / kWave;
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   }
 
   // Radix select: after the passes, prefix == key of the k_eff-th largest element
-  // and `remaining` == how many elements equal to it are taken.
+  // and `remaining` == how many elements equal to it are taken (or, after an early
+  // exit, prefix is a lower bound of the taken keys and all keys equal to it count).
   uint32_t prefix = 0u, mask = 0u;
   int remaining = k_eff;
   for (int pass = 0; pass < 4; ++pass) {
@@ -104,13 +106,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     if (tid < 256 && above < remaining && above + cnt >= remaining) {
       pick[0] = 255 - tid;
       pick[1] = above;
+      pick[2] = cnt;
     }
     __syncthreads();
     const uint32_t digit = (uint32_t)pick[0];
+    const int in_bin = pick[2];
     remaining -= pick[1];
     prefix |= digit << shift;
     mask |= 255u << shift;
     __syncthreads();
+    // The digit's bin holds exactly the keys still wanted: the selection is every
+    // key >= prefix (its low digits are zero), as the remaining passes would find,
+    // and each of them costs a read of the row.
+    if (pass < 3 && in_bin == remaining) {
+      remaining = n;
+      break;
+    }
   }
 
   // Ordered collection: keys > prefix, plus the first `remaining` keys == prefix.
@@ -188,8 +199,9 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int x, int y, int2* total,
 
 // Among the bins of this pass (histogram `hist`, nb bins), find the digit holding
 // the remaining-th largest matching key: pick[0] = digit, pick[1] = number of
-// matching keys with a larger digit.  Thread t owns bins nb-1-c*t ... nb-c*t-c;
-// it zeroes them once read, so the histogram is clear for the next pass.
+// matching keys with a larger digit, pick[2] = keys in the digit's bin.  Thread t
+// owns bins nb-1-c*t ... nb-c*t-c; it zeroes them once read, so the histogram is
+// clear for the next pass.
 __device__ __forceinline__ void find_digit(uint32_t* hist, int nb, int remaining, int* pick, int* scan_sh) {
   const int tid = threadIdx.x;
   const int c = nb / kSelThreads > 0 ? nb / kSelThreads : 1;
@@ -214,6 +226,7 @@ __device__ __forceinline__ void find_digit(uint32_t* hist, int nb, int remaining
         if (run < remaining && run + cnt[i] >= remaining) {
           pick[0] = nb - 1 - c * tid - i;
           pick[1] = run;
+          pick[2] = cnt[i];
         }
         run += cnt[i];
       }
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
   __shared__ uint32_t hist[kHistBins];
   __shared__ int scan_sh[kSelWaves + 1];
   __shared__ int2 scan2_sh[kSelWaves + 1];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   const int row = blockIdx.x;
   const int b = row / Hkv;
   const int tid = threadIdx.x;
@@ -286,6 +299,14 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(const float* __
     remaining -= pick[1];
     prefix |= (uint32_t)pick[0] << shift;
     mask |= dmask << shift;
+    // The digit's bin holds exactly the keys still wanted: they are all taken, so
+    // the selection is every key >= prefix (the low digits of prefix are zero), and
+    // the keys == prefix are all taken as well.  The set is the one the remaining
+    // passes would reach.
+    if (pass < 2 && pick[2] == remaining) {
+      remaining = n;
+      break;
+    }
   }
 
   // Ordered collection: every key > T, and the first `remaining` keys == T in

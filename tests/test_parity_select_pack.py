@@ -137,3 +137,43 @@ def test_selector_rows_beyond_the_register_variant(gpu_lib, k):
     B, H, stride = 1, 2, 131072
     sc = (np.round(rng.standard_normal((B, H, stride)) * 16) / 16).astype(np.float32)
     _select_both(gpu_lib, sc, [131072], k, n_sink=4, n_recent=256, t_q=8)
+
+
+def _key_to_float(keys):
+    """Inverse of the Selector's order-preserving key map (positive floats have the top key bit set)."""
+    keys = np.asarray(keys, dtype=np.uint64)
+    bits = np.where(keys & 0x80000000, keys & 0x7FFFFFFF, (~keys) & 0xFFFFFFFF).astype(np.uint32)
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("stride,digits", [(4096, [(20, 12), (8, 12)]),
+                                           (131072, [(24, 8), (16, 8), (8, 8)])],
+                         ids=["register_rows", "streaming_rows"])
+def test_selector_bin_that_holds_exactly_the_wanted_keys(gpu_lib, stride, digits):
+    """A radix pass whose chosen bin holds exactly the keys still wanted settles the selection.
+
+    Row h plants, at random positions, a keys in a higher bin of digit level h, m keys in the bin
+    (two of them equal to the bin's lowest key, the rest above it), and keys just below the bin that
+    share its higher digits, so no earlier level settles it; k = a + m.  The last row has no planted
+    structure (continuous scores).  Selections must equal the oracle's top-k.
+    """
+    rng = np.random.default_rng(stride)
+    H = len(digits) + 1
+    n_sink, n_recent = 4, 16
+    lo, hi = O.candidate_range(stride, 1, n_sink, n_recent)
+    a, m = 5, 6
+    sc = np.empty((1, H, stride), np.float32)
+    for h, (shift, _) in enumerate(digits):
+        bw = 1 << shift
+        P = (0xC0000000 & ~((bw << 4) - 1)) | (5 << shift)   # digit 5 at this level, lower digits zero
+        keys = rng.integers(0x10000000, 0x70000000, size=stride, dtype=np.uint64)   # negative floats
+        planted = [P + 2 * bw + j for j in range(a)]
+        planted += [P, P] + [P + int(x) for x in rng.choice(np.arange(1, min(bw, 1 << 16)), m - 2, replace=False)]
+        planted += [P - 1 - j for j in range(3)]
+        pos = rng.choice(np.arange(lo, hi), len(planted), replace=False)
+        keys[pos] = planted
+        sc[0, h] = _key_to_float(keys)
+    sc[0, H - 1] = rng.standard_normal(stride).astype(np.float32)
+    _select_both(gpu_lib, sc, [stride], a + m, n_sink=n_sink, n_recent=n_recent)
+    for k in (1, 17, 300):
+        _select_both(gpu_lib, sc, [stride], k, n_sink=n_sink, n_recent=n_recent)
