@@ -3,7 +3,8 @@ times (bound calls, shared workspaces, the refresh driver).
 
 * The 16K decode layer (1 request, 16 query / 8 KV heads, d 128, 12.5 % retention):
   one whole step (slow step with logits -> Selector -> pack -> fast step) on the
-  benchmark's first replica, every KV head checked against the oracle.
+  benchmark's first replica, and twice the three-launch form the benchmark times on its
+  second, every KV head checked against the oracle.
 * The batched decode (16 requests, 32 query / 8 KV heads, lengths in [16K, 32K],
   selected 1024, recent 256): one slow and one fast step of RefreshSchedule; the
   Selector and pack checked on every row, attention outputs and logits on sampled
@@ -62,6 +63,10 @@ def test_16k_layer_step_at_full_size(gpu_lib):
     for call in calls:
         call()
     torch.cuda.synchronize()
+    _check_16k_step(c, L, k, cap, out, lse, sc, sel, ck, cv, nc, fo, fl)
+
+
+def _check_16k_step(c, L, k, cap, out, lse, sc, sel, ck, cv, nc, fo, fl):
     qv = c.q_values()[0, 0]
     ro, rl = O.dense_attention(qv[None], c.kv.k, c.kv.v, c.kv.block_table[0], L, c.scale, c.Hkv, kv_dtype="bf16")
     assert_close(out.cpu().numpy()[0, 0], ro[0], OUT_TOL, "dense out")
@@ -82,6 +87,53 @@ def test_16k_layer_step_at_full_size(gpu_lib):
     # the planted heavy hitters are found
     for g in range(c.Hkv):
         assert set(c.planted[(0, g)].tolist()) <= set(got_sel[g].tolist()), g
+
+
+def test_16k_layer_three_launch_step_at_full_size(gpu_lib):
+    """The step as the benchmark times it: the slow step leaves its split-K combine behind, the
+    Selector runs, and one launch does the fast step over the selection read in place, the pack
+    and that combine.  Two steps in a row on the same workspaces (the split counters must come back
+    to zero), each checked against the oracle."""
+    c = qwen06b_decode_case(1001)            # the benchmark's second replica
+    dc = DevCase(c)
+    L, k, B = int(c.seq_lens[0]), c.k_sel, 1
+    cap = c.n_sink + k
+    q1 = dc.q[:, 0].contiguous()
+    out = torch.empty((B, 1, c.Hq, c.d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, c.Hq), dtype=torch.float32, device=DEV)
+    sc = torch.empty((B, c.Hkv, L), dtype=torch.float32, device=DEV)
+    sel = torch.empty((B, c.Hkv, k), dtype=torch.int32, device=DEV)
+    ck = torch.empty((B, c.Hkv, cap, c.d), dtype=torch.bfloat16, device=DEV)
+    cv = torch.empty_like(ck)
+    nc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    fo = torch.empty((B, c.Hq, c.d), dtype=torch.float32, device=DEV)
+    fl = torch.empty((B, c.Hq), dtype=torch.float32, device=DEV)
+    kw = dict(n_sink=c.n_sink, n_recent=c.n_recent)
+    ws_dense = torch.zeros(gpu_lib.workspace_size("dense", k_pool=dc.k, block_table=dc.bt, Hq=c.Hq,
+                                                  dtype=torch.bfloat16, max_seq_len=L) + 16,
+                           dtype=torch.uint8, device=DEV)
+    ws_sparse = torch.zeros(gpu_lib.workspace_size("sparse", k_pool=dc.k, block_table=dc.bt, Hq=c.Hq,
+                                                   dtype=torch.bfloat16, max_seq_len=L, cap=cap,
+                                                   n_recent=c.n_recent) + 16, dtype=torch.uint8, device=DEV)
+    calls = [
+        gpu_lib.bind(gpu_lib.dense_attn_with_stats_deferred, dc.q, dc.k, dc.v, dc.bt, dc.lens, max_seq_len=L,
+                     out=out, lse=lse, scores=sc, workspace=ws_dense, **kw),
+        gpu_lib.bind(gpu_lib.select_topk, sc, dc.lens, k=k, sel_idx=sel, **kw),
+        gpu_lib.bind(gpu_lib.sparse_decode_indexed_attn_merge, q1, dc.k, dc.v, dc.bt, dc.lens, sel,
+                     max_seq_len=L, slow_out=out, slow_lse=lse, slow_workspace=ws_dense, compact_k=ck,
+                     compact_v=cv, n_compact=nc, out=fo, lse=fl, workspace=ws_sparse, **kw),
+    ]
+    for rep in range(2):
+        for t in (out, lse, sc, fo, fl):
+            t.fill_(float("nan"))
+        sel.fill_(-7)
+        ck.zero_()
+        cv.zero_()
+        nc.fill_(-1)
+        for call in calls:
+            call()
+        torch.cuda.synchronize()
+        _check_16k_step(c, L, k, cap, out, lse, sc, sel, ck, cv, nc, fo, fl)
 
 
 def test_batched_16k_32k_decode_at_full_size(gpu_lib):
