@@ -338,3 +338,23 @@ def test_tiny_sequence_one_slow_step_then_eight_fast_steps(gpu_lib):
                                        c.kv.block_table[0], Lf, c.n_sink, c.n_recent, c.scale)
         assert_close(out.cpu().numpy()[0], ref_o, OUT_TOL, f"step {step}")
         assert_close(lse.cpu().numpy()[0], ref_l, LSE_TOL, f"step {step}")
+
+
+@pytest.mark.parametrize("L", [64, 65, 128, 129, 255, 256, 257, 2048, 2049, 4096, 4097])
+def test_slow_step_logits_at_tile_and_split_boundaries(gpu_lib, L):
+    """Lengths on and one past the slow step's iteration (64 tokens), iteration-pair (128) and split
+    boundaries; the plan gives these lengths 64 to 320 tokens per split, some not a whole number of
+    pairs (192, 320).  Each split keeps its logits in LDS and writes them after its loop, so every
+    boundary decides which positions a split writes.  The plain slow step is checked against the
+    oracle; the variant that leaves its combine to a later launch must write the same logits, bit for
+    bit."""
+    c = make_case(1200 + L, name="tb", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[L, max(1, L - 1)],
+                  n_sink=4, n_recent=64, k_sel=8, hh_per_head=2)
+    dc = DevCase(c)
+    stride = dc.max_seq_len + 5
+    _, _, sc = _dense_check(gpu_lib, c, dc, stride=stride)
+    _, _, sc_d, _ = gpu_lib.dense_attn_with_stats_deferred(dc.q, dc.k, dc.v, dc.bt, dc.lens,
+                                                           max_seq_len=dc.max_seq_len, n_sink=c.n_sink,
+                                                           n_recent=c.n_recent, scale=c.scale, score_stride=stride)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(sc_d).view(np.uint32), sc.view(np.uint32))
