@@ -316,7 +316,6 @@ def main():
     }
 
     result["separate_combine_step"] = separate_combine_step(layers, main_s, args.steps, step_bytes, b2b)
-    result["riders_16k"] = riders_16k(sfi, layers, main_s, k_sel, cap, n_sink, n_recent, max_len, ws_dense)
     # every kernel of the step back to back over the replicas (HIP events on its stream)
     kern = {}
     for name in ("select", "finish", "pack", "fast"):
@@ -922,87 +921,7 @@ def refresh_overlap(sfi, dev):
             r[name] = {"overlapped_us": round(t_o * 1e6, 2),
                        "hidden_fraction": round(max(0.0, min(1.0, (t_s - t_o) / moved)), 3)}
         res[f"partner_{kind}"] = r
-    # Maintenance riding in the next layer's launch: layer i+1's slow step (dense + logits) carries
-    # layer i's Selector and pack as extra work-groups.  Serial: the same work as four launches.
-    scores_b = torch.empty_like(scores)
-    sel_r, ck_r, cv_r, nc_r = torch.empty_like(sel), torch.empty_like(ck), torch.empty_like(cv), torch.empty_like(nc)
-
-    def next_slow(stream):
-        sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[1],
-                                  lse=lses[1], scores=scores_b, workspace=ws_b, stream=stream)
-
-    def fused(stream):
-        sfi.dense_attn_with_refresh(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[1],
-                                    lse=lses[1], scores=scores_b, workspace=ws_b, r_k_pool=k, r_v_pool=v,
-                                    r_block_table=bt, r_max_seq_len=L, r_scores=scores, r_n_sink=4, r_n_recent=256,
-                                    k=2048, cap=cap, sel_idx=sel_r, compact_k=ck_r, compact_v=cv_r, n_compact=nc_r,
-                                    stream=stream)
-
-    def fused_select(stream):
-        sfi.dense_attn_with_refresh(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[1],
-                                    lse=lses[1], scores=scores_b, workspace=ws_b, r_k_pool=k, r_v_pool=v,
-                                    r_block_table=bt, r_max_seq_len=L, r_scores=scores, r_n_sink=4, r_n_recent=256,
-                                    k=2048, sel_idx=sel_r, pack=False, stream=stream)
-
-    def pack_r(stream):
-        sfi.pack_compact(k, v, bt, lens, sel_r, n_sink=4, cap=cap, max_seq_len=L, compact_k=ck_r, compact_v=cv_r,
-                         n_compact=nc_r, stream=stream)
-
-    t_next = time_loop(lambda i: next_slow(main_s), n, main_s)
-    t_ser = time_loop(lambda i: (slow(main_s), select(main_s), pack(main_s), next_slow(main_s)), n, main_s)
-    t_fs = time_loop(lambda i: (slow(main_s), fused_select(main_s), pack_r(main_s)), n, main_s)
-    torch.cuda.synchronize()
-    same_s = bool(torch.equal(sel_r, sel) and torch.equal(ck_r, ck) and torch.equal(nc_r, nc))
-    t_fp = time_loop(lambda i: (slow(main_s), fused(main_s)), n, main_s)
-    torch.cuda.synchronize()
-    same_p = bool(torch.equal(sel_r, sel) and torch.equal(ck_r, ck) and torch.equal(nc_r, nc))
-    res["riders"] = {"next_slow_us": round(t_next * 1e6, 2), "serial_us": round(t_ser * 1e6, 2),
-                     "select_rides_us": round(t_fs * 1e6, 2),
-                     "select_rides_hidden": round(max(0.0, min(1.0, (t_ser - t_fs) / t_sel)), 3),
-                     "select_and_pack_ride_us": round(t_fp * 1e6, 2),
-                     "select_and_pack_ride_hidden": round(max(0.0, min(1.0, (t_ser - t_fp) / (t_sel + t_pack))), 3),
-                     "matches_separate_calls": same_s and same_p}
     log(f"refresh overlap {res}")
-    return res
-
-
-def riders_16k(sfi, layers, stream, k_sel, cap, n_sink, n_recent, max_len, ws_dense):
-    """Two consecutive 16K layers at batch 1: layer i's slow step, then layer i+1's slow step with
-    layer i's Selector either as a separate launch before it (serial) or riding in its launch; the
-    pack follows as its own launch either way.  hidden = (serial - riding) / Selector."""
-    import torch
-    li, lj = layers[0], layers[1]
-    ws_b = torch.zeros_like(ws_dense)
-    sel, ck, cv, nc = (torch.empty_like(li["sel"]), torch.empty_like(li["ck"]), torch.empty_like(li["cv"]),
-                       torch.empty_like(li["nc"]))
-    sc_j = torch.empty_like(lj["scores"])
-
-    def slow_i():
-        li["dense"]()
-
-    def slow_j():
-        sfi.dense_attn_with_stats(lj["q"], lj["k"], lj["v"], lj["bt"], lj["lens"], max_seq_len=max_len,
-                                  n_sink=n_sink, n_recent=n_recent, out=lj["out"], lse=lj["lse"], scores=sc_j,
-                                  workspace=ws_b, stream=stream)
-
-    fused = sfi.bind(sfi.dense_attn_with_refresh, lj["q"], lj["k"], lj["v"], lj["bt"], lj["lens"],
-                     max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, out=lj["out"], lse=lj["lse"],
-                     scores=sc_j, workspace=ws_b, r_k_pool=li["k"], r_v_pool=li["v"], r_block_table=li["bt"],
-                     r_max_seq_len=max_len, r_scores=li["scores"], r_n_sink=n_sink, r_n_recent=n_recent, k=k_sel,
-                     sel_idx=sel, pack=False, stream=stream)
-    pack = sfi.bind(sfi.pack_compact, li["k"], li["v"], li["bt"], li["lens"], sel, n_sink=n_sink, cap=cap,
-                    max_seq_len=max_len, compact_k=ck, compact_v=cv, n_compact=nc, stream=stream)
-    n = 50
-    t_sel = time_loop(lambda i: li["select"](), n, stream)
-    t_ser = time_loop(lambda i: (slow_i(), li["select"](), li["pack"](), slow_j()), n, stream)
-    t_fus = time_loop(lambda i: (slow_i(), fused(), pack()), n, stream)
-    torch.cuda.synchronize()
-    same = bool(torch.equal(sel, li["sel"]) and torch.equal(ck, li["ck"]) and torch.equal(nc, li["nc"]))
-    res = {"select_us": round(t_sel * 1e6, 2), "serial_us": round(t_ser * 1e6, 2),
-           "select_rides_us": round(t_fus * 1e6, 2),
-           "hidden_fraction": round(max(0.0, min(1.0, (t_ser - t_fus) / t_sel)), 3),
-           "matches_separate_calls": same}
-    log(f"riders 16K {res}")
     return res
 
 

@@ -131,56 +131,6 @@ SFI_API sfi_status sfi_dense_attn_workspace_size(const sfi_shape* shape, const s
                                          int32_t t_q, size_t* bytes);
 
 /*
- * Slow-step maintenance of layer i, carried by layer i+1's launch.
- * SFI page, Fig. 3A: the Selector and the cache reorganisation of layer i run
- * while layer i+1's attention runs.  Here they run inside one launch instead of
- * on a second stream: the grid's first batch * num_kv_heads work-groups each
- * select one (request, KV head) row of layer i (the Selector's definition, as
- * sfi_select_topk with t_q = 1) and, when compact_k is non-NULL, pack that
- * row's compact buffer (as sfi_pack_compact), while the rest compute layer
- * i+1's slow step (as sfi_dense_attn_with_stats with t_q = 1).  Every output
- * is bit-identical to those calls made in order.  The two layers share shape,
- * batch and seq_lens; each has its own pools.  With compact_k NULL only the
- * selection rides (compact_v, cap and n_compact are then ignored) and the
- * caller packs with sfi_pack_compact afterwards.
- *
- *  kv            layer i's paged K/V (pools, block table, sizes)
- *  scores        layer i's masked logits [B, Hkv, score_stride] float32, as the
- *                slow step of layer i wrote them; must not be the launch's own
- *                scores.  score_stride >= kv.max_seq_len.
- *  n_sink, n_recent  layer i's budgets (define its candidate set)
- *  k             selected tokens per KV head, 1 <= k <= 8192
- *  sel_idx       out [B, Hkv, k] int32 (ascending, -1 padded)
- *  compact_k, compact_v  out [B, Hkv, cap, d], 16-byte aligned; cap >= n_sink + k;
- *                or compact_k NULL: selection only
- *  n_compact     out [B] int32 (when packing)
- */
-typedef struct sfi_refresh {
-  sfi_paged_kv kv;
-  const float* scores;
-  int64_t score_stride;
-  int32_t n_sink;
-  int32_t n_recent;
-  int32_t k;
-  int32_t* sel_idx;
-  void* compact_k;
-  void* compact_v;
-  int32_t cap;
-  int32_t* n_compact;
-} sfi_refresh;
-
-/*
- * Layer i+1's slow step (arguments as sfi_dense_attn_with_stats with t_q = 1;
- * same workspace size) plus the maintenance of layer i described by refresh.
- * Errors as the calls it combines; nothing is launched on any error.
- */
-SFI_API sfi_status sfi_dense_attn_with_refresh(const sfi_shape* shape, const sfi_paged_kv* kv,
-                                       const void* q, const int32_t* seq_lens, int32_t n_sink,
-                                       int32_t n_recent, float* out, float* lse, float* scores,
-                                       int64_t score_stride, const sfi_refresh* refresh,
-                                       void* workspace, size_t workspace_bytes, void* stream);
-
-/*
  * Selector: top-k over each KV head's masked logits.
  * SFI page, Abstract and Fig. 2 caption (the Selector refreshes the selected
  * memory from the slow step's logits); Fig. 3A (it runs on the auxiliary
@@ -323,7 +273,8 @@ SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const 
  * agree to rounding.
  *
  *   sel_idx  int32 [B, Hkv, k], device, e.g. the output of sfi_select_topk; k >= 0
- *            (sel_idx may be NULL when k is 0).
+ *            (sel_idx may be NULL when k is 0; n_sink = k = 0 attends the recent
+ *            window alone).
  *   per_head 0: one set per KV head, shared by its query heads.  1: one set per
  *            query head, sel_idx [B, Hq, k] (per-query-head selection, e.g.
  *            sfi_select_topk over the rows of sfi_dense_attn_with_head_stats); query

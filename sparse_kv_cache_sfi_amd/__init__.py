@@ -23,7 +23,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats", "dense_attn_with_refresh",
+    "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats",
     "select_topk", "pack_compact", "dense_attn_with_stats_deferred", "pack_compact_merge",
     "sparse_decode_indexed_attn_merge",
     "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
@@ -47,12 +47,6 @@ class SfiPagedKV(ctypes.Structure):
                 ("page_size", c_int32), ("num_pages", c_int32), ("max_seq_len", c_int32)]
 
 
-class SfiRefresh(ctypes.Structure):
-    _fields_ = [("kv", SfiPagedKV), ("scores", c_void_p), ("score_stride", c_int64), ("n_sink", c_int32),
-                ("n_recent", c_int32), ("k", c_int32), ("sel_idx", c_void_p), ("compact_k", c_void_p),
-                ("compact_v", c_void_p), ("cap", c_int32), ("n_compact", c_void_p)]
-
-
 class SfiError(RuntimeError):
     def __init__(self, status: int, call: str, message: str):
         super().__init__(f"{call} failed with status {status}: {message}")
@@ -64,8 +58,6 @@ _SIGS = {
     "sfi_dense_attn_with_stats": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                   c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
     "sfi_dense_attn_workspace_size": [_SHAPE_P, _KV_P, c_int32, POINTER(c_size_t)],
-    "sfi_dense_attn_with_refresh": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                    c_void_p, c_int64, POINTER(SfiRefresh), c_void_p, c_size_t, c_void_p],
     "sfi_select_topk": [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32, c_int32, c_int32, c_int32,
                         c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, POINTER(c_size_t)],
@@ -244,14 +236,19 @@ def _i32(t: torch.Tensor, name: str) -> None:
         raise TypeError(f"{name} must be int32")
 
 
-def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device, stream=None) -> Optional[torch.Tensor]:
     if workspace is not None:
         _dev(workspace, "workspace")
         return workspace
     if nbytes == 0:
         return None
-    # Zero-filled: the split-K arrival counters at its start must read zero on first use.
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    # Zero-filled: the split-K arrival counters at its start must read zero on first use.  The
+    # fill runs on the stream the call is made on, and the allocator is told that stream uses
+    # the block, so neither the fill nor a reuse of the block can overtake the launch.
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    with torch.cuda.stream(s):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    ws.record_stream(s)
     if _binding is not None:
         _binding["keep"].append(ws)
     return ws
@@ -320,87 +317,11 @@ def dense_attn_with_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     stride = scores.shape[-1] if scores is not None else 0
     need = c_size_t(0)
     _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), t_q, ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_dense_attn_with_stats", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), t_q,
           seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), _ptr(scores), stride, _ptr(ws),
           _nbytes(ws), _stream(stream, dev))
     return out, lse, scores
-
-
-def dense_attn_with_refresh(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                            block_table: torch.Tensor, seq_lens: torch.Tensor, *, max_seq_len: int,
-                            n_sink: int = 0, n_recent: int = 0, scale: Optional[float] = None,
-                            with_scores: bool = True, score_stride: Optional[int] = None,
-                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                            scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                            r_k_pool: torch.Tensor, r_v_pool: torch.Tensor, r_block_table: torch.Tensor,
-                            r_max_seq_len: int, r_scores: torch.Tensor, r_n_sink: int, r_n_recent: int, k: int,
-                            cap: int = 0, sel_idx: Optional[torch.Tensor] = None,
-                            compact_k: Optional[torch.Tensor] = None, compact_v: Optional[torch.Tensor] = None,
-                            n_compact: Optional[torch.Tensor] = None, pack: bool = True, stream=None):
-    """Slow step of one layer (q [B, 1, Hq, d], as dense_attn_with_stats) with the Selector (and,
-    with pack=True, the pack) of the previous layer (its pools r_*, its logits r_scores
-    [B, Hkv, stride]) riding in the same launch.
-    -> (out, lse, scores, sel_idx, compact_k, compact_v, n_compact); the last three are None
-    when pack is False."""
-    _dev(q, "q")
-    _i32(seq_lens, "seq_lens")
-    _dev(r_scores, "r_scores")
-    if q.dim() != 4:
-        raise ValueError("q must be [B, 1, Hq, d]")
-    B, t_q, Hq, d = q.shape
-    if t_q != 1:
-        raise ValueError("the refresh launch takes one query token per request")
-    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
-    rkv = _kv(r_k_pool, r_v_pool, r_block_table, r_max_seq_len)
-    Hkv = _check_pool(k_pool, v_pool, block_table, B, d)
-    if _check_pool(r_k_pool, r_v_pool, r_block_table, B, d) != Hkv:
-        raise ValueError("both layers' pools must hold the same KV heads")
-    if q.dtype != k_pool.dtype or r_k_pool.dtype != k_pool.dtype or tuple(seq_lens.shape) != (B,):
-        raise ValueError("q and both layers' pools must share a dtype; seq_lens must be [B]")
-    _f32_out(r_scores, (B, Hkv, r_scores.shape[-1]), "r_scores")
-    _f32_out(out, (B, 1, Hq, d), "out")
-    _f32_out(lse, (B, 1, Hq), "lse")
-    shape = _shape(B, Hq, Hkv, d, _dtype_code(q), scale)
-    dev = q.device
-    if out is None:
-        out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
-    if with_scores and scores is None:
-        stride = int(score_stride if score_stride is not None else max_seq_len)
-        scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=dev)
-    stride = scores.shape[-1] if scores is not None else 0
-    if sel_idx is None:
-        sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
-    _i32(sel_idx, "sel_idx")
-    if tuple(sel_idx.shape) != (B, Hkv, k):
-        raise ValueError(f"sel_idx must be [B, Hkv, k] = {(B, Hkv, k)}")
-    if scores is not None:
-        _f32_out(scores, (B, Hkv, scores.shape[-1]), "scores")
-    if pack:
-        if compact_k is None:
-            compact_k = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
-        if compact_v is None:
-            compact_v = torch.empty((B, Hkv, cap, d), dtype=r_k_pool.dtype, device=dev)
-        if n_compact is None:
-            n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
-        for tt, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
-            _dev(tt, n)
-            if tt.dtype != r_k_pool.dtype or tuple(tt.shape) != (B, Hkv, cap, d):
-                raise ValueError(f"{n} must be [B, Hkv, cap, d] in the pool dtype")
-        _i32(n_compact, "n_compact")
-    else:
-        compact_k = compact_v = n_compact = None
-    ref = SfiRefresh(rkv, r_scores.data_ptr(), r_scores.shape[-1], r_n_sink, r_n_recent, k, sel_idx.data_ptr(),
-                     _ptr(compact_k), _ptr(compact_v), cap, _ptr(n_compact))
-    need = c_size_t(0)
-    _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
-    _call("sfi_dense_attn_with_refresh", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
-          seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), _ptr(scores), stride,
-          ctypes.byref(ref), _ptr(ws), _nbytes(ws), _stream(stream, dev))
-    return out, lse, scores, sel_idx, compact_k, compact_v, n_compact
 
 
 def dense_attn_with_stats_deferred(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -435,7 +356,7 @@ def dense_attn_with_stats_deferred(q: torch.Tensor, k_pool: torch.Tensor, v_pool
     _f32_out(scores, (B, Hkv, scores.shape[-1]), "scores")
     need = c_size_t(0)
     _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_dense_attn_with_stats_deferred", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
           seq_lens.data_ptr(), n_sink, n_recent, out.data_ptr(), _ptr(lse), scores.data_ptr(), scores.shape[-1],
           _ptr(ws), _nbytes(ws), _stream(stream, dev))
@@ -577,7 +498,7 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
     need = c_size_t(0)
     _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), cap, n_recent,
           ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     if k_new is None:
         _call("sfi_sparse_decode_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
               n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
@@ -649,7 +570,7 @@ def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
     need = c_size_t(0)
     _call("sfi_sparse_decode_workspace_size", ctypes.byref(unit_shape), ctypes.byref(kv), n_sink + k, n_recent,
           ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_sparse_decode_indexed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), _ptr(k_new),
           _ptr(v_new), seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, int(per_head),
           _ptr(compact_k), _ptr(compact_v), cap, _ptr(n_compact), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
@@ -707,7 +628,7 @@ def sparse_decode_indexed_attn_merge(q: torch.Tensor, k_pool: torch.Tensor, v_po
     need = c_size_t(0)
     _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), n_sink + k, n_recent,
           ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_sparse_decode_indexed_attn_merge", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
           seq_lens.data_ptr(), n_sink, n_recent, sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(),
           cap, n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws), slow_out.data_ptr(),
@@ -748,7 +669,7 @@ def dense_attn_with_head_stats(q: torch.Tensor, k_pool: torch.Tensor, v_pool: to
         raise ValueError("scores must be float32 [B, Hq, score_stride]")
     need = c_size_t(0)
     _call("sfi_dense_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), 1, ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_dense_attn_with_head_stats", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), seq_lens.data_ptr(),
           n_sink, n_recent, out.data_ptr(), _ptr(lse), scores.data_ptr(), stride, _ptr(ws), _nbytes(ws),
           _stream(stream, dev))
@@ -801,7 +722,7 @@ def mixed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, bloc
     need = c_size_t(0)
     _call("sfi_mixed_attn_workspace_size", ctypes.byref(shape), ctypes.byref(kv), m, t, cap, n_recent,
           ctypes.byref(need))
-    ws = _workspace(need.value, workspace, dev)
+    ws = _workspace(need.value, workspace, dev, stream)
     _call("sfi_mixed_attn", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(), m, t, seq_lens.data_ptr(),
           n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(),
           _ptr(lse), _ptr(scores), stride, _ptr(ws), _nbytes(ws), _stream(stream, dev))

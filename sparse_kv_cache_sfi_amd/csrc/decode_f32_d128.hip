@@ -1,0 +1,10 @@
+// Split-K decode kernels for fp32 rows of head size 128.
+#include "decode_kernels.h"
+
+namespace sfi {
+
+hipError_t launch_decode_f32_d128(const AttnArgs& a, int G, bool sparse, int B, hipStream_t stream) {
+  return launch_decode_g<float, 128>(a, G, sparse, B, stream);
+}
+
+}  // namespace sfi

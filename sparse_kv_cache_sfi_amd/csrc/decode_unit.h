@@ -18,8 +18,21 @@
 // row's lanes with DPP, an online softmax in log2 units whose reference maximum is
 // only raised when a score exceeds it by more than 8 (2^8 headroom in fp32),
 // and fp32 FMA accumulation of P*V.  The split's partial (max, sum, o) per head
-// goes to the workspace, or straight to out/lse when there is one split.
+// goes to the split tail (split_tail.h), or straight to out/lse when there is one
+// split.
+//
+// The fast step's rows form a layout the host knows in full: virtual rows
+// [0, cap) are the compact slots (a slot at or past n_compact is masked) and rows
+// [cap, cap + n_recent) are the recent window, position rs + i for row cap + i with
+// rs = max(n_sink, L - n_recent) (masked at or past L).  Split boundaries therefore
+// need no device value, and a split that holds only compact rows issues its first
+// K/V loads at once, before the request's length, n_compact or any block-table entry
+// has arrived.  The index-set fast step uses the same layout with cap = n_sink + k:
+// rows [0, n_sink) are the sink positions and rows n_sink + j the j-th entry of the
+// selection, each read in place through the block table.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -93,34 +106,20 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   using S = DecodeShape<T, D, G>;
   constexpr int LPR = S::LPR, EPC = S::EPC, C = S::C, E = S::E, ROWS = S::ROWS, U = S::U;
   constexpr int WAVES = S::WAVES, TILE = S::TILE, NT = WAVES * kWave;
+  // The slow step visits rows in iteration pairs (a wave's logits of a pair are
+  // contiguous, see compute); the fast step visits them in plain tile order.
+  constexpr bool PAIRED = SCORES == 1;
+  static_assert(!INDEXED || (SPARSE && !SCORES), "the index-set path is a fast step");
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
   const int r = lane / LPR, sub = lane % LPR;
+  const bool multi = a.n_split > 1;
 
   int* bt_s = reinterpret_cast<int*>(smem);
   float* wo = reinterpret_cast<float*>(smem + kBtSlots * 4);
   float* wml = wo + WAVES * G * D;
 
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
-  static_assert(!INDEXED || (SPARSE && !SCORES), "the index-set path is a fast step");
-  int n_c = 0, rs = 0, ns = 0;
-  if constexpr (SPARSE) {
-    if constexpr (INDEXED) {
-      // Virtual rows: the sink, then every entry of the selection row (padding and
-      // entries outside [0, L) are masked rows), then the recent tokens.
-      ns = min(a.n_sink, L);
-      n_c = ns + a.sel_k;
-    } else {
-      n_c = clampi(a.n_compact[b], 0, a.cap);
-    }
-    rs = min(max(a.n_sink, L - a.n_recent), L);
-  }
-  const int n_tot = n_c + (L - rs);
-  const int t0 = split * a.split_tokens;
-  const int t1 = min(n_tot, t0 + a.split_tokens);
-
-  // This lane's slice of the G query vectors (requested before the block-table
-  // staging below, so the two loads share one memory round trip).
+  // This lane's slice of the G query vectors.
   const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)q_row0 * a.Hq + g * G) * D;
   u32x4 q[G][C];
 #pragma unroll
@@ -129,21 +128,39 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     for (int c = 0; c < C; ++c)
       q[h][c] = *reinterpret_cast<const u32x4*>(qb + h * D + (c * LPR + sub) * EPC);
 
+  // Virtual rows: [0, cap_v) compact (or sink + selection), then the recent window.
+  int cap_v = 0, t1 = 0;
+  const int t0 = split * a.split_tokens;
+  if constexpr (SPARSE) {
+    cap_v = INDEXED ? a.n_sink + a.sel_k : a.cap;
+    t1 = min(cap_v + min(a.n_recent, a.max_seq_len), t0 + a.split_tokens);
+  }
+  const bool has_recent = SPARSE && t1 > cap_v;
+  // A split of compact-buffer rows only never needs the request's length: it is not
+  // even loaded, so nothing ahead of the split's K/V loads waits for it.
+  // (A fused append always loads it: the last split stores the new row at L - 1.)
+  const bool compact_only = SPARSE && !INDEXED && !APPEND && !has_recent;
+  const int L = compact_only ? 0 : clamp_len(a.seq_lens[b], a.max_seq_len, a.max_pages);
+  if constexpr (!SPARSE) t1 = min(L, t0 + a.split_tokens);
+  const int rs = min(max(a.n_sink, L - a.n_recent), L);   // first recent position
+
   // Stage the block-table entries of this split's paged positions in LDS.  A dense
   // split stages every page of its token range that the table holds, without
-  // waiting for the request's length (entries past the end are never used).
+  // waiting for the request's length (entries past the end are never used); a fast
+  // step's split stages the pages of its recent rows.
   int pg_lo = 0, n_pg = 0;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
   if constexpr (SPARSE) {
-    const int v_first = max(t0, n_c);
-    if (t1 > v_first) {
-      pg_lo = (rs + v_first - n_c) >> 4;
-      n_pg = ((rs + t1 - 1 - n_c) >> 4) - pg_lo + 1;
+    if (has_recent) {
+      const int v_first = max(t0, cap_v);
+      const int p_first = rs + v_first - cap_v, p_last = min(rs + t1 - 1 - cap_v, L - 1);
+      pg_lo = p_first >> 4;   // (also when nothing is staged: keeps every slot index in range)
+      if (p_last >= p_first) n_pg = (p_last >> 4) - pg_lo + 1;
     }
   } else {
     pg_lo = t0 >> 4;
     n_pg = max(0, min(((t0 + a.split_tokens - 1) >> 4) - pg_lo + 1, a.max_pages - pg_lo));
   }
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
   for (int i = tid; i < n_pg; i += NT) {
     const int e = bt_row[pg_lo + i];
     bt_s[i] = (e >= 0 && e < a.num_pages) ? e : -1;
@@ -154,7 +171,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     // (sink rows are their own index, selected rows come from the selection), then
     // every block-table entry, so the staging costs two memory round trips.
     slot_s = reinterpret_cast<int*>(smem + S::IDX_OFF);
-    const int cnt = min(t1, n_c) - t0;
+    const int cnt = min(t1, cap_v) - t0;
     const int32_t* sel_row = a.sel + ((int64_t)b * a.Hkv + g) * a.sel_k;
     constexpr int PER = kMaxSplitTokens / NT;
     int pos[PER];
@@ -163,7 +180,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       const int i = tid + j * NT;
       const int vi = t0 + i;
       pos[j] = -1;
-      if (i < cnt) pos[j] = vi < ns ? vi : sel_row[vi - ns];
+      if (i < cnt) pos[j] = vi < a.n_sink ? vi : sel_row[vi - a.n_sink];
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -176,21 +193,25 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
           const int e = bt_row[pos[j] >> 4];
           if (e >= 0 && e < a.num_pages) sl = e * kPage + (pos[j] & 15);
         }
+        // a sink slot at or past the request's end is not a row of the packed buffer
+        if (t0 + i < a.n_sink && t0 + i >= L) sl = -1;
         slot_s[i] = sl;
       }
     }
     if (a.pack_n && split == 0 && g == 0 && w == 0) {
-      // n_compact of the packed buffer: ns + the entries of unit 0's selection before
-      // its first negative one (as the gather-pack counts them).
+      // n_compact of the packed buffer: min(n_sink, L) + the entries of unit 0's
+      // selection before its first negative one (as the gather-pack counts them).
       const int32_t* sel0 = a.sel + (int64_t)b * a.Hkv * a.sel_k;
       float first = (float)a.sel_k;
       for (int i = lane; i < a.sel_k; i += kWave)
         if (sel0[i] < 0) first = fminf(first, (float)i);
       first = xor_fold<1>(first, [](float x, float y) { return fminf(x, y); });
-      if (lane == 0) a.pack_n[b] = ns + (int)first;
+      if (lane == 0) a.pack_n[b] = min(a.n_sink, L) + (int)first;
     }
   }
-  __syncthreads();
+  // Only splits that read through the block table wait here; a fast-step split of
+  // compact rows goes straight to its loads.
+  if (!SPARSE || INDEXED || has_recent) __syncthreads();
 
   const T* kpool = reinterpret_cast<const T*>(a.k_pool);
   const T* vpool = reinterpret_cast<const T*>(a.v_pool);
@@ -247,22 +268,30 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     for (int e = 0; e < E; ++e) o[h][e] = 0.f;
   }
 
+  // n_compact: a compact slot at or past it is masked (read in compute only; loaded
+  // after the first K/V loads are out, see stream).
+  int n_c = 0;
+
   struct Buf {
     u32x4 k[U][C];
     u32x4 v[U][C];
   };
 
-  // Where slot u of iteration `it` comes from: its position p, whether it lies in
-  // this split (in) and whether it is backed by a compact row or a valid page (ok).
-  auto locate = [&](int it, int u, int& vi, int& p, bool& in, bool& compact, int& pg, bool& ok) {
-    // Iterations go in pairs; in pair it / 2 wave w takes the 2 U ROWS consecutive rows
-    // starting at w * 2 U ROWS of the pair's 2 TILE rows, so a wave's logits of both
-    // iterations are contiguous.
-    vi = t0 + (it >> 1) * (2 * TILE) + w * (2 * U * ROWS) + (it & 1) * (U * ROWS) + u * ROWS + r;
-    in = vi < t1;
-    compact = SPARSE && vi < n_c;
+  // Virtual row of slot u in iteration `it`.  Paired order: in pair it / 2 wave w takes
+  // the 2 U ROWS consecutive rows starting at w * 2 U ROWS of the pair's 2 TILE rows, so
+  // a wave's logits of both iterations are contiguous.  Plain order: iteration it is
+  // rows [it TILE, it TILE + TILE) of the split.
+  auto vrow = [&](int it, int u) {
+    if constexpr (PAIRED)
+      return t0 + (it >> 1) * (2 * TILE) + w * (2 * U * ROWS) + (it & 1) * (U * ROWS) + u * ROWS + r;
+    else
+      return t0 + it * TILE + w * (U * ROWS) + u * ROWS + r;
+  };
+  // Where virtual row vi lives in the pool: its position p, its page pg (-1: none) and
+  // whether a real row backs it (ok).  A compact-buffer row is handled by the callers.
+  auto paged = [&](int vi, bool in, int& p, int& pg, bool& ok) {
     if constexpr (INDEXED) {
-      if (compact) {
+      if (vi < cap_v) {
         // an index-set row: its page slot was staged (p & 15 is the row in the page)
         const int sl = in ? slot_s[vi - t0] : -1;
         p = sl;
@@ -271,35 +300,46 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
         return;
       }
     }
-    p = compact ? vi : rs + vi - n_c;
-    const int slot = in && !compact ? (p >> 4) - pg_lo : 0;
-    pg = bt_s[slot];
-    ok = in && (compact || pg >= 0);
+    // (The slot stays inside bt_s: a split spans at most kMaxSplitTokens positions.  A
+    // dense row in the split is before L; a recent row at or past L reads a stale slot and
+    // is masked.)
+    p = SPARSE ? rs + vi - cap_v : vi;
+    pg = bt_s[in ? (p >> 4) - pg_lo : 0];
+    ok = in && pg >= 0 && (!SPARSE || p < L);
   };
 
+  // The streaming loop.  CO: every row of the split is a compact-buffer row, whose
+  // address needs no device value; that loop never reads the request's length or the
+  // block table, so its loads go out at once.
+  auto stream = [&](auto co_tag) {
+  constexpr bool CO = decltype(co_tag)::value;
   // Issue the loads of one iteration.  Every lane always loads (rows outside the
   // split or behind an invalid page read row 0 of the pool and are masked), so the
   // loop carries no conditionally-loaded registers.
   auto issue = [&](int it, Buf& B) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int vi, p, pg;
-      bool in, compact, ok;
-      locate(it, u, vi, p, in, compact, pg, ok);
-      int64_t off = (int64_t)(pg < 0 ? 0 : pg) * page_elems + head_off + (int64_t)(p & 15) * D;
-      off = ok ? off : 0;
-      const T* kr = kpool + off;
-      const T* vr = vpool + off;
-      if constexpr (SPARSE && !INDEXED) {
-        if (compact) {
-          kr = ckb + (int64_t)vi * D;
-          vr = cvb + (int64_t)vi * D;
-        }
-      }
-      if constexpr (APPEND) {
-        if (ok && !compact && p == L - 1) {
-          kr = knew;
-          vr = vnew;
+      const int vi = vrow(it, u);
+      const bool in = vi < t1;
+      const T* kr;
+      const T* vr;
+      if (CO || (SPARSE && !INDEXED && vi < cap_v)) {
+        // a row past the split reads row 0 of the pool (finite data, masked)
+        kr = in ? ckb + (int64_t)vi * D : kpool;
+        vr = in ? cvb + (int64_t)vi * D : vpool;
+      } else {
+        int p, pg;
+        bool ok;
+        paged(vi, in, p, pg, ok);
+        int64_t off = (int64_t)(pg < 0 ? 0 : pg) * page_elems + head_off + (int64_t)(p & 15) * D;
+        off = ok ? off : 0;
+        kr = kpool + off;
+        vr = vpool + off;
+        if constexpr (APPEND) {
+          if (ok && (!SPARSE || vi >= cap_v) && p == L - 1) {
+            kr = knew;
+            vr = vnew;
+          }
         }
       }
 #pragma unroll
@@ -310,19 +350,36 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   };
 
-  auto compute = [&](int it, const Buf& B) {
+  auto compute = [&](int it, Buf& B) {
     bool in_[U], ok_[U];
     int pos_[U];
+    // Compact slots in [n_compact, cap) were loaded without knowing n_compact and may
+    // hold anything; a split that has such slots zeroes their V (0 * NaN would poison
+    // the sums).  The test is uniform, so full compact buffers skip it.
+    const bool scrub = SPARSE && !INDEXED && n_c < min(t1, cap_v);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int vi, pg;
-      bool compact;
-      locate(it, u, vi, pos_[u], in_[u], compact, pg, ok_[u]);
+      const int vi = vrow(it, u);
+      in_[u] = vi < t1;
+      if (CO || (SPARSE && !INDEXED && vi < cap_v)) {
+        pos_[u] = vi;
+        ok_[u] = in_[u] && vi < n_c;
+        if (scrub && !ok_[u]) {
+#pragma unroll
+          for (int c = 0; c < C; ++c) B.v[u][c] = u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        int pg;
+        paged(vi, in_[u], pos_[u], pg, ok_[u]);
+      }
       if constexpr (INDEXED) {
         // Pack while attending: the row just loaded goes to its compact slot vi
         // (zeros for a masked position, nothing for padding).
+        // (The gather-pack puts selection entry j at slot min(n_sink, L) + j.)
+        const bool compact = vi < cap_v;
         if (a.pack_k && in_[u] && compact && pos_[u] != -1) {
-          const int64_t dst = (((int64_t)b * a.Hkv + g) * a.pack_cap + vi) * D;
+          const int dslot = vi < a.n_sink ? vi : min(a.n_sink, L) + vi - a.n_sink;
+          const int64_t dst = (((int64_t)b * a.Hkv + g) * a.pack_cap + dslot) * D;
           T* dk = reinterpret_cast<T*>(a.pack_k) + dst;
           T* dv = reinterpret_cast<T*>(a.pack_v) + dst;
           const bool real = pos_[u] >= 0;
@@ -439,7 +496,8 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     }
   };
 
-  // Two-deep software pipeline; the prefetches are unconditional (see issue()).
+  // Two-deep software pipeline; the prefetches are unconditional (see issue()).  In
+  // plain order an iteration past the split's last is empty and is not computed.
   const int n_it = (t1 > t0) ? (t1 - t0 + TILE - 1) / TILE : 0;
   Buf A, Bb;
   if (n_it > 0) {
@@ -448,6 +506,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
     // forces copies that wait on the loads) and all of a refill's loads ahead of
     // the computation they overlap.
     issue(0, A);
+    if constexpr (SPARSE && !INDEXED) n_c = clampi(a.n_compact[b], 0, a.cap);
     for (int it = 0; it < n_it; it += 2) {
       issue(it + 1, Bb);
       __builtin_amdgcn_sched_barrier(0);
@@ -455,9 +514,18 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       __builtin_amdgcn_sched_barrier(0);
       issue(it + 2, A);
       __builtin_amdgcn_sched_barrier(0);
-      compute(it + 1, Bb);
+      if (PAIRED || it + 1 < n_it) compute(it + 1, Bb);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  };
+  if constexpr (SPARSE && !INDEXED) {
+    if (compact_only)
+      stream(std::true_type{});
+    else
+      stream(std::false_type{});
+  } else {
+    stream(std::false_type{});
   }
 
   if constexpr (SCORES) {
@@ -514,18 +582,16 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
       os = fmaf(al, wo[(x * G + h) * D + e], os);
     }
     const int64_t orow = SplitTail<D>::row(a, q_row0, g, G, h);
-    if (a.n_split == 1) {
+    if (!multi) {
       a.out[orow * D + e] = ls > 0.f ? os / ls : 0.f;
       if (e == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M + log2f(ls)) * kLn2 : neg_inf();
     } else {
       const int64_t prow = orow * a.part_stride + split;
       store_coherent(a.part_o + prow * D + e, os);
-      if (e == 0) {
-        store_coherent2(a.part_ml + prow * 2, M, ls);
-      }
+      if (e == 0) store_coherent2(a.part_ml + prow * 2, M, ls);
     }
   }
-  if (a.n_split > 1 && !DEFER)
+  if (multi && !DEFER)
     SplitTail<D>::run(a, b, g, q_row0, G, G, kMaxSplits, reinterpret_cast<int*>(wml + WAVES * G * 2),
                       wml + WAVES * G * 2 + 4);
 }

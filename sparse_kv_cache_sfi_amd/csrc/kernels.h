@@ -100,29 +100,6 @@ struct MixedPlan {
   int32_t split_tokens[kMaxMixedBatch];
 };
 
-// Largest k a maintenance rider keeps in LDS (its selection feeds its pack).
-constexpr int kMaxRiderK = 8192;
-
-// Slow-step maintenance of layer i carried by a layer-(i+1) attention launch: one
-// rider work-group per (request, KV head) row selects the top-k of that row's
-// logits and packs the row's compact buffer.  The rows share the launch's seq_lens.
-struct RefreshArgs {
-  const float* scores;    // [B, Hkv, score_stride] layer i's masked logits
-  int64_t score_stride;
-  const void* k_pool;     // layer i's paged pools and block table
-  const void* v_pool;
-  const int32_t* block_table;
-  int32_t max_pages, num_pages, max_seq_len, Hkv;
-  const int32_t* seq_lens;
-  int32_t n_sink, n_recent, k;
-  int32_t* sel;           // [B, Hkv, k]
-  void* ck;               // [B, Hkv, cap, d]
-  void* cv;
-  int32_t cap;
-  int32_t* n_compact;     // [B]
-  int32_t rows;           // riders: B * Hkv
-};
-
 // Launchers.  Each returns hipGetLastError() after enqueueing.
 hipError_t launch_decode(const AttnArgs& a, int dtype, int d, int G, bool sparse, int B,
                          hipStream_t stream);
@@ -142,8 +119,6 @@ struct PackArgs;
 // compact buffer described by p and, with merge non-NULL, merges a deferred slow step.
 hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int dtype, int d, int G,
                             int B, hipStream_t stream);
-hipError_t launch_dense_refresh(const AttnArgs& a, const RefreshArgs& r, int dtype, int d, int G, int B,
-                                hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace sfi

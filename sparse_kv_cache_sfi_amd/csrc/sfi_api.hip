@@ -3,6 +3,7 @@
 // a rejected call launches nothing and touches no output.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <climits>
@@ -97,20 +98,28 @@ sfi_status check_budgets(int32_t n_sink, int32_t n_recent) {
 }
 
 // Split-K plan: about one work-group per CU (256), but splits of at least
-// 256 tokens (512 once a unit has 8192 or more: the merge of many splits costs more
-// than the parallelism gains), at most kMaxSplitTokens, at most max_splits splits,
-// rounded to the kernel's tile.
+// min_split tokens, at most kMaxSplitTokens, at most max_splits splits, rounded to
+// the kernel's tile.  SFI_TUNE_MIN_SPLIT and SFI_TUNE_TARGET_WGS (environment, read
+// on every call) override the two targets for tuning sweeps; results stay correct
+// for any value.
 struct Split {
   int tokens;
   int n;
 };
 
-Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::kMaxSplits) {
-  constexpr int64_t kTargetWGs = 256;
+int64_t tune_env(const char* name, int64_t fallback) {
+  const char* v = getenv(name);
+  if (!v || !*v) return fallback;
+  const long long x = atoll(v);
+  return x > 0 ? x : fallback;
+}
+
+Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int max_splits = sfi::kMaxSplits) {
+  const int64_t target = tune_env("SFI_TUNE_TARGET_WGS", 256);
+  min_split = tune_env("SFI_TUNE_MIN_SPLIT", min_split);
   if (n_tok <= 0) return {tile, 1};
-  const int64_t min_split = n_tok >= 8192 ? 512 : 256;
   const int64_t by_min = (n_tok + min_split - 1) / min_split;
-  const int64_t want = (kTargetWGs + units - 1) / units;
+  const int64_t want = (target + units - 1) / units;
   int64_t ns = by_min < want ? by_min : want;
   if (ns > max_splits) ns = max_splits;
   if (ns < 1) ns = 1;
@@ -120,6 +129,15 @@ Split plan_split(int64_t units, int64_t n_tok, int tile, int max_splits = sfi::k
   ns = (n_tok + st - 1) / st;
   return {(int)st, (int)ns};
 }
+
+// Dense splits: 256 tokens, 512 once a unit has 8192 or more (the merge of many
+// splits costs more than the parallelism gains).
+int64_t dense_min_split(int64_t n_tok) { return n_tok >= 8192 ? 512 : 256; }
+// Fast-step splits: 128 tokens, so that at small batches the step spreads over many
+// CUs (a CU streams only some tens of GB/s), but a unit of at most 320 tokens stays one
+// split: below that the split-K tail (partial stores drained, arrival ticket, merge)
+// costs more than the shorter stream saves.
+int64_t sparse_min_split(int64_t n_tok) { return n_tok <= 320 ? n_tok : 128; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -134,13 +152,16 @@ size_t partial_bytes(int64_t rows, int n_split, int d) {
 
 Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
   if (t_q > 1)
-    return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
-  return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kDecodeTile);
+    return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kVerifyTile,
+                      dense_min_split(kv->max_seq_len), sfi::kMaxVerifySplits);
+  return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kDecodeTile,
+                    dense_min_split(kv->max_seq_len));
 }
 
 Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  return plan_split((int64_t)s->batch * s->num_kv_heads, (int64_t)cap + rec, sfi::kDecodeTile);
+  const int64_t n_tok = (int64_t)cap + rec;
+  return plan_split((int64_t)s->batch * s->num_kv_heads, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
 }
 
 sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_t* seq_lens) {
@@ -222,8 +243,10 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
   }
   const int64_t units = (int64_t)B * shape->num_kv_heads;
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
-  const Split sp_d = plan_split(units, (int64_t)cap + rec, sfi::kDecodeTile);
-  const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, sfi::kMaxVerifySplits);
+  const int64_t n_tok = (int64_t)cap + rec;
+  const Split sp_d = plan_split(units, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
+  const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, dense_min_split(kv->max_seq_len),
+                                sfi::kMaxVerifySplits);
   sfi::MixedPlan& p = ms->plan;
   p = sfi::MixedPlan{};
   int q_row0[sfi::kMaxMixedBatch];
@@ -381,87 +404,6 @@ sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const sfi_page
                     workspace_bytes, stream);
 }
 
-sfi_status sfi_dense_attn_with_refresh(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
-                                       const int32_t* seq_lens, int32_t n_sink, int32_t n_recent, float* out,
-                                       float* lse, float* scores, int64_t score_stride, const sfi_refresh* refresh,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
-  SFI_TRY(check_shape(shape));
-  SFI_TRY(check_kv(kv));
-  SFI_TRY(check_ptr16(q, "q"));
-  SFI_TRY(check_ptr16(out, "out"));
-  if (!seq_lens) return fail(SFI_ERR_INVALID_ARG, "seq_lens is NULL");
-  SFI_TRY(check_budgets(n_sink, n_recent));
-  if (scores && score_stride < kv->max_seq_len)
-    return fail(SFI_ERR_INVALID_ARG, "score_stride (%lld) must be >= max_seq_len (%d)", (long long)score_stride,
-                kv->max_seq_len);
-  if (!refresh) return fail(SFI_ERR_INVALID_ARG, "refresh is NULL");
-  SFI_TRY(check_kv(&refresh->kv));
-  if (!refresh->scores || !refresh->sel_idx)
-    return fail(SFI_ERR_INVALID_ARG, "refresh scores and sel_idx must be non-NULL");
-  if (refresh->scores == scores) return fail(SFI_ERR_INVALID_ARG, "refresh scores must not be the launch's own scores");
-  const bool pack = refresh->compact_k != nullptr;
-  if (pack) {
-    SFI_TRY(check_ptr16(refresh->compact_k, "refresh compact_k"));
-    SFI_TRY(check_ptr16(refresh->compact_v, "refresh compact_v"));
-    if (!refresh->n_compact) return fail(SFI_ERR_INVALID_ARG, "refresh n_compact must be non-NULL when packing");
-  }
-  SFI_TRY(check_budgets(refresh->n_sink, refresh->n_recent));
-  if (refresh->score_stride < refresh->kv.max_seq_len || refresh->score_stride > INT32_MAX)
-    return fail(SFI_ERR_INVALID_ARG, "refresh score_stride (%lld) must be in [kv.max_seq_len, 2^31)",
-                (long long)refresh->score_stride);
-  if (refresh->k < 1 || refresh->k > sfi::kMaxRiderK)
-    return fail(SFI_ERR_UNSUPPORTED, "refresh k must be in [1, %d] (got %d)", sfi::kMaxRiderK, refresh->k);
-  if (pack && (int64_t)refresh->cap < (int64_t)refresh->n_sink + refresh->k)
-    return fail(SFI_ERR_INVALID_ARG, "refresh cap (%d) must be >= n_sink + k (%lld)", refresh->cap,
-                (long long)refresh->n_sink + refresh->k);
-  if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
-    return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  const Split sp = plan_dense(shape, kv, 1);
-  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
-  SFI_TRY(check_unit_span(shape, 1, sp.n));
-  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
-  if ((int64_t)shape->batch * shape->num_kv_heads * (1 + sp.n) > INT32_MAX)
-    return fail(SFI_ERR_UNSUPPORTED, "grid too large");
-
-  sfi::AttnArgs a = base_args(shape, kv, seq_lens);
-  a.q = q;
-  a.n_sink = n_sink;
-  a.n_recent = n_recent;
-  a.split_tokens = sp.tokens;
-  a.n_split = sp.n;
-  a.t_q = 1;
-  a.out = out;
-  a.lse = lse;
-  a.scores = scores;
-  a.score_stride = score_stride;
-  set_partials(a, workspace, rows, shape->head_dim);
-
-  sfi::RefreshArgs r{};
-  r.scores = refresh->scores;
-  r.score_stride = refresh->score_stride;
-  r.k_pool = refresh->kv.k;
-  r.v_pool = refresh->kv.v;
-  r.block_table = refresh->kv.block_table;
-  r.max_pages = refresh->kv.max_pages;
-  r.num_pages = refresh->kv.num_pages;
-  r.max_seq_len = refresh->kv.max_seq_len;
-  r.Hkv = shape->num_kv_heads;
-  r.seq_lens = seq_lens;
-  r.n_sink = refresh->n_sink;
-  r.n_recent = refresh->n_recent;
-  r.k = refresh->k;
-  r.sel = refresh->sel_idx;
-  r.ck = pack ? refresh->compact_k : nullptr;
-  r.cv = pack ? refresh->compact_v : nullptr;
-  r.cap = refresh->cap;
-  r.n_compact = refresh->n_compact;
-  r.rows = shape->batch * shape->num_kv_heads;
-  const hipError_t e = sfi::launch_dense_refresh(a, r, shape->dtype, shape->head_dim, G, shape->batch,
-                                                 static_cast<hipStream_t>(stream));
-  return hip_status(e, "attention + refresh launch");
-}
-
 sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t k,
                                           size_t* bytes) {
   if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
@@ -563,7 +505,8 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
     SFI_TRY(check_ptr16(compact_v, "compact_v"));
     if (!n_compact) return fail(SFI_ERR_INVALID_ARG, "n_compact is NULL");
   }
-  if (cap < 1) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1");
+  // An index-set step may have no sink and no selection (cap 0: the recent window alone).
+  if (cap < (sel_k >= 0 ? 0 : 1)) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1");
   if ((int64_t)cap + n_recent > kMaxTokens)
     return fail(SFI_ERR_UNSUPPORTED, "cap + n_recent exceeds %lld tokens", (long long)kMaxTokens);
   if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for n in ("sfi_dense_attn_with_stats", "sfi_select_topk", "sfi_pack_compact", "sfi_sparse_decode_attn",
-              "sfi_mixed_attn", "sfi_dense_attn_with_refresh", "sfi_sparse_decode_append_attn",
+              "sfi_mixed_attn", "sfi_sparse_decode_append_attn",
               "sfi_sparse_decode_indexed_attn", "sfi_dense_attn_with_head_stats"):
         assert n in names
 
@@ -38,6 +38,12 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_symbols():
         assert hasattr(lib, n), n
+
+
+def test_in_launch_maintenance_entry_point_is_gone(lib):
+    # the slow step that carried the previous layer's Selector and pack as extra
+    # work-groups measured slower than running them serially; it was removed
+    assert not hasattr(lib, "sfi_dense_attn_with_refresh")
 
 
 def test_version_and_status_strings(lib):
@@ -126,30 +132,6 @@ def test_pack_rejects_bad_arguments(lib):
     assert call(sel=0) == 1
     assert call(k=0) == 1
     assert call(n_sink=-1) == 1
-
-
-def test_refresh_rejects_bad_arguments(lib):
-    shape, kv = _shape(), _kv()
-
-    def call(refresh=True, scores=FAKE + 0x100, **kw):
-        r = dict(kv=_kv(), scores=FAKE, score_stride=16384, n_sink=4, n_recent=64, k=1980, sel_idx=FAKE,
-                 compact_k=FAKE, compact_v=FAKE, cap=1984, n_compact=FAKE)
-        r.update(kw)
-        ref = sfi.SfiRefresh(**r)
-        return lib.sfi_dense_attn_with_refresh(ctypes.byref(shape), ctypes.byref(kv), FAKE, FAKE, 4, 64, FAKE, FAKE,
-                                               scores, 16384, ctypes.byref(ref) if refresh else None, FAKE, 1 << 40,
-                                               None)
-    assert call(refresh=False) == 1 and "refresh is NULL" in lib.sfi_last_error().decode()
-    assert call(scores=FAKE) == 1 and "must not be" in lib.sfi_last_error().decode()
-    assert call(k=8193) == 2 and "8192" in lib.sfi_last_error().decode()
-    assert call(k=0) == 2
-    assert call(cap=100) == 1 and "cap" in lib.sfi_last_error().decode()
-    assert call(sel_idx=0) == 1
-    assert call(n_compact=0) == 1
-    assert call(compact_k=MISALIGNED) == 1
-    assert call(score_stride=100) == 1 and "score_stride" in lib.sfi_last_error().decode()
-    assert call(n_recent=-1) == 1
-    assert call(kv=_kv(page=8)) == 2
 
 
 def test_sparse_rejects_bad_arguments(lib):
@@ -246,9 +228,15 @@ def test_split_plan_of_the_16k_decode_layer():
     # 1 request x 8 KV heads x 16384 tokens: 32 splits of 512 tokens -> 256 work-groups.
     assert sfi.plan_splits(0, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384) == (512, 32)
-    # fast step, 1.6 % retention: 192 compact slots + 64 recent -> a single split
+    # fast step, 1.6 % retention: 192 compact slots + 64 recent -> one split (no split-K tail)
     assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=192, n_recent=64) == (256, 1)
+    # 12.5 %: 1984 compact slots + 64 recent -> 16 splits of 128 tokens, 128 work-groups
+    assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=1984, n_recent=64) == (128, 16)
+    # batch 16: 128 units of two splits fill the 256 CUs
+    assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=1984, n_recent=64) == (1024, 2)
 
 
 def test_binding_refuses_host_tensors():

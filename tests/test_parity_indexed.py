@@ -123,6 +123,17 @@ def test_indexed_with_zero_k_is_sink_plus_recent(gpu_lib):
     _check_vs_oracle(c, out, lse, sels, L)
 
 
+def test_indexed_recent_window_alone(gpu_lib):
+    # no sink and no selection (cap 0): the fast step attends the recent window only
+    c = make_case(308, name="ix_h", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", seq_lens=[900, 20], n_sink=0,
+                  n_recent=32, k_sel=8)
+    dc = DevCase(c)
+    sels = [np.zeros((2, 0), np.int32)] * 2
+    L = c.seq_lens.astype(np.int32)
+    out, lse = _indexed(gpu_lib, c, dc, sels, L)
+    _check_vs_oracle(c, out, lse, sels, L)
+
+
 def test_indexed_with_append_stores_and_attends_the_new_token(gpu_lib):
     c = make_case(308, name="ix_h", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[1000, 2500],
                   capacity=[1010, 2510], n_sink=4, n_recent=64, k_sel=128)
