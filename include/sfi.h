@@ -228,6 +228,32 @@ SFI_API sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, cons
                                             int32_t cap, int32_t n_recent, size_t* bytes);
 
 /*
+ * The fast step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * sfi_sparse_decode_attn, with the same kernels and the same results bit for bit,
+ * but its split-K scratch is a library-owned static device array of
+ * sfi_static_scratch_bytes() bytes (8 MiB) on each GPU instead of a workspace
+ * argument.  The call allocates nothing, neither through HIP nor otherwise.
+ *
+ *  - The first call on a device looks up that device's copy of the array and
+ *    enqueues one small kernel on `stream` that zeroes its arrival counters; every
+ *    call leaves them at zero again.  The array lives until the process ends.
+ *  - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *    contents: calls that may overlap on one GPU (other streams, other threads)
+ *    race and must be ordered by the caller.
+ *  - Errors: as sfi_sparse_decode_attn; SFI_ERR_WORKSPACE, before anything touches
+ *    the device, when the call's split-K scratch (the size
+ *    sfi_sparse_decode_workspace_size reports) exceeds the array.
+ */
+SFI_API sfi_status sfi_sparse_decode_attn_static(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                         const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                         const void* compact_k, const void* compact_v, int32_t cap,
+                                         const int32_t* n_compact, float* out, float* lse, void* stream);
+
+/* Bytes of the static scratch sfi_sparse_decode_attn_static uses on each device. */
+SFI_API size_t sfi_static_scratch_bytes(void);
+
+/*
  * Fast step with KV append: the token being decoded (position seq_lens[b] - 1)
  * has its K/V in k_new / v_new [B, Hkv, d] (pool dtype, 16-byte aligned).  The
  * launch stores them into that position's page of kv.k / kv.v (which must be

@@ -26,7 +26,7 @@ __all__ = [
     "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats",
     "select_topk", "pack_compact", "dense_attn_with_stats_deferred", "pack_compact_merge",
     "sparse_decode_indexed_attn_merge",
-    "sparse_decode_attn", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
+    "sparse_decode_attn", "sparse_decode_attn_static", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
 ]
 
@@ -73,6 +73,9 @@ _SIGS = {
     "sfi_sparse_decode_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_sparse_decode_workspace_size": [_SHAPE_P, _KV_P, c_int32, c_int32, POINTER(c_size_t)],
+    "sfi_sparse_decode_attn_static": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                      c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
+    "sfi_static_scratch_bytes": [],
     "sfi_sparse_decode_append_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p],
@@ -92,7 +95,7 @@ _SIGS = {
     "sfi_last_error": [],
     "sfi_version": [],
 }
-_RES = {"sfi_status_string": c_char_p, "sfi_last_error": c_char_p}
+_RES = {"sfi_status_string": c_char_p, "sfi_last_error": c_char_p, "sfi_static_scratch_bytes": c_size_t}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -459,11 +462,14 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
                        n_compact: torch.Tensor, *, n_sink: int, n_recent: int, max_seq_len: int,
                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-                       k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None):
+                       k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                       _static: bool = False):
     """Fast step: q [B, Hq, d] -> (out [B, Hq, d] fp32, lse [B, Hq]).  With k_new / v_new
     [B, Hkv, d] (the decoded token's K/V) the launch also stores them into the pools at
     position seq_lens[b] - 1 (sfi_sparse_decode_append_attn)."""
     _dev(q, "q")
+    if _static and (workspace is not None or k_new is not None):
+        raise ValueError("the static-scratch fast step takes no workspace and no appended token")
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
     if k_new is not None:
@@ -495,6 +501,11 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if _static:
+        _call("sfi_sparse_decode_attn_static", ctypes.byref(shape), ctypes.byref(kv), q.data_ptr(),
+              seq_lens.data_ptr(), n_sink, n_recent, compact_k.data_ptr(), compact_v.data_ptr(), cap,
+              n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _stream(stream, dev))
+        return out, lse
     need = c_size_t(0)
     _call("sfi_sparse_decode_workspace_size", ctypes.byref(shape), ctypes.byref(kv), cap, n_recent,
           ctypes.byref(need))
@@ -509,6 +520,18 @@ def sparse_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
               compact_v.data_ptr(), cap, n_compact.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(ws), _nbytes(ws),
               _stream(stream, dev))
     return out, lse
+
+
+def sparse_decode_attn_static(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor, compact_k: torch.Tensor,
+                              compact_v: torch.Tensor, n_compact: torch.Tensor, *, n_sink: int, n_recent: int,
+                              max_seq_len: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, stream=None):
+    """The fast step for callers that cannot allocate (sfi_sparse_decode_attn_static): its split-K
+    scratch is the library's static device array; pass out (and lse) to allocate nothing here either."""
+    return sparse_decode_attn(q, k_pool, v_pool, block_table, seq_lens, compact_k, compact_v, n_compact,
+                              n_sink=n_sink, n_recent=n_recent, max_seq_len=max_seq_len, scale=scale, out=out,
+                              lse=lse, stream=stream, _static=True)
 
 
 def sparse_decode_indexed_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "sfi.h"
@@ -734,5 +735,79 @@ const char* sfi_status_string(sfi_status status) {
 const char* sfi_last_error(void) { return g_last_error.c_str(); }
 
 int32_t sfi_version(void) { return SFI_VERSION; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------- no-allocation fast step
+// The fast step's split-K scratch (arrival counters, then partials) in a file-scope
+// device array instead of a caller workspace, for callers that cannot allocate.  Each
+// GPU the library runs on holds its own copy until the process ends; host code uses
+// the per-device address that hipGetSymbolAddress reports, never the array's name.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+StaticScratch g_static;
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+// The current device's scratch.  On the first call on a device: look up its address
+// (that device current) and zero its counter region with a fill kernel on `stream`
+// (the counters must start at zero; every call leaves them at zero again).
+sfi_status static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SFI_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_static.mu);
+  if (!g_static.ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    const int64_t words = (int64_t)(sfi::kCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "scratch clear launch");
+    g_static.ptr[dev] = p;
+  }
+  *out = g_static.ptr[dev];
+  return SFI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sfi_status sfi_sparse_decode_attn_static(const sfi_shape* shape, const sfi_paged_kv* kv, const void* q,
+                                         const int32_t* seq_lens, int32_t n_sink, int32_t n_recent,
+                                         const void* compact_k, const void* compact_v, int32_t cap,
+                                         const int32_t* n_compact, float* out, float* lse, void* stream) {
+  // The size check runs before any device call.
+  SFI_TRY(check_shape(shape));
+  SFI_TRY(check_kv(kv));
+  if (cap < 1 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1 and n_recent >= 0");
+  const Split sp = plan_sparse(shape, cap, n_recent, kv);
+  const size_t need = partial_bytes((int64_t)shape->batch * shape->num_q_heads, sp.n, shape->head_dim);
+  if (need > kStaticScratchBytes)
+    return fail(SFI_ERR_WORKSPACE, "this call needs %zu bytes of split-K scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) SFI_TRY(static_scratch(static_cast<hipStream_t>(stream), &ws));
+  return sparse_call(shape, kv, q, nullptr, nullptr, seq_lens, n_sink, n_recent, compact_k, compact_v, cap,
+                     n_compact, nullptr, -1, false, out, lse, ws, need > 0 ? kStaticScratchBytes : 0, stream);
+}
+
+size_t sfi_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 }  // extern "C"

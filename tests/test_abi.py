@@ -288,3 +288,15 @@ def test_indexed_fast_step_with_pack_and_combine_rejects_bad_arguments(lib):
     assert call(slow_bytes=10) == 3
     assert call(ws=WS + 64) == 1 and "overlap" in lib.sfi_last_error().decode()
     assert call(shape_=_shape(d=96)) == 2
+
+
+def test_static_scratch_fast_step_rejects_calls_beyond_its_scratch(lib, monkeypatch):
+    # Many splits (tuning override of the work-group target) need more split-K scratch
+    # than the static array holds: rejected on the host, before any device call.
+    monkeypatch.setenv("SFI_TUNE_TARGET_WGS", "1000000")
+    shape = sfi.SfiShape(8, 64, 8, 128, sfi.SFI_BF16, 0.088)
+    kv = _kv()
+    st = lib.sfi_sparse_decode_attn_static(ctypes.byref(shape), ctypes.byref(kv), FAKE, FAKE, 4, 64, FAKE, FAKE,
+                                           16380, FAKE, FAKE, FAKE, None)
+    assert st == sfi.SFI_ERR_WORKSPACE and "static scratch" in lib.sfi_last_error().decode()
+    assert lib.sfi_static_scratch_bytes() == 8 << 20
