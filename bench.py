@@ -1,31 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the SFI decode-attention path on one MI355X.
 
-Workload (the layer the headline metric is quoted on): a Qwen3-0.6B-shaped
-decode layer in bf16 - batch 1, 16 query heads on 8 KV heads, head_dim 128,
-KV length 16384, page size 16, sink 4, recent 64.  One step is one pass of the
-whole t_q = 1 path on one batch:
+Headline (the metric's own quantity): the FAST STEP - sparse decode attention over
+sink + selected (compact buffer) + recent (paged, in place) - of a Qwen3-0.6B-shaped
+decode layer in bf16: batch 1, 16 query / 8 KV heads, head_dim 128, KV length 16384,
+page 16, sink 4, recent 64, 12.5 % retention (1980 selected tokens per KV head).
 
-    slow step   dense attention + masked group logits
-    Selector    top-k per KV head, k = 1980 (12.5 % retention)
-    pack        gather-pack sink + selected into the compact buffer
-    fast step   sparse attention over compact + recent
+    value          = algorithmic K/V bytes of one fast step / its kernel time  [GB/s]
+    speedup        = dense attention (same shape, no logits) time / fast-step time
+    roofline       = that fast-step kernel against the 8 TB/s HBM peak
+    pct_measured_read = value against this GPU's streaming read rate (sfi_stream_read)
 
-Within one layer these four calls depend on each other in order, so the step
-runs them on one stream (an auxiliary stream only pays off when the Selector and
-pack of layer i overlap the attention of layer i+1; pass --aux-stream to run
-them on a second stream anyway).
+Every timed loop rotates over replicas whose distinct bytes total >= 512 MiB (twice
+the 256 MB Infinity Cache): each replica has its own compact buffers, its own block
+table (a random page permutation, so its recent window sits on other pages) and one of
+several K/V pools, so no launch re-reads what a recent launch left in a cache.  The
+bytes rotated are reported with every figure.
 
-`value` = algorithmic KV bytes of the step (dense K/V read, pack read + write,
-fast-step K/V read) / step time.  Inputs are resident in HBM before timing;
-every step uses another of R replicas so the working set (>= 512 MiB) exceeds
-the 256 MB Infinity Cache.
+A step (what --steps K / --warmup W count and ms_per_step times) is one pass of the
+whole decode path on one batch: slow step (dense attention + masked group logits,
+split-K combine deferred) -> Selector (top-1980 per KV head) -> one launch with the
+fast step over the selection read in place, the gather-pack of the compact buffer and
+the slow step's combine.  Inputs are resident in HBM before timing.
 
-Also reported (same process, outside the timed steps): the retention sweep of
-the fast step against dense attention at 16K (batch 1 and batch 16), the dense
-kernel's HBM roofline fraction, and the fp64 oracle's throughput on host cores.
+Also reported: the retention sweep (SFI page, Table 1: 1.6 % ... 100 %) at batch 1 and
+16 and at 32K-128K, the slow step, the Selector, the two-stream maintenance schedules
+at 64K, the 128K draft/verify mix, the next rows, and the fp64 oracle's rate on the host
+CPU (one thread and every core).
 """
 import argparse
+import hashlib
 import json
 import os
 import re
@@ -39,16 +43,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode-attn effective KV GB/s (% HBM peak) + speedup vs dense at 16K"
-
+MIN_ROTATE = 512 << 20          # distinct bytes every timed loop cycles through
 
 DECODE_SOURCES = ["sparse_kv_cache_sfi_amd/csrc/decode_unit.h", "sparse_kv_cache_sfi_amd/csrc/split_tail.h",
-                  "sparse_kv_cache_sfi_amd/csrc/decode.hip", "sparse_kv_cache_sfi_amd/csrc/common.h"]
-TRAFFIC_PROFILE = "profiles/decode_layer_16k_b1_hbm_bytes.txt"
-DENSE_KERNEL = "decode_kernel<unsigned short, 128, 2, false, 1, false, false, true>"
+                  "sparse_kv_cache_sfi_amd/csrc/decode_kernels.h", "sparse_kv_cache_sfi_amd/csrc/common.h",
+                  "sparse_kv_cache_sfi_amd/csrc/kernels.h"]
+TRAFFIC_PROFILE = "profiles/fast_step_16k_b1_hbm_bytes.txt"
+FAST_KERNEL = "decode_kernel<unsigned short, 128, 2, true, 0, false, false, false>"
 
 
 def decode_source_hash():
-    import hashlib
     h = hashlib.sha1()
     for f in DECODE_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
@@ -56,10 +60,10 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def profiled_traffic():
-    """HBM bytes per launch of the slow-step kernel from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, each scaled by what a plain copy of known size reads back),
-    or None when the summary is absent or was taken on other kernel sources."""
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what a plain copy of known size reads back), or None when the
+    summary is absent or was taken on other kernel sources."""
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if not os.path.exists(path):
         return None, "no counter summary"
@@ -68,7 +72,7 @@ def profiled_traffic():
     if not m or m.group(1) != decode_source_hash():
         return None, "kernel changed since the counters were taken"
     for line in text.splitlines():
-        if DENSE_KERNEL in line:
+        if line.startswith(kernel):
             read_mib, write_mib = (float(x) for x in line.split()[-2:])
             return int(round((read_mib + write_mib) * 2 ** 20)), TRAFFIC_PROFILE
     return None, "kernel not in counter summary"
@@ -79,29 +83,14 @@ def log(msg):
 
 
 def upload(a, dev):
-    import numpy as np
     import torch
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def make_layers(n, L, B, frac, dev, seed0):
-    from sfi_synth import qwen06b_decode_case
-    out = []
-    for r in range(n):
-        c = qwen06b_decode_case(seed0 + r, L=L, B=B, frac=frac)
-        out.append(dict(case=c, k=upload(c.kv.k, dev), v=upload(c.kv.v, dev), bt=upload(c.kv.block_table, dev),
-                        lens=upload(c.seq_lens.astype("int32"), dev), q=upload(c.q, dev),
-                        q1=upload(c.q[:, 0], dev)))
-    return out
-
-
-def kv_bytes_dense(B, Hkv, L, d, esize=2):
-    return B * Hkv * L * 2 * d * esize
-
-
 def time_loop(fn, n, stream):
+    """Seconds per call of fn(i), i = 0..n-1, between HIP events on `stream`."""
     import torch
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
@@ -109,361 +98,19 @@ def time_loop(fn, n, stream):
         fn(i)
     e.record(stream)
     e.synchronize()
-    return s.elapsed_time(e) / n * 1e-3   # seconds per call
+    return s.elapsed_time(e) / n * 1e-3
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--aux-stream", action="store_true")
-    ap.add_argument("--specmix-only", action="store_true",
-                    help="run only the 128K draft/verify mix (for counter collection) and print its figures")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
-    ap.add_argument("--only", default="",
-                    help="comma-separated legs to run alone, printing their figures: append_fast, draft_refresh, "
-                         "head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-    import sparse_kv_cache_sfi_amd as sfi
-
-    sfi.load()
-    dev = torch.device("cuda:0")
-    if args.specmix_only:
-        print(json.dumps({"specmix_128k": specmix(sfi, dev)}), flush=True)
-        return
-    if args.only:
-        legs = {"append_fast": lambda: append_fast(sfi, dev, torch.cuda.current_stream(dev)),
-                "draft_refresh": lambda: draft_refresh_c3(sfi, dev),
-                "head_selection": lambda: head_selection(sfi, dev),
-                "refresh_schedule": lambda: refresh_schedule_c3(sfi, dev),
-                "refresh_64k_overlap": lambda: refresh_overlap(sfi, dev),
-                "specmix_128k": lambda: specmix(sfi, dev)}
-        names = [n for n in args.only.split(",") if n]
-        unknown = [n for n in names if n not in legs]
-        if unknown:
-            print(f"unknown legs {unknown}; known: {sorted(legs)}", file=sys.stderr)
-            sys.exit(2)
-        print(json.dumps({n: legs[n]() for n in names}), flush=True)
-        return
-    L, B, Hq, Hkv, d = 16384, 1, 16, 8, 128
-    n_sink, n_recent = 4, 64
-    frac = (1, 8)
-    R = args.replicas
-    log(f"generating {R} replicas of the 16K layer")
-    layers = make_layers(R, L, B, frac, dev, 1000)
-    c0 = layers[0]["case"]
-    k_sel = c0.k_sel
-    cap = n_sink + k_sel
-    max_len = L
-    main_s = torch.cuda.current_stream(dev)
-    aux_s = torch.cuda.Stream(device=dev) if args.aux_stream else main_s
-
-    # per-replica outputs and buffers, all allocated before timing
-    for ly in layers:
-        ly["out"] = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
-        ly["lse"] = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
-        ly["scores"] = torch.empty((B, Hkv, max_len), dtype=torch.float32, device=dev)
-        ly["sel"] = torch.empty((B, Hkv, k_sel), dtype=torch.int32, device=dev)
-        ly["ck"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
-        ly["cv"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
-        ly["nc"] = torch.empty((B,), dtype=torch.int32, device=dev)
-        ly["fout"] = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-        ly["flse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ex = layers[0]
-    ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
-                                              dtype=torch.bfloat16, max_seq_len=max_len) + 16,
-                           dtype=torch.uint8, device=dev)
-    ws_sparse = torch.zeros(sfi.workspace_size("sparse", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
-                                               dtype=torch.bfloat16, max_seq_len=max_len, cap=cap,
-                                               n_recent=n_recent) + 16, dtype=torch.uint8, device=dev)
-    # Every call of the step is marshalled once per replica (sfi.bind), so the host
-    # cost of a step is four C calls; the GPU work is unchanged.
-    for ly in layers:
-        ly["dense"] = sfi.bind(sfi.dense_attn_with_stats, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"],
-                               max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
-                               scores=ly["scores"], workspace=ws_dense, stream=main_s)
-        ly["select"] = sfi.bind(sfi.select_topk, ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink,
-                                n_recent=n_recent, sel_idx=ly["sel"], stream=aux_s)
-        # The step's slow step leaves its split-K combine to the pack launch (same outputs, bit for
-        # bit, as the plain slow step and pack).
-        ly["dense_d"] = sfi.bind(sfi.dense_attn_with_stats_deferred, ly["q"], ly["k"], ly["v"], ly["bt"],
-                                 ly["lens"], max_seq_len=max_len, n_sink=n_sink, n_recent=n_recent, out=ly["out"],
-                                 lse=ly["lse"], scores=ly["scores"], workspace=ws_dense, stream=main_s)
-        ly["pack"] = sfi.bind(sfi.pack_compact, ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"], n_sink=n_sink,
-                              cap=cap, max_seq_len=max_len, compact_k=ly["ck"], compact_v=ly["cv"],
-                              n_compact=ly["nc"], stream=aux_s)
-        ly["pack_m"] = sfi.bind(sfi.pack_compact_merge, ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"],
-                                n_sink=n_sink, cap=cap, max_seq_len=max_len, out=ly["out"], lse=ly["lse"],
-                                workspace=ws_dense, compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
-                                stream=main_s)
-        # The rest of the step in one launch: the fast step over the selection read in place, with the
-        # pack and the slow step's combine as work-groups of their own.
-        ly["finish"] = sfi.bind(sfi.sparse_decode_indexed_attn_merge, ly["q1"], ly["k"], ly["v"], ly["bt"],
-                                ly["lens"], ly["sel"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
-                                slow_out=ly["out"], slow_lse=ly["lse"], slow_workspace=ws_dense,
-                                compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"], out=ly["fout"],
-                                lse=ly["flse"], workspace=ws_sparse, stream=main_s)
-        ly["fast"] = sfi.bind(sfi.sparse_decode_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["ck"],
-                              ly["cv"], ly["nc"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
-                              out=ly["fout"], lse=ly["flse"], workspace=ws_sparse, stream=main_s)
-    dense_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(R)]
-    sync_ev = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(args.steps + args.warmup)]
-
-    def step(i, record=None):
-        ly = layers[i % R]
-        aux = aux_s is not main_s
-        if record is not None:
-            dense_ev[record][0].record(main_s)
-        # On one stream the last launch (fast step + pack) finishes the slow step; with the maintenance
-        # on a second stream the slow step merges its own splits.
-        (ly["dense"] if aux else ly["dense_d"])()
-        if record is not None:
-            dense_ev[record][1].record(main_s)
-        if aux:
-            ready, packed = sync_ev[i]
-            ready.record(main_s)
-            aux_s.wait_event(ready)
-            ly["select"]()
-            ly["pack"]()
-            packed.record(aux_s)
-            main_s.wait_event(packed)
-            ly["fast"]()
-        else:
-            ly["select"]()
-            ly["finish"]()
-
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0e.record(main_s)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t1e.record(main_s)
-    torch.cuda.synchronize()
-    step_s = t0e.elapsed_time(t1e) * 1e-3 / args.steps
-    # The slow-step launch inside the step, between events recorded around it (outside the timed
-    # steps: each event adds a stream command of its own).
-    for i in range(R):
-        step(i, record=i)
-    torch.cuda.synchronize()
-    in_step_dense_s = float(np.mean([a.elapsed_time(b) for a, b in dense_ev])) * 1e-3
-    # The slow-step kernel's own duration: the same bound launches back to back over the replicas
-    # (events on its stream).  Inside the step its event pair also spans the dispatch gap after the
-    # previous kernel, which rocprofv3's kernel durations do not count.
-    n_b2b = 20 * R
-
-    def b2b(name):
-        for i in range(R):
-            layers[i][name]()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(main_s)
-        for i in range(n_b2b):
-            layers[i % R][name]()
-        b1.record(main_s)
-        torch.cuda.synchronize()
-        return b0.elapsed_time(b1) * 1e-3 / n_b2b
-    dense_s = b2b("dense_d")
-
-    esize = 2
-    n_c = cap
-    dense_kv = kv_bytes_dense(B, Hkv, L, d, esize)
-    pack_bytes = 2 * B * Hkv * n_c * 2 * d * esize
-    fast_kv = B * Hkv * (n_c + n_recent) * 2 * d * esize
-    step_bytes = dense_kv + pack_bytes + fast_kv
-    value = step_bytes / step_s / 1e9
-    dense_alg = dense_kv + B * Hkv * L * 4            # K/V read + scores written
-    traffic, traffic_src = profiled_traffic()
-    roof = {"kernel": "decode_kernel<bf16, d128, G2, dense + group logits> (slow step; its split-K combine "
-                      "runs in the step's last launch)", "bound": "hbm",
-            "achieved": dense_alg / dense_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dense_alg / dense_s / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-            "traffic_source": traffic_src, "alg_bytes_per_launch": dense_alg, "avg_launch_us": dense_s * 1e6,
-            "timing": f"{n_b2b} back-to-back launches over {R} replicas, HIP events on the launch stream",
-            "in_step_event_us": in_step_dense_s * 1e6}
-    log(f"step {step_s * 1e6:.1f} us, {value:.0f} GB/s; dense kernel {dense_s * 1e6:.1f} us "
-        f"= {roof['achieved']:.0f} GB/s ({100 * roof['frac']:.1f}% of peak)")
-
-    result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: B=1, Hq=16, Hkv=8, d=128, page 16, "
-                               "sink 4, recent 64, selected 1980 (12.5% retention); step = slow step "
-                               "(dense + logits) + Selector + one launch of fast step over the selection read in "
-                               "place, pack, and the slow step's split combine"
-                               + (" (Selector and pack on a second stream)" if args.aux_stream else ""),
-                   "global_batch": B, "seq_len": L, "replicas": R, "step_kv_bytes": step_bytes},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": roof,
-    }
-
-    result["separate_combine_step"] = separate_combine_step(layers, main_s, args.steps, step_bytes, b2b)
-    # every kernel of the step back to back over the replicas (HIP events on its stream)
-    kern = {}
-    for name in ("select", "finish", "pack", "fast"):
-        for i in range(R):
-            layers[i][name]()
-        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        k0.record(main_s)
-        for i in range(n_b2b):
-            layers[i % R][name]()
-        k1.record(main_s)
-        torch.cuda.synchronize()
-        kern[name + "_us"] = round(k0.elapsed_time(k1) * 1e3 / n_b2b, 2)
-    kern["dense_us"] = round(dense_s * 1e6, 2)
-    kern["finish_GBps"] = round((pack_bytes + fast_kv) / kern["finish_us"] / 1e3, 1)
-    kern["select_GBps"] = round(B * Hkv * (L - n_sink - n_recent) * 4 / kern["select_us"] / 1e3, 1)
-    kern["pack_GBps"] = round(pack_bytes / kern["pack_us"] / 1e3, 1)
-    kern["fast_GBps"] = round(fast_kv / kern["fast_us"] / 1e3, 1)
-    result["step_kernels"] = kern
-    log(f"step kernels {kern}")
-    result["fused_pack_step"] = fused_pack_steps(sfi, layers, dev, args.steps, k_sel, cap, n_sink, n_recent, max_len,
-                                                 ws_dense, ws_sparse)
-    result["hip_graph"] = graph_steps(sfi, layers, dev, args.steps, step_bytes, k_sel, cap, n_sink, n_recent,
-                                      max_len, ws_dense, ws_sparse)
-
-    if not args.no_sweep:
-        result["sweep"] = sweep(sfi, layers, dev, main_s, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense, ws_sparse)
-        log("batch-16 sweep")
-        big = make_layers(1, L, 16, frac, dev, 5000)
-        result["sweep_b16"] = sweep(sfi, big, dev, main_s, 16, Hq, Hkv, d, L, n_sink, n_recent, None, None)
-        del big
-        log("long-context sweeps")
-        result["sweep_long"] = sweep_long(sfi, dev, main_s, Hq, Hkv, d, n_sink, n_recent)
-
-    if not args.no_sweep:
-        log("64K refresh overlap")
-        result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
-        log("fused KV append + fast step")
-        result["append_fast"] = append_fast(sfi, dev, main_s)
-        log("per-query-head selection")
-        result["head_selection"] = head_selection(sfi, dev)
-        log("draft steps with an intra-draft refresh layer")
-        result["draft_refresh"] = draft_refresh_c3(sfi, dev)
-        log("refresh schedule on drifting support")
-        result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
-        log("128K speculative mix")
-        result["specmix_128k"] = specmix(sfi, dev)
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, L, B, frac, n_sink, n_recent, step_bytes)
-    if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            sfi.stream_copy(src, dst)
-        torch.cuda.synchronize()
-    print(json.dumps(result), flush=True)
+def kv_bytes(B, Hkv, tokens, d, esize=2):
+    return B * Hkv * tokens * 2 * d * esize
 
 
-def sweep(sfi, layers, dev, stream, B, Hq, Hkv, d, L, n_sink, n_recent, ws_dense, ws_sparse):
-    """Fast step at each Table 1 retention vs plain dense attention at the same shape."""
-    import torch
-    from sfi_synth import RETENTIONS, retention_budget
-    R = len(layers)
-    max_len = L
-    ex = layers[0]
-    if ws_dense is None:
-        ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
-                                                  dtype=torch.bfloat16, max_seq_len=max_len) + 16,
-                               dtype=torch.uint8, device=dev)
-    outs = [torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev) for _ in range(R)]
-    lses = [torch.empty((B, 1, Hq), dtype=torch.float32, device=dev) for _ in range(R)]
-    n_rep = max(20, 400 // R * R)
-
-    dense_calls = [sfi.bind(sfi.dense_attn_with_stats, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"],
-                            max_seq_len=max_len, with_scores=False, out=outs[r], lse=lses[r], workspace=ws_dense,
-                            stream=stream) for r, ly in enumerate(layers)]
-
-    def dense(i):
-        dense_calls[i % R]()
-    for i in range(R):
-        dense(i)
-    t_dense = time_loop(dense, n_rep, stream)
-    dense_kv = kv_bytes_dense(B, Hkv, L, d)
-    # The slow step itself (dense + logits), with its own split-K combine and deferred as the step
-    # runs it (the combine then rides in the step's last launch); algorithmic bytes are K/V + logits.
-    scs = [torch.empty((B, Hkv, max_len), dtype=torch.float32, device=dev) for _ in range(R)]
-    slow_bytes = dense_kv + B * Hkv * L * 4
-    slow = {}
-    for name, op in (("slow_step", sfi.dense_attn_with_stats), ("slow_step_deferred", sfi.dense_attn_with_stats_deferred)):
-        calls = [sfi.bind(op, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len, n_sink=n_sink,
-                          n_recent=n_recent, out=outs[r], lse=lses[r], scores=scs[r], workspace=ws_dense,
-                          stream=stream) for r, ly in enumerate(layers)]
-        for i in range(R):
-            calls[i]()
-        t_s = time_loop(lambda i: calls[i % R](), n_rep, stream)
-        slow[name] = {"us": round(t_s * 1e6, 2), "GBps": round(slow_bytes / t_s / 1e9, 1),
-                      "pct_peak": round(100 * slow_bytes / t_s / 1e9 / HBM_PEAK_GBS, 1)}
-        del calls
-    del scs
-    rows = []
-    rng = __import__("numpy").random.default_rng(9)
-    for frac in RETENTIONS:
-        k = retention_budget(L, frac, n_sink, n_recent)
-        cap = n_sink + max(k, 1)
-        # selection: k random candidates per (b, g) (the fast step's cost does not depend on which)
-        import numpy as np
-        lo, hi = n_sink, L - n_recent
-        comp = []
-        for ly in layers:
-            sel = np.full((B, Hkv, max(k, 1)), -1, np.int32)
-            for b in range(B):
-                for g in range(Hkv):
-                    if k:
-                        sel[b, g, :k] = np.sort(rng.choice(np.arange(lo, hi), k, replace=False))
-            sel_d = torch.from_numpy(sel).to(dev)
-            ck, cv, nc = sfi.pack_compact(ly["k"], ly["v"], ly["bt"], ly["lens"], sel_d, n_sink=n_sink, cap=cap,
-                                          max_seq_len=max_len, stream=stream)
-            comp.append((ck, cv, nc, torch.empty((B, Hq, d), dtype=torch.float32, device=dev),
-                         torch.empty((B, Hq), dtype=torch.float32, device=dev)))
-        ws = torch.zeros(sfi.workspace_size("sparse", k_pool=ex["k"], block_table=ex["bt"], Hq=Hq,
-                                            dtype=torch.bfloat16, max_seq_len=max_len, cap=cap, n_recent=n_recent)
-                         + 16, dtype=torch.uint8, device=dev)
-
-        fast_calls = [sfi.bind(sfi.sparse_decode_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ck, cv, nc,
-                               n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=o, lse=l, workspace=ws,
-                               stream=stream) for ly, (ck, cv, nc, o, l) in zip(layers, comp)]
-
-        def fast(i):
-            fast_calls[i % R]()
-        for i in range(R):
-            fast(i)
-        t = time_loop(fast, n_rep, stream)
-        kv = B * Hkv * (n_sink + k + n_recent) * 2 * d * 2
-        r = (n_sink + k + n_recent) / L
-        rows.append({"retention_pct": round(100 * r, 2), "selected": k, "fast_us": round(t * 1e6, 2),
-                     "fast_GBps": round(kv / t / 1e9, 1), "fast_pct_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 1),
-                     "dense_us": round(t_dense * 1e6, 2), "dense_GBps": round(dense_kv / t_dense / 1e9, 1),
-                     "speedup": round(t_dense / t, 3), "speedup_x_r": round(t_dense / t * r, 3)})
-        del comp, fast_calls
-    log(f"sweep L={L} B={B} " + " ".join(f"{r['retention_pct']}%:{r['speedup']}x" for r in rows)
-        + f"; slow step {slow['slow_step']['pct_peak']}% of peak, deferred {slow['slow_step_deferred']['pct_peak']}%")
-    return {"batch": B, "kv_len": L, "replicas": R, "launches_per_point": n_rep, "points": rows, **slow}
-
+# --------------------------------------------------------------------------- inputs
 
 def gpu_layers(R, L, B, Hq, Hkv, d, dev, seed):
     """Replicas of a decode layer drawn on the GPU (seeded N(0,1) bf16 Q/K/V, block tables that are
-    random permutations of the page pool): the long-context sweeps only time kernels, and drawing
-    hundreds of MiB per replica on the host would dominate the run."""
+    random permutations of the page pool): the sweeps only time kernels, and drawing hundreds of MiB
+    per replica on the host would dominate the run."""
     import torch
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -479,18 +126,414 @@ def gpu_layers(R, L, B, Hq, Hkv, d, dev, seed):
     return out
 
 
-def sweep_long(sfi, dev, stream, Hq, Hkv, d, n_sink, n_recent):
-    """The batch-1 retention sweep at longer contexts (32K, 64K, 128K)."""
-    import torch
-    res = {}
-    for L in (32768, 65536, 131072):
-        R = max(2, (1 << 30) // (Hkv * L * 2 * d * 2))      # >= 1 GiB of K/V across replicas
-        layers = gpu_layers(R, L, 1, Hq, Hkv, d, dev, 7000 + L)
-        res[str(L)] = sweep(sfi, layers, dev, stream, 1, Hq, Hkv, d, L, n_sink, n_recent, None, None)
-        del layers
+class Workload:
+    """P K/V pools of one decode-layer shape (>= 512 MiB together, or one pool when one is that
+    large) for the dense baseline and the slow step, and the means to build fast-step replicas
+    over them at any retention."""
+
+    def __init__(self, sfi, dev, B, L, Hq, Hkv, d, n_sink, n_recent, seed):
+        import torch
+        self.sfi, self.dev = sfi, dev
+        self.B, self.L, self.Hq, self.Hkv, self.d = B, L, Hq, Hkv, d
+        self.n_sink, self.n_recent = n_sink, n_recent
+        pool_bytes = kv_bytes(B, Hkv, L, d)
+        self.P = max(1, -(-MIN_ROTATE // pool_bytes))
+        self.layers = gpu_layers(self.P, L, B, Hq, Hkv, d, dev, seed)
+        self.stream = torch.cuda.current_stream(dev)
+        self.seed = seed
+        self.ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=self.layers[0]["k"],
+                                                       block_table=self.layers[0]["bt"], Hq=Hq,
+                                                       dtype=torch.bfloat16, max_seq_len=L) + 16,
+                                    dtype=torch.uint8, device=dev)
+
+    def dense(self):
+        """Plain dense attention (Table 1's denominator) over the pools."""
+        import torch
+        sfi, P = self.sfi, self.P
+        outs = [torch.empty((self.B, 1, self.Hq, self.d), dtype=torch.float32, device=self.dev) for _ in range(P)]
+        calls = [sfi.bind(sfi.dense_attn_with_stats, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"],
+                          max_seq_len=self.L, with_scores=False, out=outs[r], workspace=self.ws_dense,
+                          stream=self.stream) for r, ly in enumerate(self.layers)]
+        return self._time(calls, kv_bytes(self.B, self.Hkv, self.L, self.d))
+
+    def slow(self, deferred):
+        """The slow step (dense + masked group logits), with its own split-K combine or deferred
+        (its partials are then left for a later launch; nothing here reads them)."""
+        import torch
+        sfi, P = self.sfi, self.P
+        op = sfi.dense_attn_with_stats_deferred if deferred else sfi.dense_attn_with_stats
+        scs = [torch.empty((self.B, self.Hkv, self.L), dtype=torch.float32, device=self.dev) for _ in range(P)]
+        outs = [torch.empty((self.B, 1, self.Hq, self.d), dtype=torch.float32, device=self.dev) for _ in range(P)]
+        ws = self.ws_dense if not deferred else torch.zeros_like(self.ws_dense)
+        calls = [sfi.bind(op, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=self.L,
+                          n_sink=self.n_sink, n_recent=self.n_recent, out=outs[r], scores=scs[r],
+                          workspace=ws, stream=self.stream) for r, ly in enumerate(self.layers)]
+        return self._time(calls, kv_bytes(self.B, self.Hkv, self.L, self.d) + self.B * self.Hkv * self.L * 4)
+
+    def fast(self, k):
+        """The fast step at k selected tokens per (request, KV head) over replicas rotating >= 512 MiB."""
+        import torch
+        sfi = self.sfi
+        tot = self.n_sink + k + self.n_recent
+        fb = kv_bytes(self.B, self.Hkv, tot, self.d)
+        R = max(self.P, -(-MIN_ROTATE // fb))
+        cap = self.n_sink + max(k, 1)
+        lo, hi = self.n_sink, self.L - self.n_recent
+        rng = np.random.default_rng(self.seed + k)
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(self.seed + 7 * k)
+        npg = self.B * self.L // 16
+        reps = []
+        for r in range(R):
+            ly = self.layers[r % self.P]
+            bt = torch.randperm(npg, generator=g, device=self.dev).to(torch.int32).reshape(self.B, self.L // 16)
+            sel = np.full((self.B, self.Hkv, max(k, 1)), -1, np.int32)
+            for b in range(self.B):
+                for h in range(self.Hkv):
+                    if k:
+                        sel[b, h, :k] = np.sort(rng.permutation(hi - lo)[:k] + lo)
+            ck, cv, nc = sfi.pack_compact(ly["k"], ly["v"], bt, ly["lens"], torch.from_numpy(sel).to(self.dev),
+                                          n_sink=self.n_sink, cap=cap, max_seq_len=self.L)
+            q1 = torch.randn((self.B, self.Hq, self.d), generator=g, device=self.dev).to(torch.bfloat16)
+            reps.append((ly, bt, ck, cv, nc, q1))
+        ws = torch.zeros(sfi.workspace_size("sparse", k_pool=self.layers[0]["k"], block_table=self.layers[0]["bt"],
+                                            Hq=self.Hq, dtype=torch.bfloat16, max_seq_len=self.L, cap=cap,
+                                            n_recent=self.n_recent) + 16, dtype=torch.uint8, device=self.dev)
+        outs = [torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device=self.dev) for _ in range(R)]
+        calls = [sfi.bind(sfi.sparse_decode_attn, q1, ly["k"], ly["v"], bt, ly["lens"], ck, cv, nc,
+                          n_sink=self.n_sink, n_recent=self.n_recent, max_seq_len=self.L, out=outs[r],
+                          workspace=ws, stream=self.stream)
+                 for r, (ly, bt, ck, cv, nc, q1) in enumerate(reps)]
+        res = self._time(calls, fb)
+        del reps, calls, outs
         torch.cuda.empty_cache()
+        return res
+
+    def _time(self, calls, nbytes):
+        n_c = len(calls)
+        n = max(400, n_c)
+        for i in range(n_c):
+            calls[i]()
+        t = time_loop(lambda i: calls[i % n_c](), n, self.stream)
+        return {"us": t * 1e6, "GBps": nbytes / t / 1e9, "bytes": nbytes, "launches": n, "replicas": n_c,
+                "rotated_bytes": n_c * nbytes}
+
+
+def retention_points(L, n_sink, n_recent):
+    from sfi_synth import RETENTIONS, retention_budget
+    return [(frac, retention_budget(L, frac, n_sink, n_recent)) for frac in RETENTIONS]
+
+
+def sweep(sfi, dev, B, L, Hq, Hkv, d, n_sink, n_recent, read_GBps, seed):
+    """Fast step at each Table 1 retention against plain dense attention at the same shape, and the
+    slow step (own combine and deferred), every loop cache-clean."""
+    import torch
+    w = Workload(sfi, dev, B, L, Hq, Hkv, d, n_sink, n_recent, seed)
+    dn = w.dense()
+    slow = {name: w.slow(deferred) for name, deferred in (("slow_step", False), ("slow_step_deferred", True))}
+    points = []
+    for frac, k in retention_points(L, n_sink, n_recent):
+        f = w.fast(k)
+        r = (n_sink + k + n_recent) / L
+        points.append({"retention_pct": round(100 * r, 2), "selected": k, "fast_us": round(f["us"], 2),
+                       "fast_GBps": round(f["GBps"], 1), "fast_pct_peak": round(100 * f["GBps"] / HBM_PEAK_GBS, 1),
+                       "fast_pct_measured_read": round(100 * f["GBps"] / read_GBps, 1),
+                       "dense_us": round(dn["us"], 2), "speedup": round(dn["us"] / f["us"], 3),
+                       "speedup_x_r": round(dn["us"] / f["us"] * r, 3), "rotated_bytes": f["rotated_bytes"]})
+    out = {"batch": B, "kv_len": L, "dense": {"us": round(dn["us"], 2), "GBps": round(dn["GBps"], 1),
+                                              "pct_peak": round(100 * dn["GBps"] / HBM_PEAK_GBS, 1),
+                                              "pct_measured_read": round(100 * dn["GBps"] / read_GBps, 1),
+                                              "rotated_bytes": dn["rotated_bytes"]},
+           "points": points}
+    for name, sres in slow.items():
+        out[name] = {"us": round(sres["us"], 2), "GBps": round(sres["GBps"], 1),
+                     "pct_peak": round(100 * sres["GBps"] / HBM_PEAK_GBS, 1), "rotated_bytes": sres["rotated_bytes"]}
+    log(f"sweep L={L} B={B} " + " ".join(f"{p['retention_pct']}%:{p['fast_us']}us/{p['speedup']}x" for p in points)
+        + f"; dense {out['dense']['us']} us; slow step {out['slow_step']['us']} / deferred "
+        + f"{out['slow_step_deferred']['us']} us")
+    del w
+    torch.cuda.empty_cache()
+    return out
+
+
+def sweep_long(sfi, dev, read_GBps):
+    """The batch-1 retention sweep at longer contexts (32K, 64K, 128K)."""
+    return {str(L): sweep(sfi, dev, 1, L, 16, 8, 128, 4, 64, read_GBps, 7000 + L) for L in (32768, 65536, 131072)}
+
+
+def read_ceiling(sfi, dev):
+    """Streaming read rate of this GPU: sfi_stream_read over 512 MiB buffers, alternating two."""
+    import torch
+    bufs = [torch.empty(512 << 20, dtype=torch.uint8, device=dev) for _ in range(2)]
+    for b in bufs:
+        b.random_(0, 255)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    for i in range(4):
+        sfi.stream_read(bufs[i % 2], sink, stream=st)
+    t = time_loop(lambda i: sfi.stream_read(bufs[i % 2], sink, stream=st), 40, st)
+    res = {"GBps": round((512 << 20) / t / 1e9, 1), "bytes_per_launch": 512 << 20,
+           "kernel": "stream_read_kernel (sfi_stream_read)"}
+    del bufs
+    torch.cuda.empty_cache()
+    log(f"streaming read {res['GBps']} GB/s")
     return res
 
+
+# --------------------------------------------------------------------------- the step
+
+def make_layers(n, L, B, frac, dev, seed0):
+    from sfi_synth import qwen06b_decode_case
+    out = []
+    for r in range(n):
+        c = qwen06b_decode_case(seed0 + r, L=L, B=B, frac=frac)
+        out.append(dict(case=c, k=upload(c.kv.k, dev), v=upload(c.kv.v, dev), bt=upload(c.kv.block_table, dev),
+                        lens=upload(c.seq_lens.astype("int32"), dev), q=upload(c.q, dev),
+                        q1=upload(c.q[:, 0], dev)))
+    return out
+
+
+def step_leg(sfi, dev, steps, warmup, R=8):
+    """K steps of the whole path on the 16K layer (rotating R replicas of 64 MiB K/V each)."""
+    import torch
+    L, B, Hq, Hkv, d = 16384, 1, 16, 8, 128
+    n_sink, n_recent, frac = 4, 64, (1, 8)
+    layers = make_layers(R, L, B, frac, dev, 1000)
+    k_sel = layers[0]["case"].k_sel
+    cap = n_sink + k_sel
+    st = torch.cuda.current_stream(dev)
+    ws_dense = torch.zeros(sfi.workspace_size("dense", k_pool=layers[0]["k"], block_table=layers[0]["bt"], Hq=Hq,
+                                              dtype=torch.bfloat16, max_seq_len=L) + 16, dtype=torch.uint8, device=dev)
+    ws_sparse = torch.zeros(sfi.workspace_size("sparse", k_pool=layers[0]["k"], block_table=layers[0]["bt"], Hq=Hq,
+                                               dtype=torch.bfloat16, max_seq_len=L, cap=cap, n_recent=n_recent) + 16,
+                            dtype=torch.uint8, device=dev)
+    for ly in layers:
+        ly["out"] = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
+        ly["lse"] = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+        ly["scores"] = torch.empty((B, Hkv, L), dtype=torch.float32, device=dev)
+        ly["sel"] = torch.empty((B, Hkv, k_sel), dtype=torch.int32, device=dev)
+        ly["ck"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+        ly["cv"] = torch.empty((B, Hkv, cap, d), dtype=torch.bfloat16, device=dev)
+        ly["nc"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        ly["fout"] = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        ly["flse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ly["slow"] = sfi.bind(sfi.dense_attn_with_stats_deferred, ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"],
+                              max_seq_len=L, n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
+                              scores=ly["scores"], workspace=ws_dense, stream=st)
+        ly["select"] = sfi.bind(sfi.select_topk, ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent,
+                                sel_idx=ly["sel"], stream=st)
+        ly["finish"] = sfi.bind(sfi.sparse_decode_indexed_attn_merge, ly["q1"], ly["k"], ly["v"], ly["bt"],
+                                ly["lens"], ly["sel"], n_sink=n_sink, n_recent=n_recent, max_seq_len=L,
+                                slow_out=ly["out"], slow_lse=ly["lse"], slow_workspace=ws_dense,
+                                compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"], out=ly["fout"],
+                                lse=ly["flse"], workspace=ws_sparse, stream=st)
+
+    def step(i):
+        ly = layers[i % R]
+        ly["slow"]()
+        ly["select"]()
+        ly["finish"]()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0e.record(st)
+    for i in range(steps):
+        step(warmup + i)
+    t1e.record(st)
+    torch.cuda.synchronize()
+    step_s = t0e.elapsed_time(t1e) * 1e-3 / steps
+    # the step's kernels one at a time, back to back over the replicas (a deferred slow step is
+    # always followed by the launch that merges it, so those two are timed as a pair)
+    kern = {"select_us": round(time_loop(lambda i: layers[i % R]["select"](), 20 * R, st) * 1e6, 2)}
+    pair = time_loop(lambda i: (layers[i % R]["slow"](), layers[i % R]["finish"]()), 20 * R, st)
+    kern["slow_plus_finish_us"] = round(pair * 1e6, 2)
+    step_bytes = (kv_bytes(B, Hkv, L, d) + B * Hkv * L * 4 + 2 * kv_bytes(B, Hkv, cap, d)
+                  + kv_bytes(B, Hkv, cap + n_recent, d))
+    res = {"ms_per_step": step_s * 1e3, "us_per_step": round(step_s * 1e6, 2), "step_bytes": step_bytes,
+           "step_GBps": round(step_bytes / step_s / 1e9, 1), "kernels": kern, "replicas": R,
+           "rotated_bytes": R * kv_bytes(B, Hkv, L, d),
+           "form": "deferred slow step (dense + logits) -> Selector (k 1980) -> fast step over the selection read "
+                   "in place + gather-pack + the slow step's split-K combine, one launch"}
+    log(f"step {step_s * 1e6:.1f} us; kernels {kern}")
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle's fast step on the headline workload (the 16K layer at 12.5 %, all 8 KV
+    heads), timed on the host for ~budget_s, on every core and on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import oracle as O
+    from sfi_synth import qwen06b_decode_case
+    L, B, n_sink, n_recent = 16384, 1, 4, 64
+    c = qwen06b_decode_case(1000, L=L, B=B, frac=(1, 8))
+    b = 0
+    Qv = c.q_values()[b]
+    lo, hi = O.candidate_range(L, 1, n_sink, n_recent)
+    rng = np.random.default_rng(0)
+    sel = np.stack([np.sort(rng.permutation(hi - lo)[:c.k_sel] + lo) for _ in range(c.Hkv)]).astype(np.int32)
+    ck, cv, nc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, sel, n_sink + c.k_sel)
+    fast_bytes = kv_bytes(1, c.Hkv, n_sink + c.k_sel + n_recent, c.d)
+
+    def run(threads, budget):
+        t0 = time.perf_counter()
+        n = 0
+        with threadpool_limits(limits=threads):
+            while True:
+                O.sparse_decode(Qv[0], ck, cv, nc, c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, n_recent,
+                                c.scale, kv_dtype="bf16")
+                n += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+        return (time.perf_counter() - t0) / n, n
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    dt_all, n_all = run(cores, budget_s / 2)
+    dt_one, n_one = run(1, budget_s / 2)
+    blas = [{k: i.get(k) for k in ("internal_api", "num_threads")} for i in threadpool_info()]
+    return {"value": round(fast_bytes / dt_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_all} fast steps of the 16K layer at 12.5 % retention (1 request x 8 KV heads, compact "
+                      f"{n_sink + c.k_sel} + recent {n_recent} tokens), fp64 NumPy, {cores} threads; "
+                      f"{dt_all * 1e3:.1f} ms per step",
+            "value_1_thread": round(fast_bytes / dt_one / 1e9, 4),
+            "sample_1_thread": f"{n_one} fast steps, one thread; {dt_one * 1e3:.1f} ms per step",
+            "host_cpus": os.cpu_count(), "affinity_cpus": cores, "blas": blas}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true", help="headline and step only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated legs to run alone, printing their figures: headline, append_fast, "
+                         "draft_refresh, head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k, "
+                         "sweep_b1, sweep_b16, sweep_long")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_kv_cache_sfi_amd as sfi
+
+    sfi.load()
+    dev = torch.device("cuda:0")
+    L, B, Hq, Hkv, d, n_sink, n_recent = 16384, 1, 16, 8, 128, 4, 64
+
+    def headline(read):
+        """The fast step at 12.5 % (16K, batch 1), the dense baseline, their roofline and read ratio."""
+        w = Workload(sfi, dev, B, L, Hq, Hkv, d, n_sink, n_recent, 2024)
+        f = w.fast(1980)
+        dn = w.dense()
+        traffic, src = profiled_traffic(FAST_KERNEL)
+        roof = {"kernel": "decode_kernel<bf16, d128, G2, fast step> (sfi_sparse_decode_attn, 16 splits of 128 "
+                          "tokens per KV head, split-K combine in the launch)",
+                "bound": "hbm", "achieved": round(f["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(f["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": src,
+                "alg_bytes_per_launch": f["bytes"], "avg_launch_us": round(f["us"], 3),
+                "timing": f"{f['launches']} back-to-back launches over {f['replicas']} replicas "
+                          f"({f['rotated_bytes'] >> 20} MiB distinct), HIP events on the launch stream",
+                "pct_measured_read": round(100 * f["GBps"] / read["GBps"], 1)}
+        dense_roof = {"kernel": "decode_kernel<bf16, d128, G2, dense> (sfi_dense_attn_with_stats without logits)",
+                      "achieved": round(dn["GBps"], 1), "frac": round(dn["GBps"] / HBM_PEAK_GBS, 4),
+                      "avg_launch_us": round(dn["us"], 3), "rotated_bytes": dn["rotated_bytes"],
+                      "pct_measured_read": round(100 * dn["GBps"] / read["GBps"], 1)}
+        del w
+        torch.cuda.empty_cache()
+        log(f"fast step 12.5% {f['us']:.2f} us = {f['GBps']:.0f} GB/s; dense {dn['us']:.2f} us; "
+            f"speedup {dn['us'] / f['us']:.2f}x")
+        return f, dn, roof, dense_roof
+
+    if args.only:
+        legs = {"append_fast": lambda: append_fast(sfi, dev, torch.cuda.current_stream(dev)),
+                "draft_refresh": lambda: draft_refresh_c3(sfi, dev),
+                "head_selection": lambda: head_selection(sfi, dev),
+                "refresh_schedule": lambda: refresh_schedule_c3(sfi, dev),
+                "refresh_64k_overlap": lambda: refresh_overlap(sfi, dev),
+                "specmix_128k": lambda: specmix(sfi, dev),
+                "headline": lambda: headline(read_ceiling(sfi, dev))[2],
+                "sweep_b1": lambda: sweep(sfi, dev, 1, L, Hq, Hkv, d, n_sink, n_recent,
+                                          read_ceiling(sfi, dev)["GBps"], 3000),
+                "sweep_b16": lambda: sweep(sfi, dev, 16, L, Hq, Hkv, d, n_sink, n_recent,
+                                           read_ceiling(sfi, dev)["GBps"], 5000),
+                "sweep_long": lambda: sweep_long(sfi, dev, read_ceiling(sfi, dev)["GBps"])}
+        names = [n for n in args.only.split(",") if n]
+        unknown = [n for n in names if n not in legs]
+        if unknown:
+            print(f"unknown legs {unknown}; known: {sorted(legs)}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({n: legs[n]() for n in names}), flush=True)
+        return
+
+    read = read_ceiling(sfi, dev)
+    f, dn, roof, dense_roof = headline(read)
+    step = step_leg(sfi, dev, args.steps, args.warmup)
+    value = f["GBps"]
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-0.6B-shaped decode layer, 16K KV: batch 1, Hq 16 / Hkv 8, d 128, page 16, "
+                               "sink 4, recent 64, 1980 selected (12.5% retention); value = fast-step K/V bytes / "
+                               "fast-step kernel time (cache-clean rotation); a step = slow step + Selector + "
+                               "fast step with pack and combine",
+                   "global_batch": B, "seq_len": L, "retention_pct": 12.5,
+                   "fast_step_kv_bytes": f["bytes"], "rotated_bytes": f["rotated_bytes"]},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_measured_read": round(100 * value / read["GBps"], 2),
+        "speedup_vs_dense": round(dn["us"] / f["us"], 3),
+        "fast_step_us": round(f["us"], 3), "dense_us": round(dn["us"], 3),
+        "roofline": roof,
+        "dense_roofline": dense_roof,
+        "measured_read": read,
+        "step": step,
+    }
+
+    if not args.no_sweep:
+        log("retention sweeps")
+        result["sweep_b1_16k"] = sweep(sfi, dev, 1, L, Hq, Hkv, d, n_sink, n_recent, read["GBps"], 3000)
+        result["sweep_b16_16k"] = sweep(sfi, dev, 16, L, Hq, Hkv, d, n_sink, n_recent, read["GBps"], 5000)
+        result["sweep_long"] = sweep_long(sfi, dev, read["GBps"])
+        log("64K refresh overlap")
+        result["refresh_64k_overlap"] = refresh_overlap(sfi, dev)
+        log("fused KV append + fast step")
+        result["append_fast"] = append_fast(sfi, dev, torch.cuda.current_stream(dev))
+        log("per-query-head selection")
+        result["head_selection"] = head_selection(sfi, dev)
+        log("draft steps with an intra-draft refresh layer")
+        result["draft_refresh"] = draft_refresh_c3(sfi, dev)
+        log("refresh schedule on drifting support")
+        result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
+        log("128K speculative mix")
+        result["specmix_128k"] = specmix(sfi, dev)
+
+    if not args.no_cpu_baseline:
+        log("oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            sfi.stream_copy(src, dst)
+        torch.cuda.synchronize()
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------- other legs
 
 def append_fast(sfi, dev, stream, Hq=16, Hkv=8, d=128, n_sink=4, n_recent=64):
     """Fast step with the decoded token's K/V stored in the same launch
@@ -925,132 +968,6 @@ def refresh_overlap(sfi, dev):
     return res
 
 
-def separate_combine_step(layers, stream, steps, step_bytes, b2b):
-    """The step as four launches: with the slow step's own split-K combine (sfi_dense_attn_with_stats,
-    sfi_select_topk, sfi_pack_compact, fast step over the compact buffer), and with the combine in the pack
-    launch (sfi_pack_compact_merge).  Their times, the slow-step and pack kernels back to back, and whether
-    every output of the step (slow-step output and lse, logits, selection, compact buffer, fast-step output
-    and lse) equals that of the three-launch step, bit for bit."""
-    import torch
-    R = len(layers)
-    names = ("out", "lse", "scores", "sel", "ck", "cv", "nc", "fout", "flse")
-    main = ("dense_d", "select", "finish")
-    plain = ("dense", "select", "pack", "fast")
-    pack_combine = ("dense_d", "select", "pack_m", "fast")
-
-    def run(ly, calls):
-        for c in calls:
-            ly[c]()
-    same = {"plain": True, "pack_combine": True}
-    for ly in layers:
-        run(ly, main)
-        torch.cuda.synchronize()
-        ref = {n: ly[n].clone() for n in names}
-        for key, calls in (("plain", plain), ("pack_combine", pack_combine)):
-            for n in names:
-                ly[n].zero_()
-            run(ly, calls)
-            torch.cuda.synchronize()
-            same[key] &= all(torch.equal(ref[n].view(torch.uint8), ly[n].view(torch.uint8)) for n in names)
-    t_plain = time_loop(lambda i: run(layers[i % R], plain), steps, stream)
-    t_pc = time_loop(lambda i: run(layers[i % R], pack_combine), steps, stream)
-    res = {"plain_ms_per_step": round(t_plain * 1e3, 5), "plain_value": round(step_bytes / t_plain / 1e9, 2),
-           "pack_combine_ms_per_step": round(t_pc * 1e3, 5),
-           "dense_us": round(b2b("dense") * 1e6, 2), "pack_combine_us": round(b2b("pack_m") * 1e6, 2),
-           "outputs_match_three_launch_step": same}
-    log(f"four-launch steps {res}")
-    return res
-
-
-def fused_pack_steps(sfi, layers, dev, steps, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
-    """The three-launch step with the slow step's own combine: slow step -> Selector -> one launch of the
-    fast step over sink + selected + recent read in place, whose pack work-groups write the compact buffer
-    (sfi_sparse_decode_indexed_attn with a compact buffer).  Outputs, selection and compact buffer must
-    equal the headline step's bit for bit."""
-    import torch
-    stream = torch.cuda.current_stream(dev)
-    R = len(layers)
-    B, Hq, d = layers[0]["q1"].shape
-    Hkv = layers[0]["k"].shape[1]
-    calls = []
-    for ly in layers:
-        fz = {"ck": torch.empty_like(ly["ck"]), "cv": torch.empty_like(ly["cv"]), "nc": torch.empty_like(ly["nc"]),
-              "out": torch.empty_like(ly["fout"]), "lse": torch.empty_like(ly["flse"])}
-        ly["fused"] = fz
-        calls.append((ly["dense"], ly["select"],
-                      sfi.bind(sfi.sparse_decode_indexed_attn, ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"],
-                               ly["sel"], n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len, out=fz["out"],
-                               lse=fz["lse"], workspace=ws_sparse, stream=stream, compact_k=fz["ck"],
-                               compact_v=fz["cv"], n_compact=fz["nc"])))
-
-    def step(i):
-        for c in calls[i % R]:
-            c()
-    for i in range(R):
-        step(i)
-        layers[i]["pack"]()
-        layers[i]["fast"]()
-    torch.cuda.synchronize()
-    same = all(torch.equal(ly["fused"]["out"], ly["fout"]) and torch.equal(ly["fused"]["lse"], ly["flse"])
-               and torch.equal(ly["fused"]["nc"], ly["nc"])
-               and torch.equal(ly["fused"]["ck"].view(torch.int16), ly["ck"].view(torch.int16))
-               and torch.equal(ly["fused"]["cv"].view(torch.int16), ly["cv"].view(torch.int16)) for ly in layers)
-    t = time_loop(step, steps, stream)
-    res = {"ms_per_step": round(t * 1e3, 5), "launches_per_step": 3, "matches_four_launch_step": bool(same)}
-    log(f"fused-pack step {res}")
-    return res
-
-
-def graph_steps(sfi, layers, dev, steps, step_bytes, k_sel, cap, n_sink, n_recent, max_len, ws_dense, ws_sparse):
-    """The same step captured once per replica in a HIP graph and replayed: the GPU time of the
-    step without host launch cost or launch gaps between its kernels.  The first replay's
-    fast-step output is checked against the eager step's."""
-    import torch
-    R = len(layers)
-    side = torch.cuda.Stream(device=dev)
-
-    def run(ly):
-        sfi.dense_attn_with_stats_deferred(ly["q"], ly["k"], ly["v"], ly["bt"], ly["lens"], max_seq_len=max_len,
-                                           n_sink=n_sink, n_recent=n_recent, out=ly["out"], lse=ly["lse"],
-                                           scores=ly["scores"], workspace=ws_dense)
-        sfi.select_topk(ly["scores"], ly["lens"], k=k_sel, n_sink=n_sink, n_recent=n_recent, sel_idx=ly["sel"])
-        sfi.sparse_decode_indexed_attn_merge(ly["q1"], ly["k"], ly["v"], ly["bt"], ly["lens"], ly["sel"],
-                                             n_sink=n_sink, n_recent=n_recent, max_seq_len=max_len,
-                                             slow_out=ly["out"], slow_lse=ly["lse"], slow_workspace=ws_dense,
-                                             compact_k=ly["ck"], compact_v=ly["cv"], n_compact=ly["nc"],
-                                             out=ly["fout"], lse=ly["flse"], workspace=ws_sparse)
-
-    torch.cuda.synchronize()
-    eager = layers[0]["fout"].clone()
-    layers[0]["fout"].zero_()
-    graphs = []
-    side.wait_stream(torch.cuda.current_stream(dev))
-    for ly in layers:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            run(ly)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    matches = bool(torch.equal(layers[0]["fout"], eager))
-    for i in range(2 * R):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        graphs[i % R].replay()
-    t1.record()
-    t1.synchronize()
-    step_s = t0.elapsed_time(t1) * 1e-3 / steps
-    res = {"ms_per_step": round(step_s * 1e3, 5), "value": round(step_bytes / step_s / 1e9, 2),
-           "pct_hbm_peak": round(100 * step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 2),
-           "replay_matches_eager": matches}
-    log(f"graph step {res}")
-    return res
-
-
 def specmix(sfi, dev):
     """4 drafting requests (fast step, 5 % retention) + 4 verifying requests (8 draft tokens, dense causal,
     with statistics) at KV length 131072, 32 query / 8 KV heads: one mixed launch vs the two separate calls."""
@@ -1093,37 +1010,6 @@ def specmix(sfi, dev):
            "mfma_TFLOPs": round(flops / t_m / 1e12, 2), "mfma_pct_bf16_peak": round(100 * flops / t_m / 2.5e15, 2)}
     log(f"specmix {res}")
     return res
-
-
-def cpu_baseline(budget_s, L, B, frac, n_sink, n_recent, step_bytes):
-    """The fp64 oracle timed on host cores on the same workload (one request, all 8 KV heads), one thread."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    import oracle as O
-    from sfi_synth import qwen06b_decode_case
-    c = qwen06b_decode_case(1000, L=L, B=B, frac=frac)
-    t_start = time.perf_counter()
-    n = 0
-    with threadpool_limits(limits=1):
-        while True:
-            b = 0
-            Qv = c.q_values()[b]
-            O.dense_attention(Qv, c.kv.k, c.kv.v, c.kv.block_table[b], L, c.scale, c.Hkv, kv_dtype="bf16")
-            S = O.group_scores(Qv, c.kv.k, c.kv.block_table[b], L, c.scale, c.Hkv, n_sink, n_recent, L,
-                               kv_dtype="bf16")
-            lo, hi = O.candidate_range(L, 1, n_sink, n_recent)
-            sel = np.stack([O.select_topk(S[g].astype(np.float32), lo, hi, c.k_sel) for g in range(c.Hkv)])
-            ck, cv, nc = O.pack_compact(c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, sel, n_sink + c.k_sel)
-            O.sparse_decode(Qv[0], ck, cv, nc, c.kv.k, c.kv.v, c.kv.block_table[b], L, n_sink, n_recent, c.scale,
-                            kv_dtype="bf16")
-            n += 1
-            if time.perf_counter() - t_start >= budget_s:
-                break
-    dt = (time.perf_counter() - t_start) / n
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full steps of the same 16K layer (slow step + Selector + pack + fast step, "
-                      f"1 request x 8 KV heads), fp64 NumPy, one thread; {dt:.2f} s per step",
-            "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -408,6 +408,14 @@ SFI_API sfi_status sfi_plan_splits(int32_t op, const sfi_shape* shape, const sfi
  */
 SFI_API sfi_status sfi_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * Measurement helper, not part of the decode path: reads `bytes` bytes (a multiple
+ * of 16) of device memory at src once, in address order, and writes nothing but (in
+ * practice never) one word at sink (device, 4 bytes).  Its rate is the streaming HBM
+ * read rate the decode kernels are compared against.
+ */
+SFI_API sfi_status sfi_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 SFI_API const char* sfi_status_string(sfi_status status);
 SFI_API const char* sfi_last_error(void);
 SFI_API int32_t sfi_version(void);

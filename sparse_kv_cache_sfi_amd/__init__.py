@@ -26,7 +26,7 @@ __all__ = [
     "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats",
     "select_topk", "pack_compact", "dense_attn_with_stats_deferred", "pack_compact_merge",
     "sparse_decode_indexed_attn_merge",
-    "sparse_decode_attn", "sparse_decode_attn_static", "mixed_attn", "plan_splits", "stream_copy", "workspace_size",
+    "sparse_decode_attn", "sparse_decode_attn_static", "mixed_attn", "plan_splits", "stream_copy", "stream_read", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
 ]
 
@@ -91,6 +91,7 @@ _SIGS = {
                                       POINTER(c_size_t)],
     "sfi_plan_splits": [c_int32, _SHAPE_P, _KV_P, c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)],
     "sfi_stream_copy": [c_void_p, c_void_p, c_size_t, c_void_p],
+    "sfi_stream_read": [c_void_p, c_size_t, c_void_p, c_void_p],
     "sfi_status_string": [c_int32],
     "sfi_last_error": [],
     "sfi_version": [],
@@ -769,3 +770,11 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     _dev(dst, "dst")
     n = min(_nbytes(src), _nbytes(dst))
     _call("sfi_stream_copy", src.data_ptr(), dst.data_ptr(), n, _stream(stream, src.device))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Streaming read of src (measurement helper, not part of the decode path); sink is a device
+    int32 tensor of at least one element."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    _call("sfi_stream_read", src.data_ptr(), _nbytes(src) // 16 * 16, sink.data_ptr(), _stream(stream, src.device))

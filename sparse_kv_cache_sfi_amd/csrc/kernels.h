@@ -120,5 +120,6 @@ struct PackArgs;
 hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int dtype, int d, int G,
                             int B, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace sfi

@@ -721,6 +721,14 @@ sfi_status sfi_stream_copy(const void* src, void* dst, size_t bytes, void* strea
   return hip_status(sfi::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy launch");
 }
 
+sfi_status sfi_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  SFI_TRY(check_ptr16(src, "src"));
+  if (!sink) return fail(SFI_ERR_INVALID_ARG, "sink is NULL");
+  if (bytes % 16) return fail(SFI_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  return hip_status(sfi::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)),
+                    "read launch");
+}
+
 const char* sfi_status_string(sfi_status status) {
   switch (status) {
     case SFI_OK: return "SFI_OK";
