@@ -908,26 +908,40 @@ def refresh_overlap(sfi, dev):
                      n_compact=nc)
     torch.cuda.synchronize()
 
+    # every call marshalled once per stream (the host cost of a launch is then the C call alone)
+    streams = {"main": main_s, "aux": aux_s}
+    ws_sel = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    bound = {}
+    for sname, st in streams.items():
+        bound["slow", sname] = sfi.bind(sfi.dense_attn_with_stats, q, k, v, bt, lens, max_seq_len=L, n_sink=4,
+                                        n_recent=256, out=outs[0], lse=lses[0], scores=scores, workspace=ws_a,
+                                        stream=st)
+        bound["select", sname] = sfi.bind(sfi.select_topk, scores, lens, k=2048, n_sink=4, n_recent=256,
+                                          sel_idx=sel, workspace=ws_sel, stream=st)
+        bound["pack", sname] = sfi.bind(sfi.pack_compact, k, v, bt, lens, sel, n_sink=4, cap=cap, max_seq_len=L,
+                                        compact_k=ck, compact_v=cv, n_compact=nc, stream=st)
+        bound["dense", sname] = sfi.bind(sfi.dense_attn_with_stats, q, k, v, bt, lens, max_seq_len=L,
+                                         with_scores=False, out=outs[1], lse=lses[1], workspace=ws_b, stream=st)
+        bound["fast", sname] = sfi.bind(sfi.sparse_decode_attn, q1, k, v, bt, lens, ck, cv, nc, n_sink=4,
+                                        n_recent=256, max_seq_len=L, out=fo, lse=fl, workspace=ws_f, stream=st)
+    name_of = {id(st): sname for sname, st in streams.items()}
+
     def slow(stream):
-        sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, n_sink=4, n_recent=256, out=outs[0],
-                                  lse=lses[0], scores=scores, workspace=ws_a, stream=stream)
+        bound["slow", name_of[id(stream)]]()
 
     def select(stream):
-        sfi.select_topk(scores, lens, k=2048, n_sink=4, n_recent=256, sel_idx=sel, stream=stream)
+        bound["select", name_of[id(stream)]]()
 
     def pack(stream):
-        sfi.pack_compact(k, v, bt, lens, sel, n_sink=4, cap=cap, max_seq_len=L, compact_k=ck, compact_v=cv,
-                         n_compact=nc, stream=stream)
+        bound["pack", name_of[id(stream)]]()
 
     def partner(kind, stream):
-        if kind == "dense":
-            sfi.dense_attn_with_stats(q, k, v, bt, lens, max_seq_len=L, with_scores=False, out=outs[1],
-                                      lse=lses[1], workspace=ws_b, stream=stream)
-        else:
-            sfi.sparse_decode_attn(q1, k, v, bt, lens, ck, cv, nc, n_sink=4, n_recent=256, max_seq_len=L,
-                                   out=fo, lse=fl, workspace=ws_f, stream=stream)
+        bound[kind, name_of[id(stream)]]()
 
-    n = 20
+    n = 40
+    for fn in (slow, select, pack):        # first launches (code loading) outside the timed loops
+        fn(main_s)
+    torch.cuda.synchronize()
     res = {"requests": B, "kv_len": L, "top_k": 2048, "launches": n}
     res["slow_us"] = round(time_loop(lambda i: slow(main_s), n, main_s) * 1e6, 2)
     t_sel = time_loop(lambda i: select(main_s), n, main_s)

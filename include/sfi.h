@@ -142,7 +142,13 @@ SFI_API sfi_status sfi_dense_attn_workspace_size(const sfi_shape* shape, const s
  *  scores   [B, Hkv, score_stride] float32 (only candidate positions are read)
  *  sel_idx  [B, Hkv, k] int32: the chosen positions ascending, then -1.
  *  t_q, n_sink, n_recent define the candidate set as above.
- *  workspace: at least sfi_select_topk_workspace_size() bytes.
+ *  workspace: at least sfi_select_topk_workspace_size() bytes (no zero-fill needed;
+ *           NULL when that is 0).  Rows of at least 32768 possible candidates
+ *           (score_stride - n_sink) whose k is small enough are cut into up to 16
+ *           segments: one launch selects each segment's own top-k into the workspace,
+ *           a second selects the row's top-k among those candidates (exact: a key in
+ *           the row's top-k is in its segment's).  Other rows need no workspace.
+ *  Errors: SFI_ERR_WORKSPACE when the workspace is smaller than required.
  */
 SFI_API sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_heads,
                            int64_t score_stride, const int32_t* seq_lens, int32_t t_q,
@@ -150,7 +156,8 @@ SFI_API sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t n
                            void* workspace, size_t workspace_bytes, void* stream);
 
 SFI_API sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads,
-                                          int64_t score_stride, int32_t k, size_t* bytes);
+                                          int64_t score_stride, int32_t n_sink, int32_t k,
+                                          size_t* bytes);
 
 /*
  * Cache reorganisation: gather-pack sink and selected tokens into the compact

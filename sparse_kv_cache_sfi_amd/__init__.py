@@ -60,7 +60,7 @@ _SIGS = {
     "sfi_dense_attn_workspace_size": [_SHAPE_P, _KV_P, c_int32, POINTER(c_size_t)],
     "sfi_select_topk": [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32, c_int32, c_int32, c_int32,
                         c_void_p, c_void_p, c_size_t, c_void_p],
-    "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, POINTER(c_size_t)],
+    "sfi_select_topk_workspace_size": [c_int32, c_int32, c_int64, c_int32, c_int32, POINTER(c_size_t)],
     "sfi_dense_attn_with_stats_deferred": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                            c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p],
     "sfi_sparse_decode_indexed_attn_merge": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
@@ -240,18 +240,20 @@ def _i32(t: torch.Tensor, name: str) -> None:
         raise TypeError(f"{name} must be int32")
 
 
-def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device, stream=None) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device, stream=None,
+               zero: bool = True) -> Optional[torch.Tensor]:
     if workspace is not None:
         _dev(workspace, "workspace")
         return workspace
     if nbytes == 0:
         return None
-    # Zero-filled: the split-K arrival counters at its start must read zero on first use.  The
-    # fill runs on the stream the call is made on, and the allocator is told that stream uses
-    # the block, so neither the fill nor a reuse of the block can overtake the launch.
+    # Zero-filled (unless the call needs no zeros): the split-K arrival counters at its start
+    # must read zero on first use.  The fill runs on the stream the call is made on, and the
+    # allocator is told that stream uses the block, so neither the fill nor a reuse of the
+    # block can overtake the launch.
     s = stream if stream is not None else torch.cuda.current_stream(device)
     with torch.cuda.stream(s):
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = (torch.zeros if zero else torch.empty)(nbytes, dtype=torch.uint8, device=device)
     ws.record_stream(s)
     if _binding is not None:
         _binding["keep"].append(ws)
@@ -368,15 +370,19 @@ def dense_attn_with_stats_deferred(q: torch.Tensor, k_pool: torch.Tensor, v_pool
 
 
 def select_topk(scores: torch.Tensor, seq_lens: torch.Tensor, *, k: int, n_sink: int, n_recent: int,
-                t_q: int = 1, sel_idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                t_q: int = 1, sel_idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
     """Selector: scores [B, Hkv, stride] fp32 -> sel_idx [B, Hkv, k] int32 (ascending, -1 padded)."""
     _dev(scores, "scores")
     _i32(seq_lens, "seq_lens")
     B, Hkv, stride = scores.shape
     if sel_idx is None:
         sel_idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=scores.device)
+    need = c_size_t(0)
+    _call("sfi_select_topk_workspace_size", B, Hkv, stride, n_sink, k, ctypes.byref(need))
+    ws = _workspace(need.value, workspace, scores.device, stream, zero=False)   # candidates: no zeros needed
     _call("sfi_select_topk", scores.data_ptr(), B, Hkv, stride, seq_lens.data_ptr(), t_q, n_sink, n_recent, k,
-          sel_idx.data_ptr(), None, 0, _stream(stream, scores.device))
+          sel_idx.data_ptr(), _ptr(ws), _nbytes(ws), _stream(stream, scores.device))
     return sel_idx
 
 

@@ -105,9 +105,12 @@ hipError_t launch_decode(const AttnArgs& a, int dtype, int d, int G, bool sparse
                          hipStream_t stream);
 hipError_t launch_verify(const AttnArgs& a, int d, int G, int B, hipStream_t stream);
 hipError_t launch_mixed(const AttnArgs& a, const MixedPlan& plan, int d, int G, hipStream_t stream);
+// ws: the candidate buffer of long rows (select_workspace_bytes bytes; may be NULL when
+// that is 0, and then rows run on one work-group each).
 hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, const int32_t* seq_lens,
-                         int t_q, int n_sink, int n_recent, int k, int32_t* sel,
+                         int t_q, int n_sink, int n_recent, int k, int32_t* sel, void* ws,
                          hipStream_t stream);
+size_t select_workspace_bytes(int B, int Hkv, int64_t stride, int n_sink, int k);
 // merge (nullable): a slow step's split partials for the launch to combine into
 // out / lse as well (head dim d), one extra work-group per (request, KV head).
 hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,

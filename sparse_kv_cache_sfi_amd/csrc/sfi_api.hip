@@ -405,20 +405,18 @@ sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const sfi_page
                     workspace_bytes, stream);
 }
 
-sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t k,
-                                          size_t* bytes) {
+sfi_status sfi_select_topk_workspace_size(int32_t batch, int32_t num_kv_heads, int64_t score_stride, int32_t n_sink,
+                                          int32_t k, size_t* bytes) {
   if (!bytes) return fail(SFI_ERR_INVALID_ARG, "bytes is NULL");
-  if (batch < 1 || num_kv_heads < 1 || score_stride < 1 || k < 1)
-    return fail(SFI_ERR_INVALID_ARG, "batch, num_kv_heads, score_stride and k must be >= 1");
-  *bytes = 0;
+  if (batch < 1 || num_kv_heads < 1 || score_stride < 1 || k < 1 || n_sink < 0)
+    return fail(SFI_ERR_INVALID_ARG, "batch, num_kv_heads, score_stride and k must be >= 1, n_sink >= 0");
+  *bytes = sfi::select_workspace_bytes(batch, num_kv_heads, score_stride, n_sink, k);
   return ok();
 }
 
 sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_heads, int64_t score_stride,
                            const int32_t* seq_lens, int32_t t_q, int32_t n_sink, int32_t n_recent, int32_t k,
                            int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!scores || !seq_lens || !sel_idx) return fail(SFI_ERR_INVALID_ARG, "scores, seq_lens and sel_idx must be non-NULL");
   if (batch < 1 || num_kv_heads < 1) return fail(SFI_ERR_INVALID_ARG, "batch and num_kv_heads must be >= 1");
   if (score_stride < 1 || score_stride > INT32_MAX)
@@ -426,8 +424,10 @@ sfi_status sfi_select_topk(const float* scores, int32_t batch, int32_t num_kv_he
   if (k < 1) return fail(SFI_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
   if (t_q < 1 || t_q > 16) return fail(SFI_ERR_INVALID_ARG, "t_q must be in [1, 16] (got %d)", t_q);
   SFI_TRY(check_budgets(n_sink, n_recent));
+  const size_t need = sfi::select_workspace_bytes(batch, num_kv_heads, score_stride, n_sink, k);
+  SFI_TRY(check_workspace(workspace, workspace_bytes, need));
   const hipError_t e = sfi::launch_select(scores, batch, num_kv_heads, score_stride, seq_lens, t_q, n_sink, n_recent,
-                                          k, sel_idx, static_cast<hipStream_t>(stream));
+                                          k, sel_idx, need ? workspace : nullptr, static_cast<hipStream_t>(stream));
   return hip_status(e, "select launch");
 }
 

@@ -118,6 +118,26 @@ def test_select_rejects_bad_arguments(lib):
     assert call(stride=0) == 1
     assert call(t_q=0) == 1
     assert call(nr=-3) == 1
+    # long rows need the candidate workspace: 65536 positions, top-2048 -> 8 segments
+    assert call(stride=65536, k=2048) == 3 and "workspace" in lib.sfi_last_error().decode()
+
+
+def test_select_workspace_size_covers_the_segment_candidates(lib):
+    def size(B, H, stride, ns, k):
+        out = ctypes.c_size_t(0)
+        assert lib.sfi_select_topk_workspace_size(B, H, stride, ns, k, ctypes.byref(out)) == 0
+        return out.value
+    # 16K rows run on one work-group each: no workspace
+    assert size(1, 8, 16384, 4, 1980) == 0
+    # the 64K refresh: 4 requests x 8 KV heads, 65532 possible candidates -> 8 segments of
+    # top-2048 candidates, 8 bytes each (key, position)
+    assert size(4, 8, 65536, 4, 2048) == 32 * 8 * 2048 * 8        # keys + positions
+    # k too large for the segments to cut the row at least in half: one work-group per row
+    assert size(4, 8, 65536, 4, 8192) == 0
+    # 1,048,576 positions: 16 segments
+    assert size(1, 1, 1 << 20, 4, 1024) == 16 * 1024 * 8
+    # the candidate rows are padded to a multiple of four: 8 segments x top-2047 = 16376 -> 16376
+    assert size(1, 1, 65536, 4, 2047) == ((8 * 2047 + 3) // 4 * 4) * 8
 
 
 def test_pack_rejects_bad_arguments(lib):

@@ -46,8 +46,17 @@ def test_selector_crafted_ties(gpu_lib, k, n_sink):
     _select_both(gpu_lib, sc, lens, k, n_sink=n_sink, n_recent=5)
 
 
+@pytest.fixture(params=["segments", "one_work_group"])
+def select_path(request, monkeypatch):
+    """Rows of >= 32768 candidates with a small k run over segments; the other value keeps every
+    row on one work-group (tuning override), so both paths see the same rows."""
+    if request.param == "one_work_group":
+        monkeypatch.setenv("SFI_TUNE_SELECT_SEGMENTS", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("k", [1, 33, 2048, 20000])
-def test_selector_large_rows_quantised_scores(gpu_lib, k):
+def test_selector_large_rows_quantised_scores(gpu_lib, k, select_path):
     rng = np.random.default_rng(100 + k)
     B, H, stride = 2, 3, 65536
     sc = (np.round(rng.standard_normal((B, H, stride)) * 8) / 8).astype(np.float32)   # many exact ties
@@ -131,7 +140,7 @@ def test_refresh_64k_select_and_pack_match_oracle_on_sampled_rows(gpu_lib):
 
 
 @pytest.mark.parametrize("k", [7, 5000])
-def test_selector_rows_beyond_the_register_variant(gpu_lib, k):
+def test_selector_rows_beyond_the_register_variant(gpu_lib, k, select_path):
     """Rows longer than 65536 candidates (the verification statistics at 128K) take the streaming kernel."""
     rng = np.random.default_rng(200 + k)
     B, H, stride = 1, 2, 131072
@@ -149,7 +158,7 @@ def _key_to_float(keys):
 @pytest.mark.parametrize("stride,digits", [(4096, [(20, 12), (8, 12)]),
                                            (131072, [(24, 8), (16, 8), (8, 8)])],
                          ids=["register_rows", "streaming_rows"])
-def test_selector_bin_that_holds_exactly_the_wanted_keys(gpu_lib, stride, digits):
+def test_selector_bin_that_holds_exactly_the_wanted_keys(gpu_lib, stride, digits, select_path):
     """A radix pass whose chosen bin holds exactly the keys still wanted settles the selection.
 
     Row h plants, at random positions, a keys in a higher bin of digit level h, m keys in the bin
@@ -177,3 +186,22 @@ def test_selector_bin_that_holds_exactly_the_wanted_keys(gpu_lib, stride, digits
     _select_both(gpu_lib, sc, [stride], a + m, n_sink=n_sink, n_recent=n_recent)
     for k in (1, 17, 300):
         _select_both(gpu_lib, sc, [stride], k, n_sink=n_sink, n_recent=n_recent)
+
+
+@pytest.mark.parametrize("k", [1, 100, 1024, 4095])
+def test_selector_segments_with_ties_across_segment_boundaries(gpu_lib, k):
+    """Long rows cut into segments: equal scores straddling segment boundaries, whole rows of one
+    value, signed zeros and -inf, and ragged lengths that leave trailing segments short or empty.
+    The lowest positions must win every tie, exactly as the one-work-group Selector and the oracle."""
+    rng = np.random.default_rng(300 + k)
+    B, H, stride = 3, 4, 98304                  # 12 segments of 8192 positions
+    vals = np.array([-np.inf, -2.0, -0.0, 0.0, 0.5, 3.0, 3.0, 7.25], dtype=np.float32)
+    sc = rng.choice(vals, size=(B, H, stride)).astype(np.float32)
+    sc[0, 1, :] = 3.0                            # one value everywhere
+    sc[1, 2, :] = -0.0
+    sc[1, 2, ::3] = 0.0                          # signed zeros only
+    seg = 8192
+    for j in range(1, 12):                       # a band of the top value across every boundary
+        sc[2, 3, 4 + j * seg - 40: 4 + j * seg + 40] = 9.5
+    lens = [98304, 70001, 33000]
+    _select_both(gpu_lib, sc, lens, k, n_sink=4, n_recent=64)
