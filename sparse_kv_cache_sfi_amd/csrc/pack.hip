@@ -91,8 +91,10 @@ hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStrea
 }
 
 // ---------------------------------------------------------------------------- streaming read
-// Plain streaming read of n16 16-byte words (each read once, in address order across
-// the grid): the HBM read rate the decode kernels are compared against.  The words are
+// Plain streaming read of n16 16-byte words (each read once; consecutive threads read
+// consecutive words, the grid strides through the buffer one 16-byte load per thread
+// and step, which measured faster than unrolled steps whose loads land in distant
+// regions): the HBM read rate the decode kernels are compared against.  The words are
 // folded into a per-thread xor whose only store is guarded by a condition that never
 // holds for it (a sentinel that the fold of the buffer would have to hit exactly), so
 // the loads stay and the kernel moves read traffic only.
@@ -100,12 +102,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
                                                           uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   uint32_t acc = 0u;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-  }
-  for (; i < n16; i += stride) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
     const u32x4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }

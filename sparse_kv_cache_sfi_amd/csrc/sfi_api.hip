@@ -115,8 +115,9 @@ int64_t tune_env(const char* name, int64_t fallback) {
   return x > 0 ? x : fallback;
 }
 
-Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int max_splits = sfi::kMaxSplits) {
-  const int64_t target = tune_env("SFI_TUNE_TARGET_WGS", 256);
+Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int max_splits = sfi::kMaxSplits,
+                 int64_t target = 0) {
+  if (target <= 0) target = tune_env("SFI_TUNE_TARGET_WGS", 256);
   min_split = tune_env("SFI_TUNE_MIN_SPLIT", min_split);
   if (n_tok <= 0) return {tile, 1};
   const int64_t by_min = (n_tok + min_split - 1) / min_split;
@@ -130,6 +131,11 @@ Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int 
   ns = (n_tok + st - 1) / st;
   return {(int)st, (int)ns};
 }
+
+// Verification work-groups: about two per CU.  A verification work-group keeps one
+// 32-token K/V tile in flight per wave, so the launch needs two of them on a CU to
+// keep enough bytes in flight (one per CU left the HBM idle half the time).
+int64_t verify_target_wgs() { return tune_env("SFI_TUNE_VERIFY_WGS", 512); }
 
 // Dense splits: 256 tokens, 512 once a unit has 8192 or more (the merge of many
 // splits costs more than the parallelism gains).
@@ -154,7 +160,7 @@ size_t partial_bytes(int64_t rows, int n_split, int d) {
 Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
   if (t_q > 1)
     return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kVerifyTile,
-                      dense_min_split(kv->max_seq_len), sfi::kMaxVerifySplits);
+                      dense_min_split(kv->max_seq_len), sfi::kMaxVerifySplits, verify_target_wgs());
   return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kDecodeTile,
                     dense_min_split(kv->max_seq_len));
 }
@@ -242,12 +248,17 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
       return fail(SFI_ERR_UNSUPPORTED, "t_q[%d] * G must be <= %d", b, sfi::kMaxVerifyRows);
     rows += t_q[b];
   }
-  const int64_t units = (int64_t)B * shape->num_kv_heads;
+  // Each kind is planned over its own requests: the verifying ones fill the GPU about
+  // twice over, the drafting ones (a small share of the bytes) take one pass.
+  int n_verify = 0;
+  for (int b = 0; b < B; ++b) n_verify += modes[b] == 1 ? 1 : 0;
+  const int64_t units_v = (int64_t)std::max(n_verify, 1) * shape->num_kv_heads;
+  const int64_t units_d = (int64_t)std::max(B - n_verify, 1) * shape->num_kv_heads;
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
   const int64_t n_tok = (int64_t)cap + rec;
-  const Split sp_d = plan_split(units, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
-  const Split sp_v = plan_split(units, kv->max_seq_len, sfi::kVerifyTile, dense_min_split(kv->max_seq_len),
-                                sfi::kMaxVerifySplits);
+  const Split sp_d = plan_split(units_d, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
+  const Split sp_v = plan_split(units_v, kv->max_seq_len, sfi::kVerifyTile, dense_min_split(kv->max_seq_len),
+                                sfi::kMaxVerifySplits, verify_target_wgs());
   sfi::MixedPlan& p = ms->plan;
   p = sfi::MixedPlan{};
   int q_row0[sfi::kMaxMixedBatch];
