@@ -11,6 +11,8 @@
 // merge fill them instead of running as launches of their own.  Work-groups
 // [0, n_attn) are the attention's split-K units (dispatched first, they start at
 // once), then one merge work-group per (request, KV head), then the pack's blocks.
+// Once the attention's work-groups fill the CUs, the launch has no pack blocks: the
+// attention writes the rows it loads (a.pack_k set) and the merge rides alone.
 #include <algorithm>
 
 #include "decode_unit.h"
@@ -42,16 +44,18 @@ __global__ __launch_bounds__(256) void fast_pack_kernel(AttnArgs a, PackArgs p, 
     }
     bid -= n_units;
   }
+  if (pack_x == 0) return;   // (no pack blocks in the grid then)
   const int bx = bid % pack_x, g = (bid / pack_x) % a.Hkv, b = bid / (pack_x * a.Hkv);
   pack_block<D * (int)sizeof(T), kFastPackRows>(p, bx, g, b);
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_fp_t(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int B,
+static hipError_t launch_fp_t(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, bool pack_blocks, int B,
                               hipStream_t stream) {
   const int64_t units = (int64_t)B * a.Hkv;
   // at least one block per unit: block 0 of KV head 0 writes n_compact
-  const int pack_x = (int)std::max<int64_t>(1, ((int64_t)p.n_sink + p.k + kFastPackRows - 1) / kFastPackRows);
+  const int pack_x =
+      pack_blocks ? (int)std::max<int64_t>(1, ((int64_t)p.n_sink + p.k + kFastPackRows - 1) / kFastPackRows) : 0;
   const int64_t n_wg = (int64_t)a.n_split * units + (merge ? units : 0) + (int64_t)pack_x * units;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   if (merge)
@@ -64,25 +68,25 @@ static hipError_t launch_fp_t(const AttnArgs& a, const PackArgs& p, const AttnAr
 }
 
 template <typename T, int D>
-static hipError_t launch_fp_g(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int G, int B,
-                              hipStream_t stream) {
+static hipError_t launch_fp_g(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, bool pack_blocks, int G,
+                              int B, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_fp_t<T, D, 1>(a, p, merge, B, stream);
-    case 2: return launch_fp_t<T, D, 2>(a, p, merge, B, stream);
-    case 4: return launch_fp_t<T, D, 4>(a, p, merge, B, stream);
-    case 8: return launch_fp_t<T, D, 8>(a, p, merge, B, stream);
+    case 1: return launch_fp_t<T, D, 1>(a, p, merge, pack_blocks, B, stream);
+    case 2: return launch_fp_t<T, D, 2>(a, p, merge, pack_blocks, B, stream);
+    case 4: return launch_fp_t<T, D, 4>(a, p, merge, pack_blocks, B, stream);
+    case 8: return launch_fp_t<T, D, 8>(a, p, merge, pack_blocks, B, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int dtype, int d, int G,
-                            int B, hipStream_t stream) {
+hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, bool pack_blocks, int dtype,
+                            int d, int G, int B, hipStream_t stream) {
   if (dtype == 1) {
-    if (d == 128) return launch_fp_g<uint16_t, 128>(a, p, merge, G, B, stream);
-    if (d == 64) return launch_fp_g<uint16_t, 64>(a, p, merge, G, B, stream);
+    if (d == 128) return launch_fp_g<uint16_t, 128>(a, p, merge, pack_blocks, G, B, stream);
+    if (d == 64) return launch_fp_g<uint16_t, 64>(a, p, merge, pack_blocks, G, B, stream);
   } else {
-    if (d == 128) return launch_fp_g<float, 128>(a, p, merge, G, B, stream);
-    if (d == 64) return launch_fp_g<float, 64>(a, p, merge, G, B, stream);
+    if (d == 128) return launch_fp_g<float, 128>(a, p, merge, pack_blocks, G, B, stream);
+    if (d == 64) return launch_fp_g<float, 64>(a, p, merge, pack_blocks, G, B, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -118,10 +118,12 @@ hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, con
                        const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck,
                        void* cv, int cap, int32_t* n_compact, hipStream_t stream, const AttnArgs* merge = nullptr);
 struct PackArgs;
-// Index-set fast step (a.sel, a.sel_k; no in-place packing) whose launch also packs the
-// compact buffer described by p and, with merge non-NULL, merges a deferred slow step.
-hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, int dtype, int d, int G,
-                            int B, hipStream_t stream);
+// Index-set fast step (a.sel, a.sel_k) whose launch also packs the compact buffer
+// described by p, with pack_blocks in work-groups of its own (a.pack_k NULL), else in
+// the attention's work-groups (a.pack_k set), and, with merge non-NULL, merges a
+// deferred slow step.
+hipError_t launch_fast_pack(const AttnArgs& a, const PackArgs& p, const AttnArgs* merge, bool pack_blocks, int dtype,
+                            int d, int G, int B, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -553,17 +553,30 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (pack_k && head_div == 1 && !k_new) {
-    // The pack (and a deferred slow step's merge) as work-groups of their own in the
-    // attention's launch; the attention reads the selected rows in place.
-    a.pack_k = a.pack_v = nullptr;
-    a.pack_n = nullptr;
+  // Who writes the packed rows.  With fewer attention work-groups than CUs, pack blocks
+  // of their own in the same launch (they read the selected rows a second time, on CUs
+  // the attention leaves idle; at 16K, batch 1, 1/8 retention: 11.7 us against 18.2 us
+  // when the few attention work-groups also write the rows).  Once the attention fills
+  // the CUs, its work-groups write the rows they have loaded (batch 16: 52.4 us against
+  // 80.8 us, which re-read 128 MiB).  A deferred combine rides in both forms.
+  // SFI_TUNE_PACK_IN_ATTN_WGS (environment) moves the threshold for tuning; the results
+  // do not depend on it.
+  if (merge && !(pack_k && head_div == 1 && !k_new))
+    return fail(SFI_ERR_INVALID_ARG, "a deferred combine rides only with packing and no appended token");
+  const bool pack_blocks = pack_k && head_div == 1 && !k_new &&
+                           (int64_t)sp.n * shape->batch * shape->num_kv_heads <
+                               tune_env("SFI_TUNE_PACK_IN_ATTN_WGS", 256);
+  if (pack_blocks || merge) {
+    if (pack_blocks) {
+      a.pack_k = a.pack_v = nullptr;
+      a.pack_n = nullptr;
+    }
     const sfi::PackArgs p{kv->k, kv->v, kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len,
                           shape->num_kv_heads, seq_lens, n_sink, sel, sel_k, pack_k, pack_v, pack_cap, pack_n};
-    const hipError_t e = sfi::launch_fast_pack(a, p, merge, shape->dtype, shape->head_dim, G, shape->batch, st);
+    const hipError_t e =
+        sfi::launch_fast_pack(a, p, merge, pack_blocks, shape->dtype, shape->head_dim, G, shape->batch, st);
     return hip_status(e, "sparse decode + pack launch");
   }
-  if (merge) return fail(SFI_ERR_INVALID_ARG, "a deferred combine rides only with packing and no appended token");
   hipError_t e = sfi::launch_decode(a, shape->dtype, shape->head_dim, G, true, shape->batch, st);
   return hip_status(e, "sparse decode launch");
 }
