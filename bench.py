@@ -418,7 +418,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
     ap.add_argument("--only", default="",
-                    help="comma-separated legs to run alone, printing their figures: headline, append_fast, "
+                    help="comma-separated legs to run alone, printing their figures: headline, selector, append_fast, "
                          "draft_refresh, head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k, "
                          "sweep_b1, sweep_b16, sweep_long")
     args = ap.parse_args()
@@ -460,6 +460,7 @@ def main():
 
     if args.only:
         legs = {"append_fast": lambda: append_fast(sfi, dev, torch.cuda.current_stream(dev)),
+                "selector": lambda: selector(sfi, dev),
                 "draft_refresh": lambda: draft_refresh_c3(sfi, dev),
                 "head_selection": lambda: head_selection(sfi, dev),
                 "refresh_schedule": lambda: refresh_schedule_c3(sfi, dev),
@@ -534,6 +535,35 @@ def main():
 
 
 # --------------------------------------------------------------------------- other legs
+
+def selector(sfi, dev):
+    """The Selector alone on logit rows of the two layer shapes: 16K at batch 1 (8 rows of 16316
+    candidates, k 1980, register path) and 64K at batch 4 (32 rows of 65276 candidates, k 2048,
+    segmented path: one work-group per row segment, then a merge), on 64 replicas of the rows and
+    lengths (the slow step writes the rows just before, so they are not cache-cold in a step)."""
+    import torch
+    res = {}
+    st = torch.cuda.current_stream(dev)
+    for name, B, L, k, n_recent in (("16k_b1", 1, 16384, 1980, 64), ("64k_b4", 4, 65536, 2048, 256)):
+        Hkv, R = 8, 64
+        g = torch.Generator(device=dev)
+        g.manual_seed(7 + L)
+        rows = [torch.randn((B, Hkv, L), generator=g, device=dev) for _ in range(R)]
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        outs = [torch.empty((B, Hkv, k), dtype=torch.int32, device=dev) for _ in range(R)]
+        calls = [sfi.bind(sfi.select_topk, rows[i], lens, k=k, n_sink=4, n_recent=n_recent, sel_idx=outs[i],
+                          stream=st) for i in range(R)]
+        for i in range(2 * R):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        t = time_loop(lambda i: calls[i % R](), 10 * R, st)
+        res[name] = {"rows": B * Hkv, "candidates": L - 4 - n_recent, "k": k, "us": round(t * 1e6, 2),
+                     "row_bytes_GBps": round(B * Hkv * L * 4 / t / 1e9, 1)}
+        del rows, outs, calls
+        torch.cuda.empty_cache()
+    log(f"selector {res}")
+    return res
+
 
 def append_fast(sfi, dev, stream, Hq=16, Hkv=8, d=128, n_sink=4, n_recent=64):
     """Fast step with the decoded token's K/V stored in the same launch
