@@ -179,24 +179,23 @@ SFI_API sfi_status sfi_pack_compact(const sfi_shape* shape, const sfi_paged_kv* 
                             int32_t* n_compact, void* stream);
 
 /*
- * Slow step whose split-K combine runs in the pack launch.  SFI page, Fig. 2
- * caption: the slow step's logits go to the Selector, whose selection is packed
- * into the compact buffer (Fig. 3B); when the three run in order on one stream,
- * the pack launch is the first after the slow step with CUs to spare, and it
- * finishes the slow step there.  sfi_dense_attn_with_stats_deferred computes the
- * slow step (arguments as sfi_dense_attn_with_stats with t_q = 1; scores must be
- * non-NULL; workspace of sfi_dense_attn_workspace_size(shape, kv, 1) bytes) but,
- * when the call is split over more than one work-group per (request, KV head),
- * leaves the split partials in the workspace and writes neither out nor lse.
- * sfi_pack_compact_merge packs exactly as sfi_pack_compact and, in one extra
- * work-group per (request, KV head) of the same launch, merges those partials
- * into out and lse; it must be enqueued after the deferred slow step, on the
- * same stream (or ordered by events), with the same shape, kv, seq_lens, out,
- * lse and workspace, and no other call may use the workspace in between (the
- * Selector, sfi_select_topk, uses none).  Together the calls give out, lse,
- * scores, the selection and the compact buffer bit-identical to
- * sfi_dense_attn_with_stats, sfi_select_topk and sfi_pack_compact.  Until the
- * pack has run, out and lse are undefined.  Errors as the calls they replace;
+ * Slow step whose split-K combine runs in a later launch of the step.  SFI page,
+ * Fig. 2 caption: the slow step's logits go to the Selector, whose selection is
+ * packed into the compact buffer (Fig. 3B) for the fast steps that follow; when
+ * these run in order on one stream, the launch after the Selector (the fast step
+ * over the selection with the pack, sfi_sparse_decode_indexed_attn_merge) has CUs
+ * to spare and finishes the slow step there.  sfi_dense_attn_with_stats_deferred
+ * computes the slow step (arguments as sfi_dense_attn_with_stats with t_q = 1;
+ * scores must be non-NULL; workspace of sfi_dense_attn_workspace_size(shape, kv, 1)
+ * bytes) but, when the call is split over more than one work-group per (request,
+ * KV head), leaves the split partials in the workspace and writes neither out nor
+ * lse.  sfi_sparse_decode_indexed_attn_merge must then be enqueued after it, on
+ * the same stream (or ordered by events), with the same shape, kv, seq_lens, out,
+ * lse and workspace (as slow_out, slow_lse, slow_workspace), and no other call may
+ * use the workspace in between (the Selector, sfi_select_topk, uses none).  out,
+ * lse, scores, the selection and the compact buffer are then bit-identical to
+ * sfi_dense_attn_with_stats, sfi_select_topk and sfi_pack_compact.  Until that
+ * launch has run, out and lse are undefined.  Errors as sfi_dense_attn_with_stats;
  * nothing is launched on any error.
  */
 SFI_API sfi_status sfi_dense_attn_with_stats_deferred(const sfi_shape* shape, const sfi_paged_kv* kv,
@@ -204,12 +203,6 @@ SFI_API sfi_status sfi_dense_attn_with_stats_deferred(const sfi_shape* shape, co
                                               int32_t n_sink, int32_t n_recent, float* out,
                                               float* lse, float* scores, int64_t score_stride,
                                               void* workspace, size_t workspace_bytes, void* stream);
-
-SFI_API sfi_status sfi_pack_compact_merge(const sfi_shape* shape, const sfi_paged_kv* kv,
-                                  const int32_t* seq_lens, int32_t n_sink, const int32_t* sel_idx,
-                                  int32_t k, void* compact_k, void* compact_v, int32_t cap,
-                                  int32_t* n_compact, float* out, float* lse, void* workspace,
-                                  size_t workspace_bytes, void* stream);
 
 /*
  * Fast step: sparse decode attention over the two-segment state.

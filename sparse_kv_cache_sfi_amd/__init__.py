@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "SfiError", "load", "bind", "BoundCall", "dense_attn_with_stats",
-    "select_topk", "pack_compact", "dense_attn_with_stats_deferred", "pack_compact_merge",
+    "select_topk", "pack_compact", "dense_attn_with_stats_deferred",
     "sparse_decode_indexed_attn_merge",
     "sparse_decode_attn", "sparse_decode_attn_static", "mixed_attn", "plan_splits", "stream_copy", "stream_read", "workspace_size",
     "SFI_OK", "SFI_ERR_INVALID_ARG", "SFI_ERR_UNSUPPORTED", "SFI_ERR_WORKSPACE", "SFI_ERR_HIP",
@@ -66,8 +66,6 @@ _SIGS = {
     "sfi_sparse_decode_indexed_attn_merge": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                              c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
-    "sfi_pack_compact_merge": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
-                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "sfi_pack_compact": [_SHAPE_P, _KV_P, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                          c_void_p, c_void_p],
     "sfi_sparse_decode_attn": [_SHAPE_P, _KV_P, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
@@ -336,9 +334,9 @@ def dense_attn_with_stats_deferred(q: torch.Tensor, k_pool: torch.Tensor, v_pool
                                    score_stride: Optional[int] = None, out: Optional[torch.Tensor] = None,
                                    lse: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
                                    workspace: Optional[torch.Tensor] = None, stream=None):
-    """Slow step whose split-K combine is left to pack_compact_merge: q [B, 1, Hq, d] -> (out, lse, scores,
-    workspace).  out and lse are complete only once pack_compact_merge has run with the same out, lse and
-    workspace (pass the returned workspace on)."""
+    """Slow step whose split-K combine is left to sparse_decode_indexed_attn_merge: q [B, 1, Hq, d] ->
+    (out, lse, scores, workspace).  out and lse are complete only once that call has run with them and the
+    returned workspace as slow_out, slow_lse and slow_workspace."""
     _dev(q, "q")
     _i32(seq_lens, "seq_lens")
     if q.dim() != 4 or q.shape[1] != 1:
@@ -418,49 +416,6 @@ def pack_compact(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.
     _call("sfi_pack_compact", ctypes.byref(shape), ctypes.byref(kv), seq_lens.data_ptr(), n_sink,
           sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
           _stream(stream, dev))
-    return compact_k, compact_v, n_compact
-
-
-def pack_compact_merge(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
-                       seq_lens: torch.Tensor, sel_idx: torch.Tensor, *, n_sink: int, cap: int, max_seq_len: int,
-                       out: torch.Tensor, lse: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
-                       scale: Optional[float] = None, compact_k: Optional[torch.Tensor] = None,
-                       compact_v: Optional[torch.Tensor] = None, n_compact: Optional[torch.Tensor] = None,
-                       stream=None):
-    """Gather-pack that also merges the split partials a dense_attn_with_stats_deferred call left in
-    workspace into its out [B, 1, Hq, d] and lse [B, 1, Hq]: -> (compact_k, compact_v, n_compact)."""
-    _i32(sel_idx, "sel_idx")
-    _i32(seq_lens, "seq_lens")
-    _dev(out, "out")
-    if sel_idx.dim() != 3 or out.dim() != 4 or out.shape[1] != 1:
-        raise ValueError("sel_idx must be [B, Hkv, k] and out [B, 1, Hq, d]")
-    B, Hkv, k = sel_idx.shape
-    Hq, d = out.shape[2], out.shape[3]
-    kv = _kv(k_pool, v_pool, block_table, max_seq_len)
-    if _check_pool(k_pool, v_pool, block_table, B, d) != Hkv:
-        raise ValueError(f"sel_idx has {Hkv} rows per request; the pools hold {k_pool.shape[1]} KV heads")
-    _f32_out(out, (B, 1, Hq, d), "out")
-    _f32_out(lse, (B, 1, Hq), "lse")
-    if workspace is not None:
-        _dev(workspace, "workspace")
-    shape = _shape(B, Hq, Hkv, d, _dtype_code(k_pool), scale)
-    dev = k_pool.device
-    if compact_k is None:
-        compact_k = torch.empty((B, Hkv, cap, d), dtype=k_pool.dtype, device=dev)
-    if compact_v is None:
-        compact_v = torch.empty((B, Hkv, cap, d), dtype=k_pool.dtype, device=dev)
-    if n_compact is None:
-        n_compact = torch.empty((B,), dtype=torch.int32, device=dev)
-    for t, n in ((compact_k, "compact_k"), (compact_v, "compact_v")):
-        _dev(t, n)
-        if t.dtype != k_pool.dtype or tuple(t.shape) != (B, Hkv, cap, d):
-            raise ValueError(f"{n} must be [B, Hkv, cap, d] = {(B, Hkv, cap, d)} in the pool dtype")
-    _i32(n_compact, "n_compact")
-    if tuple(seq_lens.shape) != (B,) or tuple(n_compact.shape) != (B,):
-        raise ValueError("seq_lens and n_compact must be [B]")
-    _call("sfi_pack_compact_merge", ctypes.byref(shape), ctypes.byref(kv), seq_lens.data_ptr(), n_sink,
-          sel_idx.data_ptr(), k, compact_k.data_ptr(), compact_v.data_ptr(), cap, n_compact.data_ptr(),
-          out.data_ptr(), _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream, dev))
     return compact_k, compact_v, n_compact
 
 

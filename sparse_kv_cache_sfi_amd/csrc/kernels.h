@@ -111,12 +111,10 @@ hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, co
                          int t_q, int n_sink, int n_recent, int k, int32_t* sel, void* ws,
                          hipStream_t stream);
 size_t select_workspace_bytes(int B, int Hkv, int64_t stride, int n_sink, int k);
-// merge (nullable): a slow step's split partials for the launch to combine into
-// out / lse as well (head dim d), one extra work-group per (request, KV head).
 hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_pages, int num_pages, int max_seq_len,
                        const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck,
-                       void* cv, int cap, int32_t* n_compact, hipStream_t stream, const AttnArgs* merge = nullptr);
+                       void* cv, int cap, int32_t* n_compact, hipStream_t stream);
 struct PackArgs;
 // Index-set fast step (a.sel, a.sel_k) whose launch also packs the compact buffer
 // described by p, with pack_blocks in work-groups of its own (a.pack_k NULL), else in

@@ -9,65 +9,37 @@
 // or behind an invalid block-table entry, produce zero rows; negative entries
 // of sel_idx (padding) produce no row.
 //
-// With MD = d > 0 the launch also finishes a slow step whose kernel left its split-K
-// partials behind (SFI page, Fig. 2: the slow step feeds the Selector, which feeds this
-// reorganisation; on one stream this launch is the first with spare CUs after the
-// slow step): the first work-group of every (request b, KV head g) merges the partials
-// of query heads g G ... g G + G - 1 of request b into out and lse with the slow step's
-// own merge code, while the other work-groups copy rows.
 #include "common.h"
 #include "kernels.h"
 #include "pack_unit.h"
-#include "split_tail.h"
 
 namespace sfi {
 
-// Query heads per KV head, at most (the merge's LDS is sized for it).
-constexpr int kPackMergeRows = 8;
-
-template <int ROW_BYTES, int RPB, int MD>
-__global__ __launch_bounds__(256) void pack_kernel(PackArgs p, AttnArgs m) {
-  const int b = blockIdx.z, g = blockIdx.y;
-  if constexpr (MD > 0) {
-    if (blockIdx.x == 0) {
-      __shared__ float tail[SplitTail<MD>::bytes(kPackMergeRows, kMaxSplits) / 4];
-      const int G = m.Hq / m.Hkv;
-      SplitTail<MD>::merge(m, g, b, G, G, kMaxSplits, tail);
-      return;
-    }
-  }
-  pack_block<ROW_BYTES, RPB>(p, blockIdx.x - (MD > 0 ? 1 : 0), g, b);
+template <int ROW_BYTES, int RPB>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
+  pack_block<ROW_BYTES, RPB>(p, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 hipError_t launch_pack(int dtype, int d, int B, int Hkv, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, int max_pages, int num_pages, int max_seq_len,
                        const int32_t* seq_lens, int n_sink, const int32_t* sel, int k, void* ck, void* cv,
-                       int cap, int32_t* n_compact, hipStream_t stream, const AttnArgs* merge) {
+                       int cap, int32_t* n_compact, hipStream_t stream) {
   PackArgs p{k_pool, v_pool, block_table, max_pages, num_pages, max_seq_len, Hkv, seq_lens,
              n_sink, sel, k, ck, cv, cap, n_compact};
   const int64_t rows = (int64_t)n_sink + k;
   const bool small = (int64_t)B * Hkv * ((rows + 15) / 16) <= kPackSmallGrid;
   const int rpb = small ? 16 : 32;
-  const int md = merge ? d : 0;
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb + (md ? 1 : 0)), Hkv, B), block(256);
-  const AttnArgs m = merge ? *merge : AttnArgs{};
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb), Hkv, B), block(256);
   const int row_bytes = d * (dtype == 1 ? 2 : 4);
-#define SFI_PACK(RB, RPB_)                                                                            \
-  do {                                                                                                \
-    if (md == 128) hipLaunchKernelGGL((pack_kernel<RB, RPB_, 128>), grid, block, 0, stream, p, m);    \
-    else if (md == 64) hipLaunchKernelGGL((pack_kernel<RB, RPB_, 64>), grid, block, 0, stream, p, m); \
-    else hipLaunchKernelGGL((pack_kernel<RB, RPB_, 0>), grid, block, 0, stream, p, m);                \
-  } while (0)
   switch (row_bytes * (small ? 1 : -1)) {
-    case 128: SFI_PACK(128, 16); break;
-    case 256: SFI_PACK(256, 16); break;
-    case 512: SFI_PACK(512, 16); break;
-    case -128: SFI_PACK(128, 32); break;
-    case -256: SFI_PACK(256, 32); break;
-    case -512: SFI_PACK(512, 32); break;
+    case 128: hipLaunchKernelGGL((pack_kernel<128, 16>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((pack_kernel<256, 16>), grid, block, 0, stream, p); break;
+    case 512: hipLaunchKernelGGL((pack_kernel<512, 16>), grid, block, 0, stream, p); break;
+    case -128: hipLaunchKernelGGL((pack_kernel<128, 32>), grid, block, 0, stream, p); break;
+    case -256: hipLaunchKernelGGL((pack_kernel<256, 32>), grid, block, 0, stream, p); break;
+    case -512: hipLaunchKernelGGL((pack_kernel<512, 32>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
-#undef SFI_PACK
   return hipGetLastError();
 }
 

@@ -369,7 +369,7 @@ sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void
 
 sfi_status pack_call(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens, int32_t n_sink,
                      const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v, int32_t cap,
-                     int32_t* n_compact, void* stream, const sfi::AttnArgs* merge = nullptr) {
+                     int32_t* n_compact, void* stream) {
   SFI_TRY(check_shape(shape));
   SFI_TRY(check_kv(kv));
   if (!seq_lens || !sel_idx || !n_compact) return fail(SFI_ERR_INVALID_ARG, "seq_lens, sel_idx and n_compact must be non-NULL");
@@ -382,7 +382,7 @@ sfi_status pack_call(const sfi_shape* shape, const sfi_paged_kv* kv, const int32
   const hipError_t e = sfi::launch_pack(shape->dtype, shape->head_dim, shape->batch, shape->num_kv_heads, kv->k, kv->v,
                                         kv->block_table, kv->max_pages, kv->num_pages, kv->max_seq_len, seq_lens,
                                         n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact,
-                                        static_cast<hipStream_t>(stream), merge);
+                                        static_cast<hipStream_t>(stream));
   return hip_status(e, "pack launch");
 }
 
@@ -447,30 +447,6 @@ sfi_status sfi_pack_compact(const sfi_shape* shape, const sfi_paged_kv* kv, cons
                             const int32_t* sel_idx, int32_t k, void* compact_k, void* compact_v, int32_t cap,
                             int32_t* n_compact, void* stream) {
   return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream);
-}
-
-sfi_status sfi_pack_compact_merge(const sfi_shape* shape, const sfi_paged_kv* kv, const int32_t* seq_lens,
-                                  int32_t n_sink, const int32_t* sel_idx, int32_t k, void* compact_k,
-                                  void* compact_v, int32_t cap, int32_t* n_compact, float* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  SFI_TRY(check_shape(shape));
-  SFI_TRY(check_kv(kv));
-  SFI_TRY(check_ptr16(out, "out"));
-  // The partials are laid out as the deferred slow step of the same shape left them.
-  const Split sp = plan_dense(shape, kv, 1);
-  const int64_t rows = (int64_t)shape->batch * shape->num_q_heads;
-  SFI_TRY(check_unit_span(shape, 1, sp.n));
-  SFI_TRY(check_workspace(workspace, workspace_bytes, partial_bytes(rows, sp.n, shape->head_dim)));
-  if (sp.n <= 1)   // the slow step wrote out and lse itself
-    return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream);
-  sfi::AttnArgs m = base_args(shape, kv, seq_lens);
-  m.n_split = sp.n;
-  m.split_tokens = sp.tokens;
-  m.t_q = 1;
-  m.out = out;
-  m.lse = lse;
-  set_partials(m, workspace, rows, shape->head_dim);
-  return pack_call(shape, kv, seq_lens, n_sink, sel_idx, k, compact_k, compact_v, cap, n_compact, stream, &m);
 }
 
 sfi_status sfi_sparse_decode_workspace_size(const sfi_shape* shape, const sfi_paged_kv* kv, int32_t cap,

@@ -40,10 +40,12 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
-def test_in_launch_maintenance_entry_point_is_gone(lib):
+def test_removed_entry_points_are_gone(lib):
     # the slow step that carried the previous layer's Selector and pack as extra
-    # work-groups measured slower than running them serially; it was removed
+    # work-groups measured slower than running them serially; the pack that merged a
+    # deferred slow step is superseded by the fused fast step + pack launch
     assert not hasattr(lib, "sfi_dense_attn_with_refresh")
+    assert not hasattr(lib, "sfi_pack_compact_merge")
 
 
 def test_version_and_status_strings(lib):
@@ -265,7 +267,7 @@ def test_binding_refuses_host_tensors():
         sfi.select_topk(torch.zeros((1, 1, 8)), torch.zeros(1, dtype=torch.int32), k=2, n_sink=0, n_recent=0)
 
 
-def test_deferred_slow_step_and_selector_merge_reject_bad_arguments(lib):
+def test_deferred_slow_step_rejects_bad_arguments(lib):
     shape, kv = _shape(), _kv()
 
     def dense(scores=FAKE, q=FAKE, ws_bytes=1 << 40):
@@ -276,16 +278,6 @@ def test_deferred_slow_step_and_selector_merge_reject_bad_arguments(lib):
     assert dense(q=MISALIGNED) == 1
     assert dense(ws_bytes=10) == 3
 
-    def merge(shape_=shape, sel=FAKE, out=FAKE, cap=200, k=100, ws_bytes=1 << 40):
-        return lib.sfi_pack_compact_merge(ctypes.byref(shape_), ctypes.byref(kv), FAKE, 4, sel, k, FAKE, FAKE, cap,
-                                          FAKE, out, FAKE, FAKE, ws_bytes, None)
-
-    assert merge(sel=0) == 1
-    assert merge(out=0) == 1
-    assert merge(cap=50) == 1 and "cap" in lib.sfi_last_error().decode()
-    assert merge(k=0) == 1 and "k must be" in lib.sfi_last_error().decode()
-    assert merge(ws_bytes=10) == 3
-    assert merge(shape_=_shape(d=96)) == 2
 
 
 def test_indexed_fast_step_with_pack_and_combine_rejects_bad_arguments(lib):

@@ -1,13 +1,15 @@
-"""GPU parity of the slow step whose split-K combine runs in the pack launch.
+"""GPU parity of the slow step whose split-K combine runs in a later launch.
 
 sfi_dense_attn_with_stats_deferred leaves the slow step's split partials in the
-workspace; after the Selector, sfi_pack_compact_merge packs and merges them into
-out and lse.  The three calls must give out, lse, scores, sel_idx and the compact
-buffer bit-identical to sfi_dense_attn_with_stats, sfi_select_topk and
-sfi_pack_compact (which the other parity files check against the oracle); the
-16K layer is also checked against the fp64 oracle directly.  Cases cover one and
-many splits, query groups of 1, 2, 4 and 8, fp32 and bf16, d 64 and 128, requests
-with fewer candidates than k, and long rows.
+workspace; after the Selector, sfi_sparse_decode_indexed_attn_merge (the fast step
+over the selection, read in place) packs the compact buffer and merges the partials
+into out and lse in the same launch.  The three calls must give out, lse, scores,
+sel_idx and the compact buffer bit-identical to sfi_dense_attn_with_stats,
+sfi_select_topk and sfi_pack_compact (which the other parity files check against
+the oracle); the 16K layer is also checked against the fp64 oracle directly.  Cases
+cover one and many splits, query groups of 1, 2, 4 and 8, fp32 and bf16, d 64 and
+128, requests with fewer candidates than k, long rows, and both forms of the
+launch's pack (blocks of their own, rows written by the attention).
 """
 import numpy as np
 import pytest
@@ -38,14 +40,17 @@ def _zero_compact(dc, cap):
 
 
 def _pair(sfi, dc, n_sink, n_recent, k, workspace=None):
+    """Deferred slow step, Selector, then the launch that packs and finishes the slow step."""
     out, lse, sc, ws = sfi.dense_attn_with_stats_deferred(dc.q, dc.k, dc.v, dc.bt, dc.lens,
                                                           max_seq_len=dc.max_seq_len, n_sink=n_sink,
                                                           n_recent=n_recent, workspace=workspace)
     sel = sfi.select_topk(sc, dc.lens, k=k, n_sink=n_sink, n_recent=n_recent)
     ck, cv = _zero_compact(dc, n_sink + k)
-    ck, cv, nc = sfi.pack_compact_merge(dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=n_sink, cap=n_sink + k,
-                                        max_seq_len=dc.max_seq_len, out=out, lse=lse, workspace=ws,
-                                        compact_k=ck, compact_v=cv)
+    nc = torch.empty((dc.q.shape[0],), dtype=torch.int32, device=DEV)
+    sfi.sparse_decode_indexed_attn_merge(dc.q[:, -1].contiguous(), dc.k, dc.v, dc.bt, dc.lens, sel, n_sink=n_sink,
+                                         n_recent=n_recent, max_seq_len=dc.max_seq_len, slow_out=out,
+                                         slow_lse=lse, slow_workspace=ws, compact_k=ck, compact_v=cv,
+                                         n_compact=nc)
     return out, lse, sc, sel, ck, cv, nc
 
 
