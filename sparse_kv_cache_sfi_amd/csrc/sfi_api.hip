@@ -529,19 +529,22 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
   set_partials(a, workspace, rows, shape->head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  // Who writes the packed rows.  With fewer attention work-groups than CUs, pack blocks
-  // of their own in the same launch (they read the selected rows a second time, on CUs
-  // the attention leaves idle; at 16K, batch 1, 1/8 retention: 11.7 us against 18.2 us
-  // when the few attention work-groups also write the rows).  Once the attention fills
-  // the CUs, its work-groups write the rows they have loaded (batch 16: 52.4 us against
-  // 80.8 us, which re-read 128 MiB).  A deferred combine rides in both forms.
-  // SFI_TUNE_PACK_IN_ATTN_WGS (environment) moves the threshold for tuning; the results
-  // do not depend on it.
+  // Who writes the packed rows.  Pack blocks of their own in the same launch read the
+  // selected rows a second time, on CUs the attention leaves idle; the attention's
+  // work-groups can instead write the rows they have just loaded, which saves those
+  // reads but lengthens the attention.  The second wins once the rows are many (16K
+  // per request, 8 KV heads, d 128, bf16; pack blocks / rows written by the attention):
+  // 1/8 retention at batch 1 11.7 / 18.2 us, 2: 14.6 / 20.4, 4: 19.0 / 24.3,
+  // 8: 33.8 / 32.5, 16: 82.1 / 52.5; 1/64 retention, any batch up to 16: blocks by
+  // ~1 us.  The switch is at 48 MiB of packed K and V (SFI_TUNE_PACK_IN_ATTN_BYTES,
+  // environment, moves it for tuning; the results do not depend on it).  A deferred
+  // combine rides in both forms.
   if (merge && !(pack_k && head_div == 1 && !k_new))
     return fail(SFI_ERR_INVALID_ARG, "a deferred combine rides only with packing and no appended token");
+  const int64_t packed_bytes = (int64_t)shape->batch * shape->num_kv_heads * cap * 2 * shape->head_dim *
+                               (shape->dtype == SFI_BF16 ? 2 : 4);
   const bool pack_blocks = pack_k && head_div == 1 && !k_new &&
-                           (int64_t)sp.n * shape->batch * shape->num_kv_heads <
-                               tune_env("SFI_TUNE_PACK_IN_ATTN_WGS", 256);
+                           packed_bytes < tune_env("SFI_TUNE_PACK_IN_ATTN_BYTES", 48ll << 20);
   if (pack_blocks || merge) {
     if (pack_blocks) {
       a.pack_k = a.pack_v = nullptr;

@@ -211,17 +211,17 @@ def test_three_launch_step_rejects_shared_workspaces(gpu_lib):
 
 
 def test_pack_in_blocks_or_in_attention_work_groups_agree(gpu_lib, monkeypatch):
-    """The fused launch packs in work-groups of its own (small grids) or in the attention's work-groups
-    (grids that fill the CUs); both forms give all outputs bit for bit, with and without the deferred
-    combine.  SFI_TUNE_PACK_IN_ATTN_WGS forces each form."""
+    """The fused launch packs in work-groups of its own (few packed rows) or in the attention's work-groups
+    (many); both forms give all outputs bit for bit, with and without the deferred combine.
+    SFI_TUNE_PACK_IN_ATTN_BYTES forces each form."""
     sfi = gpu_lib
     c = make_case(628, name="modes", B=4, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[3000, 5000, 700, 4100],
                   n_sink=4, n_recent=64, k_sel=256, hh_per_head=12)
     dc = DevCase(c)
     q1 = dev_array(np.ascontiguousarray(c.q[:, -1]))
     got = {}
-    for thr in ("1", str(1 << 30)):
-        monkeypatch.setenv("SFI_TUNE_PACK_IN_ATTN_WGS", thr)
+    for thr in ("1", str(1 << 60)):
+        monkeypatch.setenv("SFI_TUNE_PACK_IN_ATTN_BYTES", thr)
         three = _three_launch(sfi, dc, q1, c.n_sink, c.n_recent, 256)
         sel = three[3]
         ck, cv = _zero_compact(dc, c.n_sink + 256)
@@ -232,5 +232,5 @@ def test_pack_in_blocks_or_in_attention_work_groups_agree(gpu_lib, monkeypatch):
         torch.cuda.synchronize()
         got[thr] = list(three) + [ck, cv, nc, fo, fl]
     names = list(NAMES) + ["fast_out", "fast_lse", "ck2", "cv2", "nc2", "fo2", "fl2"]
-    for nm, x, y in zip(names, got["1"], got[str(1 << 30)]):
+    for nm, x, y in zip(names, got["1"], got[str(1 << 60)]):
         assert np.array_equal(_bits(x), _bits(y)), f"{nm} differs between the two pack forms"
