@@ -521,6 +521,8 @@ def main():
         result["refresh_schedule"] = refresh_schedule_c3(sfi, dev)
         log("128K speculative mix")
         result["specmix_128k"] = specmix(sfi, dev)
+        log("Selector alone")
+        result["selector"] = selector(sfi, dev)
 
     if not args.no_cpu_baseline:
         log("oracle on the host")
