@@ -903,7 +903,8 @@ def head_selection(sfi, dev, reps=100):
 def refresh_overlap(sfi, dev):
     """Slow-step maintenance hidden behind the next layer (SFI page, Fig. 3A).  Layer i's slow step
     (dense + logits, 4 requests x 64K, 32 query / 8 KV heads) is followed by its Selector (top-2048 per
-    KV head) and pack, and by layer i+1's attention (dense, or a fast step over 2308 tokens).  Serial:
+    KV head) and pack, and by layer i+1's attention (dense, or a fast step over 2308 tokens, or the fast steps
+    of layers i+1 .. i+4, which the maintenance of layer i has until layer i's next fast step).  Serial:
     all on one stream.  Two overlapped schedules: Selector + pack on a second stream while the main
     stream runs layer i+1 ("select_pack_aux"), or the Selector on the main stream and only the pack
     on the second one ("pack_aux").  hidden = (serial - overlapped) / (time of the work moved)."""
@@ -968,7 +969,11 @@ def refresh_overlap(sfi, dev):
         bound["pack", name_of[id(stream)]]()
 
     def partner(kind, stream):
-        bound[kind, name_of[id(stream)]]()
+        if kind == "fast_x4":   # the fast steps of the next four layers (same shapes, same buffers)
+            for _ in range(4):
+                bound["fast", name_of[id(stream)]]()
+        else:
+            bound[kind, name_of[id(stream)]]()
 
     n = 40
     for fn in (slow, select, pack):        # first launches (code loading) outside the timed loops
@@ -979,7 +984,7 @@ def refresh_overlap(sfi, dev):
     t_sel = time_loop(lambda i: select(main_s), n, main_s)
     t_pack = time_loop(lambda i: pack(main_s), n, main_s)
     res["select_us"], res["pack_us"] = round(t_sel * 1e6, 2), round(t_pack * 1e6, 2)
-    for kind in ("dense", "fast"):
+    for kind in ("dense", "fast", "fast_x4"):
         t_p = time_loop(lambda i: partner(kind, main_s), n, main_s)
 
         def serial(i):
