@@ -11,8 +11,9 @@
 // merge fill them instead of running as launches of their own.  Work-groups
 // [0, n_attn) are the attention's split-K units (dispatched first, they start at
 // once), then one merge work-group per (request, KV head), then the pack's blocks.
-// Once the attention's work-groups fill the CUs, the launch has no pack blocks: the
-// attention writes the rows it loads (a.pack_k set) and the merge rides alone.
+// When the packed rows are large (the host chooses by their bytes), the launch has no
+// pack blocks: the attention writes the rows it loads (a.pack_k set), so they are read
+// once, and the merge rides alone.
 #include <algorithm>
 
 #include "decode_unit.h"
