@@ -56,7 +56,7 @@ struct AttnArgs {
   float* part_o;          // split partials [rows * Hq, part_stride, d]
   float* part_ml;         // [rows * Hq, part_stride, 2] = (max in log2 units, sum)
   int32_t part_stride;    // split slots per partial row (>= n_split)
-  int32_t* counters;      // [B * Hkv] split arrival counters (zero between calls)
+  int32_t* counters;      // kMaxCounters split arrival counters (zero between calls; unit_counter)
   float* scores;          // [B, Hkv, score_stride] (nullable)
   int64_t score_stride;
   // Fast step with append: request b's token at position L_b - 1 arrives here

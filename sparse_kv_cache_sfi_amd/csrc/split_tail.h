@@ -30,6 +30,13 @@ __device__ __forceinline__ float2 load_coherent2(const float* p) {
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
+// Arrival counter of unit c.  Consecutive units' counters sit 4 KiB apart (a
+// bijection of [0, kMaxCounters)): every split of every unit takes its ticket at
+// about the same time, and tickets on one cache line queue behind each other.
+__device__ __forceinline__ int32_t* unit_counter(int32_t* counters, int c) {
+  return counters + (c % 64) * (kMaxCounters / 64) + c / 64;
+}
+
 // Buffer-resource word 3 for raw (unswizzled, untyped) buffers on CDNA, and the
 // cache-policy bit (sc1) that makes a buffer load coherent at device scope, as an
 // agent-scope atomic load is.
@@ -137,7 +144,7 @@ struct SplitTail {
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int ticket = __hip_atomic_fetch_add(&a.counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
+      const int ticket = __hip_atomic_fetch_add(unit_counter(a.counters, b * a.Hkv + g), 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
       *flag = (ticket == a.n_split - 1) ? 1 : 0;
     }
@@ -145,7 +152,7 @@ struct SplitTail {
     if (*flag == 0) return;
     merge(a, g, q_row0, G, R, ns_max, tail);
     if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(unit_counter(a.counters, b * a.Hkv + g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // The merge itself: every thread of the work-group takes part (it has barriers).
