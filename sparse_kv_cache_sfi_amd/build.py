@@ -21,6 +21,8 @@ FLAGS = [
     # Packed fp32 instructions stay off: the device code is written as plain fp32.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(HERE, "..", "include"),
+    # Per-kernel register, LDS and scratch figures (checked below).
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -33,17 +35,53 @@ FILE_FLAGS = {
 }
 
 
-def _compile(src: str) -> str:
+def _resource_usage(stderr: str):
+    """(other diagnostics, {kernel: {figure: value}}) from hipcc's kernel-resource-usage remarks."""
+    usage, other, name, skip, pending = {}, [], None, 0, []
+    for line in stderr.splitlines():
+        if skip:
+            skip -= 1
+            continue
+        if line.startswith("In file included from"):
+            pending.append(line)   # context of the next diagnostic
+            continue
+        remark = "[-Rpass-analysis=kernel-resource-usage]" in line
+        if not remark:
+            other.extend(pending)
+        pending = []
+        if remark:
+            body = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+            key, _, val = body.partition(":")
+            if key == "Function Name":
+                name = val.strip()
+                usage[name] = {}
+                skip = 2   # the source line and caret hipcc prints under the first remark
+            elif name is not None:
+                usage[name][key.strip()] = val.strip()
+            continue
+        other.append(line)
+    return "\n".join(other), usage
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in p.stderr.splitlines() if noise not in l)
+    err, usage = _resource_usage("\n".join(l for l in p.stderr.splitlines() if noise not in l))
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
     if err.strip():
         print(err, file=sys.stderr)
-    return obj
+    # A kernel with private (scratch) memory gets a scratch allocation at every launch,
+    # which costs microseconds on kernels that take ten: none may have any.
+    bad = {k: u for k, u in usage.items()
+           if u.get("ScratchSize [bytes/lane]", "0") != "0" or u.get("VGPRs Spill", "0") != "0"}
+    if bad:
+        raise RuntimeError(f"kernels in {src} use scratch memory: " +
+                           "; ".join(f"{k} ({u.get('ScratchSize [bytes/lane]')} B/lane, "
+                                     f"{u.get('VGPRs Spill')} VGPRs spilled)" for k, u in bad.items()))
+    return obj, usage
 
 
 def build(verbose: bool = True) -> str:
@@ -51,7 +89,12 @@ def build(verbose: bool = True) -> str:
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        results = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in results]
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for _, usage in results:
+            for k, u in usage.items():
+                f.write(k + " " + " ".join(f"{a}={b}" for a, b in u.items()) + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)

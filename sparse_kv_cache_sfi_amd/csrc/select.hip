@@ -498,12 +498,13 @@ SelPlan plan_select(int64_t span, int k) {
   int64_t seg = (span + S - 1) / S;
   seg = (seg + 3) / 4 * 4;
   const int64_t m = S * (int64_t)k;
-  if (2 * m > span || m > 64 * kSelThreads || seg > 64 * kSelThreads) return p;
+  // (The merge keeps a key and a position per candidate in registers: 32 of each per
+  // thread at most, 64 would spill.)
+  if (2 * m > span || m > 32 * kSelThreads || seg > 64 * kSelThreads) return p;
   p.S = (int)S;
   p.seg = (int)seg;
   p.V1 = seg <= 8 * kSelThreads ? 8 : seg <= 16 * kSelThreads ? 16 : seg <= 32 * kSelThreads ? 32 : 64;
-  p.V2 = m <= 4 * kSelThreads ? 4 : m <= 8 * kSelThreads ? 8 : m <= 16 * kSelThreads ? 16
-       : m <= 32 * kSelThreads ? 32 : 64;
+  p.V2 = m <= 4 * kSelThreads ? 4 : m <= 8 * kSelThreads ? 8 : m <= 16 * kSelThreads ? 16 : 32;
   return p;
 }
 
@@ -545,8 +546,7 @@ hipError_t launch_select(const float* scores, int B, int Hkv, int64_t stride, co
       case 4: SFI_MRG(4); break;
       case 8: SFI_MRG(8); break;
       case 16: SFI_MRG(16); break;
-      case 32: SFI_MRG(32); break;
-      default: SFI_MRG(64); break;
+      default: SFI_MRG(32); break;
     }
 #undef SFI_MRG
     return hipGetLastError();
