@@ -130,10 +130,18 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
 
   // Virtual rows: [0, cap_v) compact (or sink + selection), then the recent window.
   int cap_v = 0, t1 = 0;
-  const int t0 = split * a.split_tokens;
+  int t0 = split * a.split_tokens;
   if constexpr (SPARSE) {
     cap_v = INDEXED ? a.n_sink + a.sel_k : a.cap;
-    t1 = min(cap_v + min(a.n_recent, a.max_seq_len), t0 + a.split_tokens);
+    const int rec = min(a.n_recent, a.max_seq_len);
+    if (!a.recent_split) {
+      t1 = min(cap_v + rec, t0 + a.split_tokens);
+    } else if (split == a.n_split - 1) {   // the recent window alone
+      t0 = cap_v;
+      t1 = cap_v + rec;
+    } else {
+      t1 = min(cap_v, t0 + a.split_tokens);
+    }
   }
   const bool has_recent = SPARSE && t1 > cap_v;
   // A split of compact-buffer rows only never needs the request's length: it is not

@@ -84,6 +84,10 @@ struct AttnArgs {
   // Leave the split partials for a later launch to merge (no arrival ticket, out and
   // lse are not written when there is more than one split); selects the kernel variant.
   int32_t defer_merge;
+  // Fast step: the recent window is the unit's last split on its own (splits 0 ..
+  // n_split - 2 cover the compact rows [0, cap) in split_tokens pieces); 0: the splits
+  // cut the virtual rows [0, cap + n_recent) evenly.
+  int32_t recent_split;
 };
 
 // Work list of the mixed launch (travels in kernel arguments).  Entry e serves

@@ -106,6 +106,7 @@ sfi_status check_budgets(int32_t n_sink, int32_t n_recent) {
 struct Split {
   int tokens;
   int n;
+  bool recent = false;   // fast step: the recent window is the last split on its own
 };
 
 int64_t tune_env(const char* name, int64_t fallback) {
@@ -165,10 +166,25 @@ Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
                     dense_min_split(kv->max_seq_len));
 }
 
+// The split that holds the recent window reads it through the block table, so its
+// loads wait for two memory round trips (the request's length, then the pages'
+// entries) that a split of compact rows never waits for; cut evenly with the compact
+// rows, it arrives last at every unit's combine (per-work-group timestamps, 16K at 1/8
+// retention: 0.7 us behind the other splits).  When the compact rows need several
+// splits anyway and one more work-group per unit still fits the work-group target, the
+// recent window becomes a short split of its own and the compact splits keep their
+// size.  SFI_TUNE_RECENT_SPLIT=0 (environment, read on every call) keeps the even cut.
 Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_paged_kv* kv) {
   const int64_t rec = n_recent < kv->max_seq_len ? n_recent : kv->max_seq_len;
   const int64_t n_tok = (int64_t)cap + rec;
-  return plan_split((int64_t)s->batch * s->num_kv_heads, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
+  const int64_t units = (int64_t)s->batch * s->num_kv_heads;
+  const Split even = plan_split(units, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
+  if (even.n > 1 && rec > 0 && rec <= sfi::kMaxSplitTokens && cap > 0 && tune_env("SFI_TUNE_RECENT_SPLIT", 1) != 0) {
+    const Split c = plan_split(units, cap, sfi::kDecodeTile, sparse_min_split(n_tok), sfi::kMaxSplits - 1);
+    if (c.n > 1 && c.tokens == even.tokens && units * (c.n + 1) <= tune_env("SFI_TUNE_TARGET_WGS", 256))
+      return {c.tokens, c.n + 1, true};
+  }
+  return even;
 }
 
 sfi::AttnArgs base_args(const sfi_shape* s, const sfi_paged_kv* kv, const int32_t* seq_lens) {
@@ -514,6 +530,7 @@ sfi_status sparse_call(const sfi_shape* shape_in, const sfi_paged_kv* kv, const 
   a.n_recent = n_recent;
   a.split_tokens = sp.tokens;
   a.n_split = sp.n;
+  a.recent_split = sp.recent ? 1 : 0;
   a.t_q = 1;
   a.out = out;
   a.lse = lse;

@@ -253,9 +253,13 @@ def test_split_plan_of_the_16k_decode_layer():
     # fast step, 1.6 % retention: 192 compact slots + 64 recent -> one split (no split-K tail)
     assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=192, n_recent=64) == (256, 1)
-    # 12.5 %: 1984 compact slots + 64 recent -> 16 splits of 128 tokens, 128 work-groups
+    # 12.5 %: 1984 compact slots in 16 splits of 128 tokens, and the 64 recent tokens as a split of
+    # their own (it waits for the block table): 136 work-groups
     assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
-                           max_seq_len=16384, cap=1984, n_recent=64) == (128, 16)
+                           max_seq_len=16384, cap=1984, n_recent=64) == (128, 17)
+    # 25 %: one more work-group per unit would pass one per CU: 32 even splits of 128
+    assert sfi.plan_splits(1, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=4032, n_recent=64) == (128, 32)
     # batch 16: 128 units of two splits fill the 256 CUs
     assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=1984, n_recent=64) == (1024, 2)
