@@ -396,6 +396,11 @@ SFI_API sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const s
  * Launch plan of the split-K attention calls, for inspection and tests
  * (host only, no GPU needed).  op: 0 = dense / verify (t_q as given),
  * 1 = sparse decode.  Returns the tokens per split and splits per (b, g).
+ * For op 1 the splits cut the virtual rows [0, cap + recent) evenly, except
+ * when the compact rows need several splits and one more work-group per
+ * (b, g) still fits the plan's target of about one work-group per CU: then
+ * n_split - 1 splits of split_tokens cover the compact rows [0, cap) and the
+ * recent window is the last split on its own.
  */
 SFI_API sfi_status sfi_plan_splits(int32_t op, const sfi_shape* shape, const sfi_paged_kv* kv,
                            int32_t t_q, int32_t cap, int32_t n_recent,
