@@ -43,22 +43,24 @@ __device__ __forceinline__ int32_t* unit_counter(int32_t* counters, int c) {
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kCoherentLoad = 16;
 
-// Wave-wide reductions (all 64 lanes receive the result).
+// Wave-wide reduction (every lane receives the result; all 64 lanes active): the
+// 16-lane rows reduce with DPP (quad_perm xor 1 and 2, row_half_mirror, row_mirror;
+// VALU operations, no LDS round trip), then the four row totals are combined from
+// readlanes in the order (r0 op r1) op (r2 op r3).
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, dpp_mov<0xB1>(x));
+  x = op(x, dpp_mov<0x4E>(x));
+  x = op(x, dpp_mov<0x141>(x));
+  x = op(x, dpp_mov<0x140>(x));
+  auto row = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  return op(op(row(0), row(16)), op(row(32), row(48)));
+}
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, lane_xor<1>(x));
-  x = fmaxf(x, lane_xor<2>(x));
-  x = fmaxf(x, lane_xor<4>(x));
-  x = fmaxf(x, lane_xor<8>(x));
-  x = fmaxf(x, lane_xor<16>(x));
-  return fmaxf(x, lane_xor<32>(x));
+  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
 }
 __device__ __forceinline__ float wave_sum(float x) {
-  x += lane_xor<1>(x);
-  x += lane_xor<2>(x);
-  x += lane_xor<4>(x);
-  x += lane_xor<8>(x);
-  x += lane_xor<16>(x);
-  return x + lane_xor<32>(x);
+  return wave_reduce(x, [](float u, float v) { return u + v; });
 }
 
 // A unit (b, g) owns R = t_q * G output rows: row r = (t, h) with t = r / G,
