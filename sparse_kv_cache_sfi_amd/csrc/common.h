@@ -64,26 +64,55 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The values x holds in lanes (lane & ~OFF) and (lane | OFF), for OFF 16 or 32, as
+// (lo, hi): v_permlane16_swap / v_permlane32_swap (gfx950), VALU operations that
+// exchange 16-lane rows or 32-lane halves without a trip through the LDS unit.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  static_assert(OFF == 16 || OFF == 32, "row or half-wave pairs");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+
 // The value of x held by lane (lane ^ OFF), for a power of two OFF < 64: DPP
 // quad_perm for 1 and 2, DPP row_ror:8 for 8 (a rotation by 8 inside a 16-lane row
-// is the xor-8 exchange), ds_swizzle in bitmask mode for 4 and 16 (source lane
-// = lane ^ OFF within 32 lanes), ds_bpermute for 32.  Every lane must be active.
+// is the xor-8 exchange), ds_swizzle in bitmask mode for 4 (source lane = lane ^ 4
+// within 32 lanes), the permlane swaps for 16 and 32.  Every lane must be active
+// (blocks are whole waves, so lane = threadIdx.x mod 64).
 template <int OFF>
 __device__ __forceinline__ float lane_xor(float x) {
   static_assert(OFF > 0 && OFF < 64 && (OFF & (OFF - 1)) == 0, "power of two below the wave width");
   if constexpr (OFF == 1) return dpp_mov<0xB1>(x);
   else if constexpr (OFF == 2) return dpp_mov<0x4E>(x);
   else if constexpr (OFF == 8) return dpp_mov<0x128>(x);
-  else if constexpr (OFF == 32) return __shfl_xor(x, 32);
-  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (OFF << 10)));
+  else if constexpr (OFF == 16 || OFF == 32) {
+    float lo, hi;
+    lane_pair<OFF>(x, lo, hi);
+    return (threadIdx.x & OFF) ? lo : hi;
+  } else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (OFF << 10)));
 }
 
 // x combined by op with the lanes at xor distance FROM, 2 FROM, ..., 32, in that
-// order: every lane ends with op over the lanes that share its bits below FROM.
+// order: every lane ends with op over the lanes that share its bits below FROM (op
+// commutative: the 16 and 32 steps combine the pair as op(lo, hi) in every lane).
 template <int FROM, typename Op>
 __device__ __forceinline__ float xor_fold(float x, Op op) {
   if constexpr (FROM < kWave) {
-    x = op(x, lane_xor<FROM>(x));
+    if constexpr (FROM == 16 || FROM == 32) {
+      float lo, hi;
+      lane_pair<FROM>(x, lo, hi);
+      x = op(lo, hi);
+    } else {
+      x = op(x, lane_xor<FROM>(x));
+    }
     return xor_fold<FROM * 2>(x, op);
   } else {
     return x;

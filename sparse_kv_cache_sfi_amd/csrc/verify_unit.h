@@ -221,10 +221,15 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
         for (int i = 0; i < w2; ++i) {
           const float keep = up ? v16[i + w2] : v16[i];
           const float send = up ? v16[i] : v16[i + w2];
-          v16[i] = keep + __shfl_xor(send, 2 * w2);
+          float got;
+          if (w2 == 8) got = lane_xor<16>(send);
+          else if (w2 == 4) got = lane_xor<8>(send);
+          else if (w2 == 2) got = lane_xor<4>(send);
+          else got = lane_xor<2>(send);
+          v16[i] = keep + got;
         }
       }
-      const float tot = v16[0] + __shfl_xor(v16[0], 1);
+      const float tot = v16[0] + lane_xor<1>(v16[0]);
       const int ri = n >> 1;
       const int tok = 8 * (ri / 4) + 4 * hb + (ri % 4);
       const int pos = tb + tok;
@@ -243,7 +248,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
       sv[i] = vis ? sacc[i] * a.scale_log2 : neg_inf();
       mx = fmaxf(mx, sv[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, lane_xor<32>(mx));
     if (__any(mx > m_run + 8.f)) {
       const float mn = fmaxf(m_run, mx);
       const float al = (m_run == neg_inf()) ? 0.f : exp2_fast(m_run - mn);
@@ -306,7 +311,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
   constexpr int MO_ROW = S::MO_ROW;
   float* mo = reinterpret_cast<float*>(big);                // [WAVES][32][MO_ROW]
   float* mml = mo + WAVES * 32 * MO_ROW;                    // [WAVES][32][2]
-  l_run += __shfl_xor(l_run, 32);
+  l_run += lane_xor<32>(l_run);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
