@@ -179,7 +179,8 @@ Split plan_sparse(const sfi_shape* s, int32_t cap, int32_t n_recent, const sfi_p
   const int64_t n_tok = (int64_t)cap + rec;
   const int64_t units = (int64_t)s->batch * s->num_kv_heads;
   const Split even = plan_split(units, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
-  if (even.n > 1 && rec > 0 && rec <= sfi::kMaxSplitTokens && cap > 0 && tune_env("SFI_TUNE_RECENT_SPLIT", 1) != 0) {
+  const char* off = getenv("SFI_TUNE_RECENT_SPLIT");
+  if (even.n > 1 && rec > 0 && rec <= sfi::kMaxSplitTokens && cap > 0 && !(off && off[0] == '0')) {
     const Split c = plan_split(units, cap, sfi::kDecodeTile, sparse_min_split(n_tok), sfi::kMaxSplits - 1);
     if (c.n > 1 && c.tokens == even.tokens && units * (c.n + 1) <= tune_env("SFI_TUNE_TARGET_WGS", 256))
       return {c.tokens, c.n + 1, true};

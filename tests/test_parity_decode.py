@@ -258,6 +258,24 @@ def test_fast_step_matches_oracle(gpu_lib, name, mk, k):
     _fast_step_check(gpu_lib, c, dc, sels, cap, L_fast, c.q[:, 0], qv)
 
 
+@pytest.mark.parametrize("recent_split", ["1", "0"])
+def test_fast_step_under_both_split_plans(gpu_lib, recent_split, monkeypatch):
+    # 1 request x 8 KV heads, 1984 compact slots + 64 recent tokens: by default 16 compact splits and the
+    # recent window as a 17th split of its own; SFI_TUNE_RECENT_SPLIT=0 cuts the 2048 rows into 16 even
+    # splits.  Both plans against the oracle.
+    monkeypatch.setenv("SFI_TUNE_RECENT_SPLIT", recent_split)
+    c = make_case(126, name="rs", B=1, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[4000], capacity=[4010],
+                  n_sink=4, n_recent=64, k_sel=1980)
+    dc = DevCase(c)
+    k = 1980
+    cap = c.n_sink + k
+    assert _splits(gpu_lib, 1, c, dc, cap=cap) == (17 if recent_split == "1" else 16)
+    rng = np.random.default_rng(126)
+    sels = [_random_selection(rng, c, int(c.seq_lens[b]), k) for b in range(c.B)]
+    L_fast = np.minimum(c.seq_lens + 3, c.kv.max_pages * 16).astype(np.int32)
+    _fast_step_check(gpu_lib, c, dc, sels, cap, L_fast, c.q[:, 0], c.q_values()[:, 0])
+
+
 def test_fast_step_at_full_retention_equals_dense(gpu_lib):
     c = qwen06b_decode_case(131, L=3072, frac=(1, 1))
     dc = DevCase(c)
