@@ -5,6 +5,7 @@ Always recompiles every source; objects go to sparse_kv_cache_sfi_amd/_build/.
 """
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -37,15 +38,19 @@ FILE_FLAGS = {
 
 def _resource_usage(stderr: str):
     """(other diagnostics, {kernel: {figure: value}}) from hipcc's kernel-resource-usage remarks."""
-    usage, other, name, skip, pending = {}, [], None, 0, []
+    usage, other, name, pending = {}, [], None, []
+    in_remark = False
     for line in stderr.splitlines():
-        if skip:
-            skip -= 1
+        # the source line and caret hipcc prints under a diagnostic ("   50 | ...", "      | ^")
+        if re.match(r"^\s*\d*\s*\|", line):
+            if not in_remark:
+                other.append(line)
             continue
         if line.startswith("In file included from"):
             pending.append(line)   # context of the next diagnostic
             continue
         remark = "[-Rpass-analysis=kernel-resource-usage]" in line
+        in_remark = remark
         if not remark:
             other.extend(pending)
         pending = []
@@ -55,7 +60,6 @@ def _resource_usage(stderr: str):
             if key == "Function Name":
                 name = val.strip()
                 usage[name] = {}
-                skip = 2   # the source line and caret hipcc prints under the first remark
             elif name is not None:
                 usage[name][key.strip()] = val.strip()
             continue
