@@ -493,7 +493,13 @@ SelPlan plan_select(int64_t span, int k) {
   const char* env = getenv("SFI_TUNE_SELECT_SEGMENTS");
   if (env && env[0] == '0') return p;
   if (span < 32768 || k < 1) return p;
-  int64_t S = (span + 8191) / 8192;
+  // Segments of up to 16 keys per thread (16384 positions): at 64K (32 rows x 65276, k
+  // 2048) four segments and a merge over 8192 candidates take 22.5 us, eight of 8192
+  // positions and a merge over 16384 take 24.0, two of 32768 take 31.9.
+  // SFI_TUNE_SELECT_SEG (environment, read on every call) sets another target size.
+  const char* segenv = getenv("SFI_TUNE_SELECT_SEG");
+  const int64_t seg_target = segenv && atoll(segenv) >= 1024 ? atoll(segenv) : 16 * kSelThreads;
+  int64_t S = (span + seg_target - 1) / seg_target;
   if (S > 16) S = 16;
   int64_t seg = (span + S - 1) / S;
   seg = (seg + 3) / 4 * 4;

@@ -188,20 +188,23 @@ def test_selector_bin_that_holds_exactly_the_wanted_keys(gpu_lib, stride, digits
         _select_both(gpu_lib, sc, [stride], k, n_sink=n_sink, n_recent=n_recent)
 
 
+@pytest.mark.parametrize("seg", [16384, 8192])
 @pytest.mark.parametrize("k", [1, 100, 1024, 4095])
-def test_selector_segments_with_ties_across_segment_boundaries(gpu_lib, k):
+def test_selector_segments_with_ties_across_segment_boundaries(gpu_lib, k, seg, monkeypatch):
     """Long rows cut into segments: equal scores straddling segment boundaries, whole rows of one
     value, signed zeros and -inf, and ragged lengths that leave trailing segments short or empty.
-    The lowest positions must win every tie, exactly as the one-work-group Selector and the oracle."""
+    The lowest positions must win every tie, exactly as the one-work-group Selector and the oracle.
+    98300 candidates make 6 segments of 16384 positions (the default size) or 12 of 8192."""
+    if seg != 16384:
+        monkeypatch.setenv("SFI_TUNE_SELECT_SEG", str(seg))
     rng = np.random.default_rng(300 + k)
-    B, H, stride = 3, 4, 98304                  # 12 segments of 8192 positions
+    B, H, stride = 3, 4, 98304
     vals = np.array([-np.inf, -2.0, -0.0, 0.0, 0.5, 3.0, 3.0, 7.25], dtype=np.float32)
     sc = rng.choice(vals, size=(B, H, stride)).astype(np.float32)
     sc[0, 1, :] = 3.0                            # one value everywhere
     sc[1, 2, :] = -0.0
     sc[1, 2, ::3] = 0.0                          # signed zeros only
-    seg = 8192
-    for j in range(1, 12):                       # a band of the top value across every boundary
+    for j in range(1, (stride - 4) // seg + 1):  # a band of the top value across every boundary
         sc[2, 3, 4 + j * seg - 40: 4 + j * seg + 40] = 9.5
     lens = [98304, 70001, 33000]
     _select_both(gpu_lib, sc, lens, k, n_sink=4, n_recent=64)
