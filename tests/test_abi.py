@@ -131,15 +131,17 @@ def test_select_workspace_size_covers_the_segment_candidates(lib):
         return out.value
     # 16K rows run on one work-group each: no workspace
     assert size(1, 8, 16384, 4, 1980) == 0
-    # the 64K refresh: 4 requests x 8 KV heads, 65532 possible candidates -> 8 segments of
-    # top-2048 candidates, 8 bytes each (key, position)
-    assert size(4, 8, 65536, 4, 2048) == 32 * 8 * 2048 * 8        # keys + positions
+    # the 64K refresh: 4 requests x 8 KV heads, 65532 possible candidates -> 4 segments of 16383
+    # positions, each keeping its top-2048 candidates, 8 bytes each (key, position)
+    assert size(4, 8, 65536, 4, 2048) == 32 * 4 * 2048 * 8        # keys + positions
     # k too large for the segments to cut the row at least in half: one work-group per row
     assert size(4, 8, 65536, 4, 8192) == 0
     # 1,048,576 positions: 16 segments
     assert size(1, 1, 1 << 20, 4, 1024) == 16 * 1024 * 8
-    # the candidate rows are padded to a multiple of four: 8 segments x top-2047 = 16376 -> 16376
-    assert size(1, 1, 65536, 4, 2047) == ((8 * 2047 + 3) // 4 * 4) * 8
+    # the candidate rows are padded to a multiple of four: 4 segments x top-2047 = 8188 -> 8188
+    assert size(1, 1, 65536, 4, 2047) == ((4 * 2047 + 3) // 4 * 4) * 8
+    # a k whose padding shows: 4 x 2045 = 8180 -> 8180; 3 segments (49148 positions) x 2045 = 6135 -> 6136
+    assert size(1, 1, 49152, 4, 2045) == 6136 * 8
 
 
 def test_pack_rejects_bad_arguments(lib):
