@@ -53,10 +53,16 @@ FAST_KERNEL = "decode_kernel<unsigned short, 128, 2, true, 0, false, false, fals
 
 
 def decode_source_hash():
+    """sha1[:16] of the decode kernel's sources with comments and blank lines removed (a comment edit does not
+    change the kernel the counters were taken on)."""
     h = hashlib.sha1()
     for f in DECODE_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -68,7 +74,7 @@ def profiled_traffic(kernel):
     if not os.path.exists(path):
         return None, "no counter summary"
     text = open(path).read()
-    m = re.search(r"decode kernel source sha1\[:16\]: ([0-9a-f]+)", text)
+    m = re.search(r"decode kernel source sha1\[:16\] \(comments removed\): ([0-9a-f]+)", text)
     if not m or m.group(1) != decode_source_hash():
         return None, "kernel changed since the counters were taken"
     for line in text.splitlines():

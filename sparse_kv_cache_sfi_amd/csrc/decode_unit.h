@@ -27,9 +27,12 @@
 // rs = max(n_sink, L - n_recent) (masked at or past L).  Split boundaries therefore
 // need no device value, and a split that holds only compact rows issues its first
 // K/V loads at once, before the request's length, n_compact or any block-table entry
-// has arrived.  The index-set fast step uses the same layout with cap = n_sink + k:
-// rows [0, n_sink) are the sink positions and rows n_sink + j the j-th entry of the
-// selection, each read in place through the block table.
+// has arrived.  The splits either cut [0, cap + n_recent) evenly or (recent_split)
+// cover [0, cap) and leave the recent window to the last split alone, which is the
+// only one that waits for the length and the block table.  The index-set fast step
+// uses the same layout with cap = n_sink + k: rows [0, n_sink) are the sink positions
+// and rows n_sink + j the j-th entry of the selection, each read in place through the
+// block table.
 #pragma once
 
 #include <type_traits>
