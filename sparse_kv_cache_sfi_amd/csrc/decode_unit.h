@@ -396,8 +396,11 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
           const bool real = pos_[u] >= 0;
 #pragma unroll
           for (int c = 0; c < C; ++c) {
-            *reinterpret_cast<u32x4*>(dk + (c * LPR + sub) * EPC) = real ? B.k[u][c] : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(dv + (c * LPR + sub) * EPC) = real ? B.v[u][c] : u32x4{0u, 0u, 0u, 0u};
+            // streaming stores, as in the gather-pack (pack_unit.h)
+            __builtin_nontemporal_store(real ? B.k[u][c] : u32x4{0u, 0u, 0u, 0u},
+                                        reinterpret_cast<u32x4*>(dk + (c * LPR + sub) * EPC));
+            __builtin_nontemporal_store(real ? B.v[u][c] : u32x4{0u, 0u, 0u, 0u},
+                                        reinterpret_cast<u32x4*>(dv + (c * LPR + sub) * EPC));
           }
         }
       }

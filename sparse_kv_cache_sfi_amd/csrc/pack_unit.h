@@ -58,9 +58,13 @@ __device__ __forceinline__ void pack_block(const PackArgs& p, const int bx, cons
         vx = *reinterpret_cast<const u32x4*>(vp + off);
       }
     }
+    // Streaming (non-temporal) stores: the packed rows are read by the next fast step,
+    // launches later, and write-back stores left them dirty in the caches, where the
+    // write-back of several MiB slowed the next launch (the 16K step: 40.9 -> 38.6 us
+    // with these, the slow step that follows the pack 2.3 us faster).
     const int64_t dst = (dst_head + i) * ROW_BYTES + chunk * 16;
-    *reinterpret_cast<u32x4*>(ckp + dst) = kx;
-    *reinterpret_cast<u32x4*>(cvp + dst) = vx;
+    __builtin_nontemporal_store(kx, reinterpret_cast<u32x4*>(ckp + dst));
+    __builtin_nontemporal_store(vx, reinterpret_cast<u32x4*>(cvp + dst));
   }
 
   if (bx == 0 && g == 0) {
