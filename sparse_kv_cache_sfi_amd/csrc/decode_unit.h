@@ -353,10 +353,13 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
           }
         }
       }
+      // Streaming (non-temporal) loads: every K/V row is read once per launch, so
+      // letting it pass through the caches without displacing anything keeps L2 for
+      // the index set, the block table and the split-K partials.
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        B.k[u][c] = *reinterpret_cast<const u32x4*>(kr + (c * LPR + sub) * EPC);
-        B.v[u][c] = *reinterpret_cast<const u32x4*>(vr + (c * LPR + sub) * EPC);
+        B.k[u][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (c * LPR + sub) * EPC));
+        B.v[u][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (c * LPR + sub) * EPC));
       }
     }
   };

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   const int64_t stride = (int64_t)gridDim.x * 256;
   uint32_t acc = 0u;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
-    const u32x4 a = src[i];
+    const u32x4 a = __builtin_nontemporal_load(src + i);   // same load form as the K/V reads
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == 0x9e3779b9u) sink[0] = acc;

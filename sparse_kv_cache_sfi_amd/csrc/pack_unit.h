@@ -54,8 +54,9 @@ __device__ __forceinline__ void pack_block(const PackArgs& p, const int bx, cons
       const int pg = bt[pos >> 4];
       if (pg >= 0 && pg < p.num_pages) {
         const int64_t off = (int64_t)pg * page_bytes + ((int64_t)g * kPage + (pos & 15)) * ROW_BYTES + chunk * 16;
-        kx = *reinterpret_cast<const u32x4*>(kp + off);
-        vx = *reinterpret_cast<const u32x4*>(vp + off);
+        // each source row is read once: streaming loads keep it out of the caches
+        kx = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
+        vx = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
       }
     }
     // Streaming (non-temporal) stores: the packed rows are read by the next fast step,

@@ -155,8 +155,9 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
       const bool in = pos < t1;
       const int pg = bt_s[in ? (pos >> 4) - pg_lo : 0];
       const int64_t off = (in && pg >= 0) ? (int64_t)pg * page_elems + head_off + (int64_t)(pos & 15) * D : 0;
-      kr[i] = *reinterpret_cast<const u32x4*>(kpool + off + ch * 8);
-      vr[i] = *reinterpret_cast<const u32x4*>(vpool + off + ch * 8);
+      // streaming loads: each K/V row is read once per launch
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off + ch * 8));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off + ch * 8));
     }
   };
   auto park_tile = [&](const u32x4 (&kr)[LOADS], const u32x4 (&vr)[LOADS]) {
