@@ -128,7 +128,21 @@ Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int 
   if (ns < 1) ns = 1;
   int64_t st = (n_tok + ns - 1) / ns;
   st = (st + tile - 1) / tile * tile;
-  if (st > sfi::kMaxSplitTokens) st = sfi::kMaxSplitTokens;
+  if (st > sfi::kMaxSplitTokens) {
+    // Capped splits give more work-groups than the target, and cut at the cap they
+    // leave a short last split: at 16 requests x 8 KV heads x 8226 tokens, 4096 + 4096
+    // + 34 tokens make 384 work-groups, so half the CUs stream two long splits while
+    // the others stream one.  Cut evenly into as many splits as fill the waves of
+    // work-groups the cap needs anyway (there, four of 2112 tokens: two per CU).
+    st = sfi::kMaxSplitTokens;
+    ns = (n_tok + st - 1) / st;
+    const int64_t waves = (units * ns + target - 1) / target;
+    const int64_t fill = std::min<int64_t>(waves * target / units, max_splits);
+    if (fill > ns) {
+      st = (n_tok + fill - 1) / fill;
+      st = (st + tile - 1) / tile * tile;
+    }
+  }
   ns = (n_tok + st - 1) / st;
   return {(int)st, (int)ns};
 }

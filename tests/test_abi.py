@@ -265,6 +265,16 @@ def test_split_plan_of_the_16k_decode_layer():
     # batch 16: 128 units of two splits fill the 256 CUs
     assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=1984, n_recent=64) == (1024, 2)
+    # batch 16 at 50 %: 8226 rows exceed two capped splits; four even splits of 2112 give every
+    # CU two work-groups, where cutting at the cap (4096 + 4096 + 34) gave half of them two long ones
+    assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=8162, n_recent=64) == (2112, 4)
+    # dense at batch 12 x 16K: five splits of 3328 (480 work-groups) instead of four of 4096 (384)
+    assert sfi.plan_splits(0, B=12, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384) == (3328, 5)
+    # where the capped cut already fills whole waves it stays: batch 16 x 16K dense, 4 x 4096
+    assert sfi.plan_splits(0, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384) == (4096, 4)
 
 
 def test_binding_refuses_host_tensors():
