@@ -129,19 +129,17 @@ Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int 
   int64_t st = (n_tok + ns - 1) / ns;
   st = (st + tile - 1) / tile * tile;
   if (st > sfi::kMaxSplitTokens) {
-    // Capped splits give more work-groups than the target, and cut at the cap they
-    // leave a short last split: at 16 requests x 8 KV heads x 8226 tokens, 4096 + 4096
-    // + 34 tokens make 384 work-groups, so half the CUs stream two long splits while
-    // the others stream one.  Cut evenly into as many splits as fill the waves of
-    // work-groups the cap needs anyway (there, four of 2112 tokens: two per CU).
-    st = sfi::kMaxSplitTokens;
-    ns = (n_tok + st - 1) / st;
-    const int64_t waves = (units * ns + target - 1) / target;
-    const int64_t fill = std::min<int64_t>(waves * target / units, max_splits);
-    if (fill > ns) {
-      st = (n_tok + fill - 1) / fill;
-      st = (st + tile - 1) / tile * tile;
-    }
+    // Capped splits give more work-groups than the target, and cut at the cap they can
+    // leave CUs with two long splits beside CUs with one: at 16 requests x 8 KV heads x
+    // 12288 tokens, three splits of 4096 make 384 work-groups (a third of a second wave),
+    // and at 12305 tokens three of 4096 and one of 17 do the same.  Cut evenly into as
+    // many splits as fill the waves of work-groups the cap needs anyway (there, four
+    // splits of 3072 or 3136 tokens: two work-groups per CU).
+    const int64_t ns_cap = (n_tok + sfi::kMaxSplitTokens - 1) / sfi::kMaxSplitTokens;
+    const int64_t waves = (units * ns_cap + target - 1) / target;
+    const int64_t fill = std::max<int64_t>(ns_cap, std::min<int64_t>(waves * target / units, max_splits));
+    st = (n_tok + fill - 1) / fill;
+    st = (st + tile - 1) / tile * tile;
   }
   ns = (n_tok + st - 1) / st;
   return {(int)st, (int)ns};

@@ -265,10 +265,13 @@ def test_split_plan_of_the_16k_decode_layer():
     # batch 16: 128 units of two splits fill the 256 CUs
     assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384, cap=1984, n_recent=64) == (1024, 2)
-    # batch 16 at 50 %: 8226 rows exceed two capped splits; four even splits of 2112 give every
-    # CU two work-groups, where cutting at the cap (4096 + 4096 + 34) gave half of them two long ones
+    # batch 16 at 75 %: 12288 rows; cut at the cap (3 x 4096, 384 work-groups) half the CUs would
+    # stream two long splits; four even splits of 3072 give every CU two
     assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
-                           max_seq_len=16384, cap=8162, n_recent=64) == (2112, 4)
+                           max_seq_len=16384, cap=12224, n_recent=64) == (3072, 4)
+    # 12305 rows: not 3 x 4096 + 17 but four even splits of 3136
+    assert sfi.plan_splits(1, B=16, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
+                           max_seq_len=16384, cap=12241, n_recent=64) == (3136, 4)
     # dense at batch 12 x 16K: five splits of 3328 (480 work-groups) instead of four of 4096 (384)
     assert sfi.plan_splits(0, B=12, Hq=16, Hkv=8, d=128, bf16=True, max_pages=1024, num_pages=1024,
                            max_seq_len=16384) == (3328, 5)
