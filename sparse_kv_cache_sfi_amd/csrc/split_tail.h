@@ -2,8 +2,6 @@
 // (request, KV head) unit.  Shared by the decode and the verification kernels.
 #pragma once
 
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -96,32 +94,36 @@ struct SplitTail {
     }
   }
 
+  // x combined by op over the P lanes of its group (P a power of two, uniform over the
+  // wave, whose lanes must all be active) by a fixed xor tree; every lane of the group
+  // receives the same value.
+  template <typename Op>
+  __device__ static float fold_p(float x, int P, Op op) {
+    if (1 < P) x = op(x, lane_xor<1>(x));
+    if (2 < P) x = op(x, lane_xor<2>(x));
+    if (4 < P) x = op(x, lane_xor<4>(x));
+    if (8 < P) x = op(x, lane_xor<8>(x));
+    if (16 < P) x = op(x, lane_xor<16>(x));
+    if (32 < P) x = op(x, lane_xor<32>(x));
+    return x;
+  }
+
   // Sums the P lane partials of one float4 output group by a fixed xor tree (P is
-  // uniform over the wave, whose lanes must all be active) and writes the group's
-  // outputs, and the row's lse, from lane p = 0.
+  // uniform over the wave, whose lanes must all be active) and, when `store`, writes the
+  // group's outputs, and the row's lse, from lane p = 0 (M: the row's max in log2 units,
+  // L: its weighted sum).
   __device__ static void fold_store(const AttnArgs& a, int q_row0, int g, int G, int r, int e4, int P, int p,
-                                    float4 acc, const float* M_r, const float* L_r) {
-    auto fold = [&](auto off_tag) {
-      constexpr int OFF = decltype(off_tag)::value;
-      if (OFF < P) {
-        acc.x += lane_xor<OFF>(acc.x);
-        acc.y += lane_xor<OFF>(acc.y);
-        acc.z += lane_xor<OFF>(acc.z);
-        acc.w += lane_xor<OFF>(acc.w);
-      }
-    };
-    fold(std::integral_constant<int, 1>{});
-    fold(std::integral_constant<int, 2>{});
-    fold(std::integral_constant<int, 4>{});
-    fold(std::integral_constant<int, 8>{});
-    fold(std::integral_constant<int, 16>{});
-    fold(std::integral_constant<int, 32>{});
-    if (p == 0) {
+                                    float4 acc, float M, float L, bool store) {
+    const auto add = [](float u, float v) { return u + v; };
+    acc.x = fold_p(acc.x, P, add);
+    acc.y = fold_p(acc.y, P, add);
+    acc.z = fold_p(acc.z, P, add);
+    acc.w = fold_p(acc.w, P, add);
+    if (store && p == 0) {
       const int64_t orow = row(a, q_row0, g, G, r);
-      const float ls = L_r[r];
       *reinterpret_cast<float4*>(a.out + orow * D + e4 * 4) =
-          ls > 0.f ? make_float4(acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls) : make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e4 == 0 && a.lse) a.lse[orow] = ls > 0.f ? (M_r[r] + log2f(ls)) * kLn2 : neg_inf();
+          L > 0.f ? make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e4 == 0 && a.lse) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : neg_inf();
     }
   }
 
@@ -187,6 +189,45 @@ struct SplitTail {
     };
     auto load4 = [&](int off) { return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(part, off, 0, kCoherentLoad)); };
 
+    // One output group per thread and all its splits in one batch of loads (the decode
+    // layers' units: two rows of 128 dimensions and up to 2 PRE splits): each lane also
+    // loads the (m, l) pairs of its own splits, and the group's P lanes combine the row
+    // max and the weighted sum by the same xor tree as the output sums, so this merge
+    // takes one memory round trip and no LDS or barrier.  (At d 64 its registers would
+    // cost the decode kernels a wave per SIMD; they keep the merge below.)
+    if (D >= 128 && n_grp * P <= NT && ns <= P * PRE) {
+      const bool act = grp0 < n_grp;
+      const int r = act ? grp0 / D4 : 0;
+      const float* mlp = a.part_ml + row(a, q_row0, g, G, r) * a.part_stride * 2;
+      float4 ov[PRE];
+      float2 ml[PRE];
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) {
+        const int sj = p + P * j;
+        const bool in = act && sj < ns;
+        ov[j] = in ? load4(offset(grp0, sj)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ml[j] = in ? load_coherent2(mlp + sj * 2) : make_float2(neg_inf(), 0.f);
+      }
+      float M = neg_inf();
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) M = fmaxf(M, ml[j].x);
+      M = fold_p(M, P, [](float u, float v) { return fmaxf(u, v); });
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) {
+        const float wt = (ml[j].x == neg_inf()) ? 0.f : exp2_fast(ml[j].x - M);
+        L = fmaf(wt, ml[j].y, L);
+        acc.x = fmaf(wt, ov[j].x, acc.x);
+        acc.y = fmaf(wt, ov[j].y, acc.y);
+        acc.z = fmaf(wt, ov[j].z, acc.z);
+        acc.w = fmaf(wt, ov[j].w, acc.w);
+      }
+      L = fold_p(L, P, [](float u, float v) { return u + v; });
+      fold_store(a, q_row0, g, G, r, grp0 % D4, P, p, acc, M, L, act);
+      return;
+    }
+
     float4 first[PRE];
     if (grp0 < n_grp) {
 #pragma unroll
@@ -232,7 +273,7 @@ struct SplitTail {
         for (int j = 0; j < PRE; ++j)
           if (p + P * (j0 + j) < ns) add(wr[p + P * (j0 + j)], v[j]);
       }
-      fold_store(a, q_row0, g, G, r, grp % D4, P, p, acc, M_r, L_r);
+      fold_store(a, q_row0, g, G, r, grp % D4, P, p, acc, M_r[r], L_r[r], true);
     }
   }
 };
