@@ -95,9 +95,29 @@ def upload(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+# After an idle stretch (host-side set-up, a pause of half a second or more) the GPU's clocks take
+# some tens of milliseconds of load to come back up: the 64K x 4 slow step ran 206, 188, 180, 177 us
+# in four back-to-back 8 ms loops.  Every timed loop is therefore preceded by at least this much
+# of the same work.
+WARM_S = 0.1
+
+
+def warm(fn, n, stream, seconds=WARM_S):
+    """Runs fn(0 .. n-1) in rounds, each ended by a stream synchronization, until `seconds` of wall
+    time have passed."""
+    t0 = time.perf_counter()
+    while True:
+        for i in range(n):
+            fn(i)
+        stream.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_loop(fn, n, stream):
-    """Seconds per call of fn(i), i = 0..n-1, between HIP events on `stream`."""
+    """Seconds per call of fn(i), i = 0..n-1, between HIP events on `stream`, after warm()."""
     import torch
+    warm(fn, n, stream)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record(stream)
     for i in range(n):
@@ -343,6 +363,7 @@ def step_leg(sfi, dev, steps, warmup, R=8):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    warm(step, R, st)   # more untimed steps, until the clocks are up (WARM_S)
     t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0e.record(st)
     for i in range(steps):
@@ -705,7 +726,9 @@ def refresh_schedule_c3(sfi, dev, steps=64, period=16):
                 cur = support[t // period]                                   # [B, Hkv, hh]
                 hit = (cur.unsqueeze(-1) == sched.sel.long().unsqueeze(-2)).any(-1).float().mean().item()
                 by_age.setdefault(t % interval, []).append(hit)
-        # timed pass
+        # timed pass, after untimed steps that bring the clocks up (the recall pass paused the GPU
+        # for host reads)
+        warm(lambda i: sched.step(), steps, torch.cuda.current_stream(dev))
         sched.t = 0
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
