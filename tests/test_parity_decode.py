@@ -88,6 +88,28 @@ def test_dense_slow_step_matches_oracle(gpu_lib, name, mk):
     _dense_check(gpu_lib, c, dc, stride=dc.max_seq_len + 37)
 
 
+# The split-K merge has two forms at d 128: one output group per thread with every split in one
+# batch of loads (up to 2 x 16 splits at two rows per unit, 16 at four), and the LDS form for more
+# splits.  Each case states the form its plan takes.
+MERGE_CASES = [
+    # two rows per unit, 20 splits: the one-batch form
+    ("g2_20_splits", dict(B=1, Hq=4, Hkv=2, seq_lens=[9000]), lambda ns: 16 < ns <= 32),
+    # two rows per unit, 40 splits: the LDS form
+    ("g2_40_splits", dict(B=1, Hq=4, Hkv=2, seq_lens=[20000]), lambda ns: ns > 32),
+    # four rows per unit, 24 splits: the LDS form (one lane per group takes at most 16)
+    ("g4_24_splits", dict(B=1, Hq=8, Hkv=2, seq_lens=[6000]), lambda ns: 16 < ns <= 32),
+]
+
+
+@pytest.mark.parametrize("name,kw,form", MERGE_CASES, ids=[n for n, _, _ in MERGE_CASES])
+def test_dense_slow_step_under_both_merge_forms(gpu_lib, name, kw, form):
+    c = make_case(150 + len(name), name=name, d=128, dtype="bf16", n_sink=4, n_recent=64, k_sel=64,
+                  hh_per_head=20, **kw)
+    dc = DevCase(c)
+    assert form(_splits(gpu_lib, 0, c, dc))
+    _dense_check(gpu_lib, c, dc)
+
+
 def test_dense_without_scores_and_determinism(gpu_lib):
     c = make_case(110, name="h", B=2, Hq=16, Hkv=8, d=128, dtype="bf16", seq_lens=[2500, 900], n_sink=4,
                   n_recent=64, k_sel=64)
