@@ -57,9 +57,12 @@ struct Elem<uint16_t> {
 template <typename T, int D, int G>
 struct DecodeShape {
   static constexpr int ROW_BYTES = D * (int)sizeof(T);
-  // Lanes per K/V row: 16 when the group is wide (fewer dimensions per lane keep the
-  // G accumulators in registers), else 8; never more lanes than 16-byte chunks.
-  static constexpr int LPR = (G >= 4 && ROW_BYTES >= 256) ? 16 : 8;
+  // Lanes per K/V row: 16 when the group is wide (fewer dimensions per lane keep the G
+  // accumulators in registers), else 8; never more lanes than 16-byte chunks.  Wide is
+  // G 8, and G 4 with rows longer than 256 bytes: at G 4 and 256-byte rows (bf16, d 128)
+  // 8 lanes per row halve the cross-lane reductions per row, which outweighs the wave
+  // per SIMD their accumulators cost (64K x 4 dense 174 -> 166 us).
+  static constexpr int LPR = ((G >= 8 && ROW_BYTES >= 256) || (G >= 4 && ROW_BYTES > 256)) ? 16 : 8;
   static constexpr int EPC = Elem<T>::kPerChunk;               // elements per 16-byte chunk
   static constexpr int C = ROW_BYTES / (16 * LPR);             // chunks per lane per row
   static constexpr int E = C * EPC;                            // elements owned per lane
