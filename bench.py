@@ -102,9 +102,10 @@ def upload(a, dev):
 WARM_S = 0.1
 
 
-def warm(fn, n, stream, seconds=WARM_S):
+def warm(fn, n, stream, seconds=None):
     """Runs fn(0 .. n-1) in rounds, each ended by a stream synchronization, until `seconds` of wall
-    time have passed."""
+    time (WARM_S unless given) have passed."""
+    seconds = WARM_S if seconds is None else seconds
     t0 = time.perf_counter()
     while True:
         for i in range(n):
@@ -442,6 +443,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="headline and step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_S,
+                    help="untimed work before every timed loop (default %(default)s s; hardware-counter runs, "
+                         "whose byte counts do not depend on clocks, can take 0 to keep their dispatch count small)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy 10 times (reference for hardware byte counters)")
     ap.add_argument("--only", default="",
@@ -449,6 +453,8 @@ def main():
                          "draft_refresh, head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k, "
                          "sweep_b1, sweep_b16, sweep_long")
     args = ap.parse_args()
+    global WARM_S
+    WARM_S = max(0.0, args.warm_seconds)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
