@@ -436,6 +436,7 @@ def cpu_baseline(budget_s):
 # --------------------------------------------------------------------------- main
 
 def main():
+    global WARM_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -453,7 +454,6 @@ def main():
                          "draft_refresh, head_selection, refresh_schedule, refresh_64k_overlap, specmix_128k, "
                          "sweep_b1, sweep_b16, sweep_long")
     args = ap.parse_args()
-    global WARM_S
     WARM_S = max(0.0, args.warm_seconds)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
