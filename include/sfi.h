@@ -396,6 +396,10 @@ SFI_API sfi_status sfi_mixed_attn_workspace_size(const sfi_shape* shape, const s
  * Launch plan of the split-K attention calls, for inspection and tests
  * (host only, no GPU needed).  op: 0 = dense / verify (t_q as given),
  * 1 = sparse decode.  Returns the tokens per split and splits per (b, g).
+ * A split holds at most 4096 tokens; where that cap needs more work-groups
+ * than the target, the tokens are cut evenly over as many splits as fill the
+ * waves of work-groups the cap needs (so that no CU streams two long splits
+ * while another streams one).
  * For op 1 the splits cut the virtual rows [0, cap + recent) evenly, except
  * when the compact rows need several splits and one more work-group per
  * (b, g) still fits the plan's target of about one work-group per CU: then
