@@ -135,11 +135,12 @@ struct SplitTail {
   // The merge sits on the critical path of every call and is run by one
   // work-group, so it is built for few instructions and one memory round trip:
   // outputs are handled as float4 groups, P consecutive lanes share a group and
-  // take splits p, p + P, ... (16-byte device-coherent loads), the first PRE
-  // loads of every lane are in flight together with all (m, l) pairs before
-  // anything waits, per-row max and sum are wave reductions, and the P lane sums
-  // are combined by a fixed xor tree.  Every sum has a fixed order, so the result
-  // does not depend on which work-group merges.  tail: LDS of bytes(R, ns_max).
+  // take splits p, p + P, ... (16-byte device-coherent loads), and the P lane sums
+  // are combined by a fixed xor tree.  The row statistics come either from each
+  // lane's own (m, l) pairs folded by the same tree (a decode unit: no LDS, no
+  // barrier) or from all pairs staged in LDS and reduced by one wave per row.  Every
+  // sum has a fixed order, so the result does not depend on which work-group
+  // merges.  tail: LDS of bytes(R, ns_max).
   __device__ static void run(const AttnArgs& a, int b, int g, int q_row0, int G, int R, int ns_max, int* flag,
                              float* tail) {
     __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
@@ -156,7 +157,8 @@ struct SplitTail {
       __hip_atomic_store(unit_counter(a.counters, b * a.Hkv + g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // The merge itself: every thread of the work-group takes part (it has barriers).
+  // The merge itself: every thread of the work-group takes part (the LDS form has
+  // barriers, and both forms exchange values across the lanes of whole waves).
   // Also run by a later launch on the partials an earlier one left (the pack or the
   // fast-step launch that finishes a deferred slow step), where the device-coherent
   // loads cost nothing extra.
