@@ -295,7 +295,14 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   // the 2 U ROWS consecutive rows starting at w * 2 U ROWS of the pair's 2 TILE rows, so
   // a wave's logits of both iterations are contiguous.  Plain order: iteration it is
   // rows [it TILE, it TILE + TILE) of the split.
+  // A compact-buffer split of 8 or more iterations without recent rows starts at
+  // iteration rot of its n_rot and wraps around (set below; 0 and 0 otherwise).
+  int rot = 0, n_rot = 0;
   auto vrow = [&](int it, int u) {
+    if constexpr (SPARSE && !INDEXED && !PAIRED) {
+      const int x = it + rot;
+      it = it < n_rot ? (x >= n_rot ? x - n_rot : x) : it;
+    }
     if constexpr (PAIRED)
       return t0 + (it >> 1) * (2 * TILE) + w * (2 * U * ROWS) + (it & 1) * (U * ROWS) + u * ROWS + r;
     else
@@ -519,6 +526,20 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const int b, cons
   // Two-deep software pipeline; the prefetches are unconditional (see issue()).  In
   // plain order an iteration past the split's last is empty and is not computed.
   const int n_it = (t1 > t0) ? (t1 - t0 + TILE - 1) / TILE : 0;
+  // Long compact-buffer splits read long contiguous runs of rows, and split-K
+  // work-groups start together: run in step, they all sit at the same offsets of their
+  // runs.  Each work-group starts at its own iteration instead (the rows and their merge
+  // are unchanged; the order of the online softmax is fixed by the plan).  16K x 16 at
+  // 50 %: 96.3 -> 86.8 us; 16K batch 1 at 98.4 % and 100 %: 16.6 -> 16.2 and 17.0 ->
+  // 16.6; splits below 8 iterations gained nothing and keep the plain order.  The
+  // index-set variant reads its rows through the block table, already spread over the
+  // pool, and keeps the plain order (the rotation cost its step 0.2 us).
+  if constexpr (SPARSE && !INDEXED && !PAIRED) {
+    if (!has_recent && n_it >= 8) {
+      n_rot = n_it;
+      rot = (int)((((int64_t)b * a.Hkv + g) * a.n_split + split) % n_it);
+    }
+  }
   Buf A, Bb;
   if (n_it > 0) {
     // Scheduling barriers keep each refill below the last use of its buffer (so

@@ -69,7 +69,12 @@ CASES = [
                                             seq_lens=[16384, 9000], n_sink=4, n_recent=64, k_sel=256), 256, 0),
     ("bf16_b16_large_grid", lambda: make_case(305, name="ix_e", B=16, Hq=16, Hkv=8, d=128, dtype="bf16",
                                                seq_lens=list(range(1500, 3100, 100)), n_sink=4, n_recent=64,
-                                               k_sel=1024), 1024, 0),
+                                               k_sel=700), 700, 0),
+    # compact splits of 576 rows: the compact fast step starts them at rotated iterations, so the two
+    # variants are compared with the oracle only
+    ("bf16_b16_long_splits", lambda: make_case(307, name="ix_g", B=16, Hq=16, Hkv=8, d=128, dtype="bf16",
+                                                seq_lens=list(range(1500, 3100, 100)), n_sink=4, n_recent=64,
+                                                k_sel=1024), 1024, 0),
 ]
 
 
@@ -82,8 +87,12 @@ def test_indexed_fast_step_matches_oracle(gpu_lib, name, mk, k, pad):
     sels = [_selection(rng, c, int(L[b]), k, pad) for b in range(c.B)]
     out, lse = _indexed(gpu_lib, c, dc, sels, L)
     _check_vs_oracle(c, out, lse, sels, L)
-    if pad == 0 and all(int(L[b]) - c.n_sink - c.n_recent >= k for b in range(c.B)):
-        # every entry valid: bit-identical to packing the same rows and the compact fast step
+    st, ns = gpu_lib.plan_splits(1, B=c.B, Hq=c.Hq, Hkv=c.Hkv, d=c.d, bf16=c.dtype == "bf16",
+                                 max_pages=c.kv.max_pages, num_pages=c.kv.num_pages, max_seq_len=dc.max_seq_len,
+                                 cap=c.n_sink + k, n_recent=c.n_recent)
+    if pad == 0 and all(int(L[b]) - c.n_sink - c.n_recent >= k for b in range(c.B)) and st < 8 * 64:
+        # every entry valid and no compact split long enough for a rotated start (8 iterations of 64
+        # rows): bit-identical to packing the same rows and the compact fast step
         sel_d = dev_array(np.stack(sels).astype(np.int32))
         ck, cv, nc = gpu_lib.pack_compact(dc.k, dc.v, dc.bt, dc.lens, sel_d, n_sink=c.n_sink, cap=c.n_sink + k,
                                           max_seq_len=dc.max_seq_len)
