@@ -295,9 +295,10 @@ SFI_API sfi_status sfi_dense_attn_with_head_stats(const sfi_shape* shape, const 
  * [max(n_sink, L_b - n_recent), L_b).  A position behind an invalid block-table
  * entry is skipped.  With every entry of sel_idx a valid position (no padding), the
  * result equals sfi_pack_compact followed by sfi_sparse_decode_attn with cap =
- * n_sink + k bit for bit while no split of the plan has 512 or more compact rows
- * (sfi_sparse_decode_attn starts such splits at a rotated iteration); otherwise, and
- * with padding (the two then split the work at other tokens), they agree to rounding.
+ * n_sink + k bit for bit while no split of the plan holds 8 or more loop iterations
+ * of compact rows only (512 rows at most shapes; sfi_sparse_decode_attn starts such
+ * splits at a rotated iteration); otherwise, and with padding (the two then split
+ * the work at other tokens), they agree to rounding.
  *
  *   sel_idx  int32 [B, Hkv, k], device, e.g. the output of sfi_select_topk; k >= 0
  *            (sel_idx may be NULL when k is 0; n_sink = k = 0 attends the recent
