@@ -44,28 +44,58 @@ __device__ __forceinline__ void pack_block(const PackArgs& p, const int bx, cons
   char* ckp = reinterpret_cast<char*>(p.ck);
   char* cvp = reinterpret_cast<char*>(p.cv);
 
-  for (int rr = threadIdx.x / CPR; rr < RPB; rr += RPP) {
-    const int i = bx * RPB + rr;
-    if (i >= ns + p.k || i >= p.cap) continue;
-    const int pos = i < ns ? i : srow[i - ns];
-    if (pos < 0) continue;
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (pos < L) {
-      const int pg = bt[pos >> 4];
-      if (pg >= 0 && pg < p.num_pages) {
-        const int64_t off = (int64_t)pg * page_bytes + ((int64_t)g * kPage + (pos & 15)) * ROW_BYTES + chunk * 16;
-        // each source row is read once: streaming loads keep it out of the caches
-        kx = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
-        vx = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
-      }
+  // Each row waits for up to four dependent loads (the request's length, its selection
+  // entry, its page, its data).  All passes of the work-group go through each stage
+  // together, and the selection entries are read before the length is known, assuming
+  // ns = n_sink (a request shorter than the sink re-reads them), so the chain costs three
+  // memory round trips per work-group instead of four per pass.
+  constexpr int NP = (RPB + RPP - 1) / RPP;   // passes
+  const int r0 = threadIdx.x / CPR;
+  int pos[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int rr = r0 + j * RPP, i = bx * RPB + rr;
+    const bool row = rr < RPB && i < p.n_sink + p.k && i < p.cap;
+    pos[j] = !row ? -1 : (i < p.n_sink ? i : srow[i - p.n_sink]);
+  }
+  if (ns != p.n_sink) {   // uniform: the request is shorter than the sink
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int rr = r0 + j * RPP, i = bx * RPB + rr;
+      const bool row = rr < RPB && i < ns + p.k && i < p.cap;
+      pos[j] = !row ? -1 : (i < ns ? i : srow[i - ns]);
     }
-    // Streaming (non-temporal) stores: the packed rows are read by the next fast step,
-    // launches later, and write-back stores left them dirty in the caches, where the
-    // write-back of several MiB slowed the next launch (the 16K step: 40.9 -> 38.6 us
-    // with these, the slow step that follows the pack 2.3 us faster).
-    const int64_t dst = (dst_head + i) * ROW_BYTES + chunk * 16;
-    __builtin_nontemporal_store(kx, reinterpret_cast<u32x4*>(ckp + dst));
-    __builtin_nontemporal_store(vx, reinterpret_cast<u32x4*>(cvp + dst));
+  }
+  int pg[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e = (pos[j] >= 0 && pos[j] < L) ? bt[pos[j] >> 4] : -1;
+    pg[j] = (e >= 0 && e < p.num_pages) ? e : -1;
+  }
+  u32x4 kx[NP], vx[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    kx[j] = u32x4{0u, 0u, 0u, 0u};
+    vx[j] = u32x4{0u, 0u, 0u, 0u};
+    if (pg[j] >= 0) {
+      const int64_t off = (int64_t)pg[j] * page_bytes + ((int64_t)g * kPage + (pos[j] & 15)) * ROW_BYTES + chunk * 16;
+      // each source row is read once: streaming loads keep it out of the caches
+      kx[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
+      vx[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+    }
+  }
+  // Streaming (non-temporal) stores: the packed rows are read by the next fast step,
+  // launches later, and write-back stores left them dirty in the caches, where the
+  // write-back of several MiB slowed the next launch (the 16K step: 40.9 -> 38.6 us
+  // with these, the slow step that follows the pack 2.3 us faster).  A padding entry
+  // (negative) writes nothing; a position past the end or behind an invalid page
+  // writes a zero row.
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (pos[j] < 0) continue;
+    const int64_t dst = (dst_head + bx * RPB + r0 + j * RPP) * ROW_BYTES + chunk * 16;
+    __builtin_nontemporal_store(kx[j], reinterpret_cast<u32x4*>(ckp + dst));
+    __builtin_nontemporal_store(vx[j], reinterpret_cast<u32x4*>(cvp + dst));
   }
 
   if (bx == 0 && g == 0) {
