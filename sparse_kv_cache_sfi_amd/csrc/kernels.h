@@ -18,6 +18,11 @@ constexpr int kBtSlots = kMaxSplitTokens / 16 + 2;
 constexpr int kMaxSplits = 256;
 // Most splits of a verification unit (its tail keeps t_q * G rows of weights).
 constexpr int kMaxVerifySplits = 64;
+// Largest verification split: twice the decode kernels' (its block-table slice, 2 KiB of
+// LDS, fits beside the tiles), so that long contexts take half the splits, one wave of
+// work-groups and half the partials for the unit's merge.
+constexpr int kMaxVerifySplitTokens = 8192;
+constexpr int kVerifyBtSlots = kMaxVerifySplitTokens / 16 + 2;
 // Most query rows (t_q * G) of one KV head in a verification call.
 constexpr int kMaxVerifyRows = 32;
 // Split-K arrival counters live at the start of every workspace that holds

@@ -117,7 +117,7 @@ int64_t tune_env(const char* name, int64_t fallback) {
 }
 
 Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int max_splits = sfi::kMaxSplits,
-                 int64_t target = 0) {
+                 int64_t target = 0, int64_t max_tokens = sfi::kMaxSplitTokens) {
   if (target <= 0) target = tune_env("SFI_TUNE_TARGET_WGS", 256);
   min_split = tune_env("SFI_TUNE_MIN_SPLIT", min_split);
   if (n_tok <= 0) return {tile, 1};
@@ -128,14 +128,14 @@ Split plan_split(int64_t units, int64_t n_tok, int tile, int64_t min_split, int 
   if (ns < 1) ns = 1;
   int64_t st = (n_tok + ns - 1) / ns;
   st = (st + tile - 1) / tile * tile;
-  if (st > sfi::kMaxSplitTokens) {
+  if (st > max_tokens) {
     // Capped splits give more work-groups than the target, and cut at the cap they can
     // leave CUs with two long splits beside CUs with one: at 16 requests x 8 KV heads x
     // 12288 tokens, three splits of 4096 make 384 work-groups (a third of a second wave),
     // and at 12305 tokens three of 4096 and one of 17 do the same.  Cut evenly into as
     // many splits as fill the waves of work-groups the cap needs anyway (there, four
     // splits of 3072 or 3136 tokens: two work-groups per CU).
-    const int64_t ns_cap = (n_tok + sfi::kMaxSplitTokens - 1) / sfi::kMaxSplitTokens;
+    const int64_t ns_cap = (n_tok + max_tokens - 1) / max_tokens;
     const int64_t waves = (units * ns_cap + target - 1) / target;
     const int64_t fill = std::max<int64_t>(ns_cap, std::min<int64_t>(waves * target / units, max_splits));
     st = (n_tok + fill - 1) / fill;
@@ -173,7 +173,8 @@ size_t partial_bytes(int64_t rows, int n_split, int d) {
 Split plan_dense(const sfi_shape* s, const sfi_paged_kv* kv, int t_q) {
   if (t_q > 1)
     return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kVerifyTile,
-                      dense_min_split(kv->max_seq_len), sfi::kMaxVerifySplits, verify_target_wgs());
+                      dense_min_split(kv->max_seq_len), sfi::kMaxVerifySplits, verify_target_wgs(),
+                      sfi::kMaxVerifySplitTokens);
   return plan_split((int64_t)s->batch * s->num_kv_heads, kv->max_seq_len, sfi::kDecodeTile,
                     dense_min_split(kv->max_seq_len));
 }
@@ -265,9 +266,9 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
   if (cap < 1 || n_recent < 0) return fail(SFI_ERR_INVALID_ARG, "cap must be >= 1 and n_recent >= 0");
   if ((int64_t)cap + n_recent > kMaxTokens)
     return fail(SFI_ERR_UNSUPPORTED, "cap + n_recent exceeds %lld tokens", (long long)kMaxTokens);
-  if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens)
+  if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxVerifySplitTokens)
     return fail(SFI_ERR_UNSUPPORTED, "max_seq_len (%d) exceeds %lld tokens for verification", kv->max_seq_len,
-                (long long)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens);
+                (long long)sfi::kMaxVerifySplits * sfi::kMaxVerifySplitTokens);
   int rows = 0;
   for (int b = 0; b < B; ++b) {
     if (modes[b] != 0 && modes[b] != 1) return fail(SFI_ERR_INVALID_ARG, "modes[%d] must be 0 or 1", b);
@@ -287,7 +288,7 @@ sfi_status plan_mixed(const sfi_shape* shape, const sfi_paged_kv* kv, const int3
   const int64_t n_tok = (int64_t)cap + rec;
   const Split sp_d = plan_split(units_d, n_tok, sfi::kDecodeTile, sparse_min_split(n_tok));
   const Split sp_v = plan_split(units_v, kv->max_seq_len, sfi::kVerifyTile, dense_min_split(kv->max_seq_len),
-                                sfi::kMaxVerifySplits, verify_target_wgs());
+                                sfi::kMaxVerifySplits, verify_target_wgs(), sfi::kMaxVerifySplitTokens);
   sfi::MixedPlan& p = ms->plan;
   p = sfi::MixedPlan{};
   int q_row0[sfi::kMaxMixedBatch];
@@ -362,9 +363,9 @@ sfi_status dense_call(const sfi_shape* shape, const sfi_paged_kv* kv, const void
     if (shape->dtype != SFI_BF16) return fail(SFI_ERR_UNSUPPORTED, "t_q > 1 needs bf16 inputs");
     if (t_q * G > sfi::kMaxVerifyRows)
       return fail(SFI_ERR_UNSUPPORTED, "t_q * G must be <= %d (got %d)", sfi::kMaxVerifyRows, t_q * G);
-    if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens)
+    if ((int64_t)kv->max_seq_len > (int64_t)sfi::kMaxVerifySplits * sfi::kMaxVerifySplitTokens)
       return fail(SFI_ERR_UNSUPPORTED, "max_seq_len (%d) exceeds %lld tokens for t_q > 1", kv->max_seq_len,
-                  (long long)sfi::kMaxVerifySplits * sfi::kMaxSplitTokens);
+                  (long long)sfi::kMaxVerifySplits * sfi::kMaxVerifySplitTokens);
   }
   if ((int64_t)shape->batch * shape->num_kv_heads > sfi::kMaxCounters)
     return fail(SFI_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= %d", sfi::kMaxCounters);

@@ -58,7 +58,7 @@ struct VerifyShape {
   static constexpr int BIG = TILES_LDS > TAIL ? TILES_LDS : TAIL;
   // The tiles start on a 128-byte boundary: 16-byte LDS accesses must be 16-byte
   // aligned to run at full rate.
-  static constexpr int BIG_OFF = (kBtSlots * 4 + 16 + 127) / 128 * 128;
+  static constexpr int BIG_OFF = (kVerifyBtSlots * 4 + 16 + 127) / 128 * 128;
   // The 32 query rows (the B operand of S^T) live in LDS, shared by the waves, rather
   // than in 32 registers per lane: that keeps the kernel within two waves per SIMD.
   static constexpr int Q_OFF = BIG_OFF + BIG;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
   const int R = a.t_q * G;
 
   int* bt_s = reinterpret_cast<int*>(smem);
-  int* flag = bt_s + kBtSlots;
+  int* flag = bt_s + kVerifyBtSlots;
   char* big = smem + S::BIG_OFF;
   char* kt = big + w * S::WAVE_LDS;   // this wave's K tile, then its V tile
   char* vt = kt + TILE * S::TILE_ROW;
