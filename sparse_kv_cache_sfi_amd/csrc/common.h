@@ -84,9 +84,10 @@ __device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
 
 // The value of x held by lane (lane ^ OFF), for a power of two OFF < 64: DPP
 // quad_perm for 1 and 2, DPP row_ror:8 for 8 (a rotation by 8 inside a 16-lane row
-// is the xor-8 exchange), ds_swizzle in bitmask mode for 4 (source lane = lane ^ 4
-// within 32 lanes), the permlane swaps for 16 and 32.  Every lane must be active
-// (blocks are whole waves, so lane = threadIdx.x mod 64).
+// is the xor-8 exchange), for 4 the rotations by 4 and by 12 inside the row (lane i
+// receives lane i - 4 or i + 4, and a lane keeps the one that is its xor-4 partner),
+// the permlane swaps for 16 and 32: VALU operations, none through the LDS unit.  Every
+// lane must be active (blocks are whole waves, so lane = threadIdx.x mod 64).
 template <int OFF>
 __device__ __forceinline__ float lane_xor(float x) {
   static_assert(OFF > 0 && OFF < 64 && (OFF & (OFF - 1)) == 0, "power of two below the wave width");
@@ -97,7 +98,11 @@ __device__ __forceinline__ float lane_xor(float x) {
     float lo, hi;
     lane_pair<OFF>(x, lo, hi);
     return (threadIdx.x & OFF) ? lo : hi;
-  } else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (OFF << 10)));
+  } else {
+    const float down = dpp_mov<0x124>(x);   // row_ror:4: lane i receives lane i - 4 (mod 16)
+    const float up = dpp_mov<0x12C>(x);     // row_ror:12: lane i receives lane i + 4 (mod 16)
+    return (threadIdx.x & 4) ? down : up;
+  }
 }
 
 // x combined by op with the lanes at xor distance FROM, 2 FROM, ..., 32, in that
