@@ -280,6 +280,15 @@ def test_split_plan_of_the_16k_decode_layer():
                            max_seq_len=16384) == (4096, 4)
 
 
+def test_verification_splits_take_up_to_8192_tokens():
+    # 4 verifying requests x 8 KV heads x 128K, 8 draft tokens: 16 splits of 8192 -> 512 work-groups, one wave
+    assert sfi.plan_splits(0, B=4, Hq=32, Hkv=8, d=128, bf16=True, max_pages=8192, num_pages=32768,
+                           max_seq_len=131072, t_q=8) == (8192, 16)
+    # the decode kernels keep 4096: one request x 8 KV heads x 256K at t_q = 1 -> 64 splits of 4096
+    assert sfi.plan_splits(0, B=1, Hq=16, Hkv=8, d=128, bf16=True, max_pages=16384, num_pages=16384,
+                           max_seq_len=262144) == (4096, 64)
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
